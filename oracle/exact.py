@@ -1,0 +1,199 @@
+"""fp64 exact-attention oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this module.  It is deliberately slow and plain: for every
+(batch, query head) it writes out the scaled score matrix row by row over all
+keys, masks it, and applies the textbook softmax and the product with V.
+No tiling, no online rescaling, no fusion: that is what the GPU path does,
+and this module exists to check it.
+
+Sources (the pages, cited by title and section):
+
+* hysenlabs.com, "FlashAttention: exakte Attention-Kernel fuer CUDA und ROCm",
+  section "Die Schnittstellen von flash_attn_func bis KV-Cache": the functions
+  compute scaled dot-product attention as softmax(Q @ K^T * softmax_scale) @ V,
+  take a ``causal`` flag and a ``softmax_scale``, and accept fewer KV heads than
+  query heads when the query head count is divisible by it (MQA/GQA).
+* same page, section "Von 2.0 bis 2.7": since version 2.1 the causal mask is
+  aligned to the bottom-right corner when query and key lengths differ.
+* tokenwerk.de, "FlashAttention", section "Was FlashAttention veraendert":
+  the method is exact attention -- not an approximate substitute -- and
+  differences against a reference are floating-point effects judged with
+  tolerances.
+* tokenwerk.de, "FlashAttention", section "Warum Kacheln beim
+  Speicherzugriff helfen" and its table: the dense score matrix of one head
+  has N x N cells (2 bytes per cell in the page's arithmetic).
+
+Readings where the pages are silent (each is listed in the design notes):
+
+* layout: q, out are [B, Nq, Hq, d]; k, v are [B, Nk, Hkv, d]; lse is
+  [B, Hq, Nq].  The oracle indexes logical (b, i, h, c) so it does not depend
+  on strides.
+* GQA grouping: query head h reads KV head floor(h / (Hq / Hkv)) -- each KV
+  head serves a contiguous run of Hq/Hkv query heads.
+* causal: key j is visible to query i iff j <= i + (Nk - Nq).
+* scale: the value the library receives is an fp32; the oracle uses that same
+  fp32 value, widened to fp64.
+* logsumexp: natural log of the sum of exp over the scaled, masked scores.
+* a query row with no visible key (causal, Nq > Nk) has output 0 and
+  logsumexp -inf (the empty-sum limit).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "attention",
+    "attention_rows",
+    "kv_head_of",
+    "allowed_keys",
+    "materialised_score_bytes",
+]
+
+
+def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
+    """KV head read by query head ``h`` (GQA/MQA, contiguous groups).
+
+    The interface page only requires Hq to be divisible by Hkv; the grouping
+    below (query heads [g*G, (g+1)*G) share KV head g, G = Hq/Hkv) is the
+    reading used throughout.
+    """
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError(f"Hq={Hq} must be a positive multiple of Hkv={Hkv}")
+    return h // (Hq // Hkv)
+
+
+def allowed_keys(i: int, Nq: int, Nk: int, causal: bool) -> int:
+    """Number of keys visible to query row ``i``; they are keys [0, count).
+
+    Non-causal rows see every key.  Causal rows see key j iff
+    j <= i + (Nk - Nq): the mask is aligned to the bottom-right corner
+    (hysenlabs.com page, section "Von 2.0 bis 2.7", version 2.1).
+    """
+    if not causal:
+        return Nk
+    return int(max(0, min(Nk, i + (Nk - Nq) + 1)))
+
+
+def materialised_score_bytes(Nq: int, Nk: int, bytes_per_cell: int = 2) -> int:
+    """Size of one head's dense score matrix, as in the tokenwerk.de page's
+    table (section "Warum Kacheln beim Speicherzugriff helfen"): Nq*Nk cells
+    at ``bytes_per_cell`` bytes each."""
+    return int(Nq) * int(Nk) * int(bytes_per_cell)
+
+
+def _as_f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # torch tensor on the CPU: widen exactly
+        import torch
+
+        x = x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _check_shapes(q: np.ndarray, k: np.ndarray, v: np.ndarray):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-D: [B, N, H, d]")
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk = k.shape
+    if v.shape != k.shape or Bk != B or dk != d:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
+    return B, Nq, Nk, Hq, Hkv, d
+
+
+def _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, want_p):
+    """Exact attention for the query rows ``rows`` of one (b, h) pair.
+
+    qh: [Nq, d]; kg, vg: [Nk, d] (already the KV head this query head reads).
+    Returns (O [R, d], lse [R], S [R, Nk], P [R, Nk] or None).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    # Scores over ALL keys: s_ij = sigma * <q_i, k_j>.
+    S = sigma * (qh[rows] @ kg.T)
+    # Mask: key j visible to row i iff j < allowed_keys(i).
+    counts = np.array([allowed_keys(int(i), Nq, Nk, causal) for i in rows], dtype=np.int64)
+    visible = np.arange(Nk)[None, :] < counts[:, None]
+    S = np.where(visible, S, -np.inf)
+    # Row-wise softmax over keys.  Subtracting the row maximum is the usual
+    # stable evaluation; it does not change the value.
+    m = S.max(axis=1) if Nk > 0 else np.full(len(rows), -np.inf)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    E = np.exp(S - m_safe[:, None])  # exp(-inf) = 0 for masked keys
+    l = E.sum(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        P = np.where(empty[:, None], 0.0, E / np.where(empty, 1.0, l)[:, None])
+        lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, l)))
+    O = P @ vg
+    return O, lse, S, (P if want_p else None)
+
+
+def attention(q, k, v, scale: float, causal: bool = False, *,
+              return_scores: bool = False, return_probs: bool = False,
+              slab_rows: int = 512):
+    """Exact attention in fp64.
+
+    Args:
+      q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d] -- numpy arrays or CPU torch
+         tensors holding the exact input values (bf16/fp16 values widen to
+         fp64 without loss).
+      scale: the softmax scale as passed to the library (an fp32 value).
+      causal: apply the bottom-right aligned causal mask.
+      return_scores / return_probs: also return the materialised score matrix
+         S and the probabilities P, shaped [B, Hq, Nq, Nk] (small inputs only).
+      slab_rows: how many query rows are written out at once.  Every row is
+         independent of the others, so this only bounds memory.
+
+    Returns:
+      (O [B, Nq, Hq, d] fp64, lse [B, Hq, Nq] fp64[, S][, P]).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, Nq, Nk, Hq, Hkv, d = _check_shapes(q, k, v)
+    sigma = float(np.float32(scale))
+    O = np.zeros((B, Nq, Hq, d))
+    lse = np.full((B, Hq, Nq), -np.inf)
+    S_all = np.full((B, Hq, Nq, Nk), -np.inf) if return_scores else None
+    P_all = np.zeros((B, Hq, Nq, Nk)) if return_probs else None
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            qh, kg, vg = q[b, :, h, :], k[b, :, g, :], v[b, :, g, :]
+            for r0 in range(0, Nq, max(1, slab_rows)):
+                rows = np.arange(r0, min(Nq, r0 + slab_rows))
+                Or, lr, Sr, Pr = _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk,
+                                                   causal, return_probs)
+                O[b, rows, h, :] = Or
+                lse[b, h, rows] = lr
+                if return_scores:
+                    S_all[b, h, rows, :] = Sr
+                if return_probs:
+                    P_all[b, h, rows, :] = Pr
+    out = (O, lse)
+    if return_scores:
+        out = out + (S_all,)
+    if return_probs:
+        out = out + (P_all,)
+    return out
+
+
+def attention_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows):
+    """Exact attention for selected query rows of one (b, h) pair.
+
+    Each output row depends only on its own query row and on all keys and
+    values of the KV head it reads, so evaluating a subset of rows is the
+    same definition restricted to those rows.  ``q`` needs only to provide
+    q[b, rows, h, :]; pass full tensors or views.
+
+    Returns (O [R, d] fp64, lse [R] fp64).
+    """
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    g = kv_head_of(h, Hq, Hkv)
+    qh = _as_f64(q[b, :, h, :])
+    kg = _as_f64(k[b, :, g, :])
+    vg = _as_f64(v[b, :, g, :])
+    sigma = float(np.float32(scale))
+    O, lse, _, _ = _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, False)
+    return O, lse
