@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Throughput of the exact attention forward on one MI355X.
+
+One step = one ``attn_fwd`` call over the whole workload (all query blocks
+of every (batch, head)), with q, k, v already resident in device memory.
+Default workload: B=4, H=16, N=4096, d=128, bf16, non-causal -- the hidden
+2048 / batch 16k/seq setup of the README benchmark described on the
+hysenlabs.com page (section "Leistungs- und Speicherangaben im README").
+
+Prints ONE JSON line on stdout.  ``value`` is TFLOP/s with the flop count
+4*B*Hq*Nq*Nk*d (halved for causal).  ``roofline`` compares the kernel's
+average duration (HIP events around every launch inside the timed region,
+on the launch stream) with MI355X's dense bf16/fp16 MFMA peak.
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
+workload (rank 0 only).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (bf16, d=128) and % of MI355X bf16 MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # MI355X dense MFMA, published
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "exact_tiled_attention_35_amd", "csrc", "attn_fwd_kernel.hpp"),
+    os.path.join(ROOT, "exact_tiled_attention_35_amd", "csrc", "attn_api.hip"),
+]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flops(w) -> float:
+    f = 4.0 * w.B * w.Hq * w.Nq * w.Nk * w.d
+    return f / 2 if w.causal else f
+
+
+def algorithmic_bytes(w) -> int:
+    el = 2
+    return (w.B * w.Nq * w.Hq * w.d * el * 2          # q read, out written
+            + w.B * w.Nk * w.Hkv * w.d * el * 2       # k, v read
+            + w.B * w.Hq * w.Nq * 4)                  # lse written
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    if they were taken on another version of the kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get("workloads", {}).get(workload_name)
+    if not rec or t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """Time the fp64 oracle head by head on this host until ``budget_s`` is spent."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        blas_threads = os.cpu_count() or 1
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    done = 0
+    t0 = time.perf_counter()
+    for (b, h) in heads:
+        oracle.attention_rows(q, k, v, w.scale, w.causal, b, h, np.arange(w.Nq))
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    f = flops(w) * done / len(heads)
+    return {
+        "value": f / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} (batch, head) pairs, all {w.Nq} query rows each, "
+                  f"fp64 NumPy, {dt:.1f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is described in the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from attn_workloads import HEADLINE, WORKLOADS, make_workload
+    from exact_tiled_attention_35_amd import attn_fwd, attn_version
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {w.name}; library {attn_version()}")
+    q, k, v = make_workload(w)
+    dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(dq)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        attn_fwd(dq, dk, dv, w.scale, w.causal, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()  # one rank: the barrier is this synchronisation
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_kernel_s = sum(kernel_ms) / K / 1e3
+    ms_per_step = wall / K * 1e3
+
+    F = flops(w)
+    value = F / (wall / K) / 1e12
+    achieved = F / avg_kernel_s / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = measured_traffic(w.name)
+    log(f"[bench] {K} steps: {ms_per_step:.4f} ms/step wall, kernel avg {avg_kernel_s*1e6:.1f} us "
+        f"(min {min(kernel_ms)*1e3:.1f} us), {achieved:.1f} TFLOP/s = {100*achieved/peak:.1f}% of peak")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0, sigma^2) inputs rounded to the element type)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk,
+                   "d": w.d, "causal": w.causal, "seed": w.seed, "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": algorithmic_bytes(w),
+            "kernel_avg_us": round(avg_kernel_s * 1e6, 2),
+        },
+        "cpu_baseline": None,
+        "context": "FlexAttention with the FA4 backend reports 1.2x-3.2x speedups on NVIDIA "
+                   "Hopper/Blackwell (liora.io news item); other hardware, not a target",
+    }
+    if not args.no_cpu_baseline:
+        del dq, dk, dv
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,50 @@
+"""ctypes loader for the HIP library ``libattn_fwd.so`` (C ABI in include/attn.h).
+
+There is no fallback: if the library is missing, ``load()`` raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_fwd.so")
+
+# attn_status values (include/attn.h).
+ATTN_OK = 0
+ATTN_ERR_NULL_POINTER = -1
+ATTN_ERR_BAD_SHAPE = -2
+ATTN_ERR_GQA_RATIO = -3
+ATTN_ERR_UNSUPPORTED_HDIM = -4
+ATTN_ERR_UNSUPPORTED_DTYPE = -5
+ATTN_ERR_BAD_SCALE = -6
+ATTN_ERR_MISALIGNED = -7
+ATTN_ERR_ALIASING = -8
+ATTN_ERR_NO_DEVICE = -9
+ATTN_ERR_LAUNCH = -10
+
+# attn_dtype values.
+ATTN_DTYPE_F16 = 0
+ATTN_DTYPE_BF16 = 1
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the library once and declare the exported signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"HIP library {LIB_PATH} is not built; run `python -m exact_tiled_attention_35_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp]
+    lib.attn_fwd.restype = ci
+    lib.attn_status_string.argtypes = [ci]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib

@@ -1,0 +1,84 @@
+"""Python binding of the C ABI: argument marshalling only.
+
+``attn_fwd`` checks that the torch tensors match the C ABI's layout
+contract, allocates the outputs with torch (device memory is torch's job),
+and calls the library's ``attn_fwd`` on torch's current HIP stream.  Every
+step of the computation runs in the HIP kernel.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+_DTYPE_CODE = {torch.float16: _lib.ATTN_DTYPE_F16, torch.bfloat16: _lib.ATTN_DTYPE_BF16}
+
+
+class AttnError(RuntimeError):
+    """A nonzero attn_status from the library; ``.code`` holds the value."""
+
+    def __init__(self, code: int):
+        self.code = code
+        super().__init__(attn_status_string(code))
+
+
+def attn_status_string(status: int) -> str:
+    return _lib.load().attn_status_string(int(status)).decode()
+
+
+def attn_version() -> str:
+    return _lib.load().attn_version().decode()
+
+
+def attn_fwd_ptr(q: int, k: int, v: int, out: int, lse: int, B: int, Hq: int, Hkv: int,
+                 Nq: int, Nk: int, d: int, scale: float, causal: bool, dtype: int,
+                 stream: int = 0) -> int:
+    """The C entry point with raw integer pointers; returns the attn_status."""
+    return _lib.load().attn_fwd(q, k, v, out, lse, int(B), int(Hq), int(Hkv), int(Nq), int(Nk),
+                                int(d), float(scale), int(bool(causal)), int(dtype), stream or None)
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: float | None = None,
+             causal: bool = False, out: torch.Tensor | None = None,
+             lse: torch.Tensor | None = None):
+    """Exact attention forward on the GPU.
+
+    q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d]; contiguous bf16 or fp16 tensors
+    on one HIP device.  ``softmax_scale`` defaults to 1/sqrt(d).
+    Returns (out [B, Nq, Hq, d] of q's dtype, lse [B, Hq, Nq] fp32).
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, N, H, d]")
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError(f"shape mismatch: q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, bf16 or fp16")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be on q's HIP device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, N, H, d]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if tuple(lse.shape) != (B, Hq, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 tensor [B, Hq, Nq]")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        code = attn_fwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, softmax_scale, causal,
+                            _DTYPE_CODE[q.dtype], stream)
+    if code != _lib.ATTN_OK:
+        raise AttnError(code)
+    return out, lse

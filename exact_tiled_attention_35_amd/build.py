@@ -1,0 +1,65 @@
+"""Build the HIP library in-tree: ``python -m exact_tiled_attention_35_amd.build``.
+
+Compiles ``csrc/attn_api.hip`` (C ABI + kernels) for gfx950 into
+``libattn_fwd.so`` next to this file, and writes the compiler's per-kernel
+resource report (VGPRs, AGPRs, LDS, scratch, occupancy) to
+``_build/resource_usage.txt``.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB_NAME = "libattn_fwd.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+BUILD_DIR = os.path.join(PKG, "_build")
+SOURCES = [os.path.join(PKG, "csrc", "attn_api.hip")]
+HEADERS = [os.path.join(PKG, "csrc", "attn_fwd_kernel.hpp"), os.path.join(ROOT, "include", "attn.h")]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def compile_flags() -> list:
+    return [
+        "--offload-arch=gfx950",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-shared",
+        # Packed fp32 VALU ops are kept out of the generated code.
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", os.path.join(ROOT, "include"),
+        "-I", os.path.join(PKG, "csrc"),
+    ]
+
+
+def build_library(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc()] + compile_flags() + ["-Rpass-analysis=kernel-resource-usage"] + SOURCES + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    report = os.path.join(BUILD_DIR, "resource_usage.txt")
+    with open(report, "w") as f:
+        f.write(proc.stderr)
+    if proc.returncode != 0:
+        errors = [ln for ln in proc.stderr.splitlines() if "error" in ln]
+        raise RuntimeError("hipcc failed:\n" + "\n".join(errors[:40] or proc.stderr.splitlines()[-40:]))
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    path = build_library(verbose="-v" in sys.argv)
+    print(path)

@@ -1,0 +1,142 @@
+// C ABI of the exact tiled attention forward (declared in include/attn.h).
+//
+// Host side only: argument validation (before any HIP call), a cached
+// per-device gfx950 check, choice of the kernel instance, grid size, and the
+// asynchronous launch on the caller's stream.  No device memory is allocated.
+
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "attn_fwd_kernel.hpp"
+
+namespace {
+
+constexpr const char* kVersion = "0.1.0 gfx950 exact-tiled-attention-fwd";
+constexpr int kMaxDevices = 64;
+
+// 0 = unknown, 1 = gfx950, 2 = other architecture.
+std::atomic<int> g_arch_state[kMaxDevices];
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_NO_DEVICE;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0 || dev >= count) return ATTN_ERR_NO_DEVICE;
+  if (dev >= kMaxDevices) return ATTN_ERR_NO_DEVICE;
+  int st = g_arch_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_NO_DEVICE;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? ATTN_OK : ATTN_ERR_NO_DEVICE;
+}
+
+template <int D, bool BF16, bool CAUSAL>
+int launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+           int Hkv, int Nq, int Nk, float scale, hipStream_t stream) {
+  using C = eta::TileCfg<D>;
+  const int nqb = (Nq + C::BM - 1) / C::BM;
+  const int64_t total64 = (int64_t)B * Hq * nqb;
+  if (total64 > 0x7fffffff) return ATTN_ERR_BAD_SHAPE;
+  const int total = (int)total64;
+  const float c_log2 = scale * 1.44269504088896340736f;
+  const int prescale = scale > 0.f ? 0 : 1;
+  hipLaunchKernelGGL((eta::attn_fwd_kernel<D, BF16, CAUSAL>), dim3(total), dim3(C::kThreads), 0,
+                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq, Hkv, Nq,
+                     Nk, nqb, total, c_log2, prescale);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+template <int D>
+int dispatch_dtype(bool bf16, bool causal, const void* q, const void* k, const void* v, void* out,
+                   float* lse, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
+                   hipStream_t s) {
+  if (bf16) {
+    return causal ? launch<D, true, true>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s)
+                  : launch<D, true, false>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s);
+  }
+  return causal ? launch<D, false, true>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s)
+                : launch<D, false, false>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s);
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                        int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                        void* stream) {
+  // 1. shape
+  if (B < 0 || Nq < 0 || Hq < 1 || Hkv < 1 || Nk < 1 || d < 1) return ATTN_ERR_BAD_SHAPE;
+  // 2. empty problem: nothing to do
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  // Element counts must fit comfortably in 64-bit byte offsets.
+  const double q_elems = (double)B * Nq * Hq * d, kv_elems = (double)B * Nk * Hkv * d;
+  if (q_elems > 0x1p60 || kv_elems > 0x1p60) return ATTN_ERR_BAD_SHAPE;
+  // 3. null pointers
+  if (!q || !k || !v || !out || !lse) return ATTN_ERR_NULL_POINTER;
+  // 4. GQA ratio
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA_RATIO;
+  // 5. head dimension
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED_HDIM;
+  // 6. element type
+  if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
+  // 7. scale
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  // 8. alignment (16-byte vector loads and stores)
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+    return ATTN_ERR_MISALIGNED;
+  // 9. aliasing: outputs must not overlap inputs or each other
+  const size_t qb = (size_t)q_elems * 2, kvb = (size_t)kv_elems * 2;
+  const size_t lb = (size_t)B * Hq * Nq * sizeof(float);
+  if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kvb) || overlaps(out, qb, v, kvb) ||
+      overlaps(lse, lb, q, qb) || overlaps(lse, lb, k, kvb) || overlaps(lse, lb, v, kvb) ||
+      overlaps(out, qb, lse, lb))
+    return ATTN_ERR_ALIASING;
+  // 10. device
+  const int dev_status = check_device();
+  if (dev_status != ATTN_OK) return dev_status;
+  // 11. launch
+  const bool bf16 = dtype == ATTN_DTYPE_BF16;
+  const bool c = causal != 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (d) {
+    case 64: return dispatch_dtype<64>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s);
+    case 128: return dispatch_dtype<128>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s);
+    default: return dispatch_dtype<256>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s);
+  }
+}
+
+extern "C" const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK: success";
+    case ATTN_ERR_NULL_POINTER: return "ATTN_ERR_NULL_POINTER: q, k, v, out or lse is NULL";
+    case ATTN_ERR_BAD_SHAPE:
+      return "ATTN_ERR_BAD_SHAPE: need B>=0, Nq>=0, Hq>=1, Hkv>=1, Nk>=1, d>=1 and a size that fits";
+    case ATTN_ERR_GQA_RATIO: return "ATTN_ERR_GQA_RATIO: Hq must be a multiple of Hkv";
+    case ATTN_ERR_UNSUPPORTED_HDIM: return "ATTN_ERR_UNSUPPORTED_HDIM: d must be 64, 128 or 256";
+    case ATTN_ERR_UNSUPPORTED_DTYPE: return "ATTN_ERR_UNSUPPORTED_DTYPE: dtype must be fp16 or bf16";
+    case ATTN_ERR_BAD_SCALE: return "ATTN_ERR_BAD_SCALE: scale must be finite";
+    case ATTN_ERR_MISALIGNED: return "ATTN_ERR_MISALIGNED: every pointer must be 16-byte aligned";
+    case ATTN_ERR_ALIASING: return "ATTN_ERR_ALIASING: out and lse must not overlap the inputs or each other";
+    case ATTN_ERR_NO_DEVICE: return "ATTN_ERR_NO_DEVICE: no HIP device, or the current device is not gfx950";
+    case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown attn status";
+  }
+}
+
+extern "C" const char* attn_version(void) { return kVersion; }

@@ -1,0 +1,99 @@
+/*
+ * attn.h -- C ABI of the exact tiled attention forward for AMD MI355X (gfx950).
+ *
+ * What is computed.  For every batch b, query head h and query row i:
+ *
+ *     out[b,i,h,:] = sum_j P[i,j] * v[b,j,g,:],
+ *     P[i,:]       = softmax_j( scale * <q[b,i,h,:], k[b,j,g,:]> )  over visible j,
+ *     lse[b,h,i]   = log( sum_j exp(scale * <q[b,i,h,:], k[b,j,g,:]>) )  (natural log)
+ *
+ * with g = floor(h / (Hq / Hkv)).  This is scaled dot-product attention as the
+ * interface section of the page "FlashAttention: exakte Attention-Kernel fuer
+ * CUDA und ROCm" (hysenlabs.com, section "Die Schnittstellen von
+ * flash_attn_func bis KV-Cache") states it: softmax(Q @ K^T * softmax_scale) @ V,
+ * with a causal flag and fewer KV heads than query heads when the query head
+ * count is divisible (MQA/GQA).  It is exact attention (tokenwerk.de,
+ * "FlashAttention", section "Was FlashAttention veraendert"): the result
+ * differs from a reference only by floating-point rounding.  The N x N score
+ * matrix is never written to device memory; the kernel streams K/V tiles
+ * through on-chip memory (tokenwerk.de, section "Warum Kacheln beim
+ * Speicherzugriff helfen"; unite.ai, "Was ist FlashAttention?", section
+ * "Eine fuenfstufige Betriebsuebersicht").
+ *
+ * Causal masking: key j is visible to query i iff j <= i + (Nk - Nq), i.e. the
+ * mask is aligned to the bottom-right corner when Nq != Nk (hysenlabs.com page,
+ * section "Von 2.0 bis 2.7", version 2.1).  A query row with no visible key gets
+ * out = 0 and lse = -inf.
+ *
+ * Layouts (all contiguous, row-major, element = 2 bytes):
+ *     q, out : [B, Nq, Hq, d]     k, v : [B, Nk, Hkv, d]     lse : [B, Hq, Nq] fp32
+ * out has the element type of q, k and v; outputs are rounded to nearest-even.
+ *
+ * Ownership: every pointer is a DEVICE pointer owned by the caller, who keeps
+ * the buffers alive until the enqueued work has finished.  The library
+ * allocates no device memory and keeps no state besides a per-device cached
+ * architecture check.
+ *
+ * Synchronisation: attn_fwd enqueues one kernel on `stream` (a hipStream_t;
+ * NULL = the default stream) and returns without waiting.  Faults during
+ * execution surface at the caller's next synchronisation.  Calls are
+ * re-entrant and thread-safe.
+ *
+ * Errors: arguments are validated before any HIP call, in this order, and the
+ * first failing check is returned; nothing is enqueued on error:
+ *     shape -> empty (B == 0 or Nq == 0: returns ATTN_OK, pointers may be NULL)
+ *     -> null pointers -> GQA ratio -> head dim -> dtype -> scale
+ *     -> 16-byte alignment -> aliasing -> device -> launch.
+ */
+#ifndef EXACT_TILED_ATTENTION_ATTN_H
+#define EXACT_TILED_ATTENTION_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of q, k, v and out (the page's FlashAttention-2 envelope:
+ * fp16 and bf16, hysenlabs.com, section "GPU-Abdeckung"). */
+typedef enum { ATTN_DTYPE_F16 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL_POINTER = -1,      /* q, k, v, out or lse is NULL                        */
+  ATTN_ERR_BAD_SHAPE = -2,         /* B<0, Nq<0, Hq<1, Hkv<1, Nk<1, d<1, or too large    */
+  ATTN_ERR_GQA_RATIO = -3,         /* Hq is not a multiple of Hkv                         */
+  ATTN_ERR_UNSUPPORTED_HDIM = -4,  /* d not in {64, 128, 256}                             */
+  ATTN_ERR_UNSUPPORTED_DTYPE = -5, /* dtype is not ATTN_DTYPE_F16 or ATTN_DTYPE_BF16      */
+  ATTN_ERR_BAD_SCALE = -6,         /* scale is NaN or +-inf                               */
+  ATTN_ERR_MISALIGNED = -7,        /* a base pointer is not 16-byte aligned              */
+  ATTN_ERR_ALIASING = -8,          /* out or lse overlaps an input, or each other        */
+  ATTN_ERR_NO_DEVICE = -9,         /* no HIP device, or the current device is not gfx950 */
+  ATTN_ERR_LAUNCH = -10            /* the kernel launch failed                            */
+} attn_status;
+
+/*
+ * Exact attention forward.
+ *   q      [B, Nq, Hq, d]  element type `dtype`            (read)
+ *   k, v   [B, Nk, Hkv, d] element type `dtype`            (read)
+ *   out    [B, Nq, Hq, d]  element type `dtype`            (written)
+ *   lse    [B, Hq, Nq]     fp32, natural-log logsumexp     (written)
+ *   scale  the softmax scale (any finite value; 1/sqrt(d) is the usual one)
+ *   causal nonzero: bottom-right aligned causal mask
+ *   dtype  an attn_dtype value
+ *   stream hipStream_t to enqueue on, or NULL
+ * Returns an attn_status value.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d,
+             float scale, int causal, int dtype, void* stream);
+
+/* A fixed, static message for a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* Library version and build description, e.g. "0.1.0 gfx950". */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_TILED_ATTENTION_ATTN_H */

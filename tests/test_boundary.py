@@ -1,0 +1,140 @@
+"""Host-side tests of the C ABI (no GPU needed, no kernel is ever launched).
+
+Every call below fails validation before the library makes any HIP call,
+except the no-device check, which only runs where no GPU is visible.  The
+pointers are fake but 16-byte aligned, and are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from exact_tiled_attention_35_amd import _lib
+from exact_tiled_attention_35_amd.attention import attn_fwd_ptr, attn_status_string, attn_version
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Fake, aligned, non-overlapping "device" addresses (never dereferenced).
+Q, K, V, OUT, LSE = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+GOOD = dict(q=Q, k=K, v=V, out=OUT, lse=LSE, B=2, Hq=8, Hkv=2, Nq=100, Nk=120, d=128,
+            scale=0.088, causal=True, dtype=_lib.ATTN_DTYPE_BF16)
+
+
+def call(**over):
+    a = dict(GOOD)
+    a.update(over)
+    return attn_fwd_ptr(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                        a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"])
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "attn.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert names == ["attn_fwd", "attn_status_string", "attn_version"]
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_version_and_messages():
+    assert "gfx950" in attn_version()
+    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10]
+    msgs = [attn_status_string(c) for c in codes]
+    assert len(set(msgs)) == len(codes)
+    assert msgs[0].startswith("ATTN_OK")
+    assert attn_status_string(12345) == "unknown attn status"
+
+
+@pytest.mark.parametrize("field,value", [("B", -1), ("Nq", -1), ("Hq", 0), ("Hkv", 0), ("Nk", 0), ("d", 0)])
+def test_bad_shape(field, value):
+    assert call(**{field: value}) == _lib.ATTN_ERR_BAD_SHAPE
+
+
+def test_too_large_is_bad_shape():
+    assert call(B=1 << 30, Nq=1 << 30, Hq=1 << 8, Hkv=1, d=256) == _lib.ATTN_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("field", ["B", "Nq"])
+def test_empty_problem_is_a_noop_even_with_null_pointers(field):
+    assert call(**{field: 0}, q=0, k=0, v=0, out=0, lse=0, dtype=99, d=7) == _lib.ATTN_OK
+
+
+def test_shape_is_checked_before_empty():
+    assert call(B=0, Nk=0) == _lib.ATTN_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "out", "lse"])
+def test_null_pointer(field):
+    assert call(**{field: 0}) == _lib.ATTN_ERR_NULL_POINTER
+
+
+def test_gqa_ratio():
+    assert call(Hq=8, Hkv=3) == _lib.ATTN_ERR_GQA_RATIO
+    assert call(Hq=2, Hkv=4) == _lib.ATTN_ERR_GQA_RATIO
+
+
+@pytest.mark.parametrize("d", [1, 32, 96, 100, 192, 512])
+def test_unsupported_head_dim(d):
+    assert call(d=d) == _lib.ATTN_ERR_UNSUPPORTED_HDIM
+
+
+@pytest.mark.parametrize("dtype", [-1, 2, 7])
+def test_unsupported_dtype(dtype):
+    assert call(dtype=dtype) == _lib.ATTN_ERR_UNSUPPORTED_DTYPE
+
+
+@pytest.mark.parametrize("scale", [float("nan"), float("inf"), float("-inf"), 1e39])
+def test_bad_scale(scale):
+    # 1e39 overflows to +inf when narrowed to the ABI's fp32.
+    assert call(scale=scale) == _lib.ATTN_ERR_BAD_SCALE
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "out", "lse"])
+def test_misaligned(field):
+    assert call(**{field: GOOD[field] + 8}) == _lib.ATTN_ERR_MISALIGNED
+
+
+def test_aliasing():
+    # out overlapping q, lse overlapping v, out overlapping lse, in-place out == q
+    assert call(out=Q) == _lib.ATTN_ERR_ALIASING
+    assert call(lse=V + 64) == _lib.ATTN_ERR_ALIASING
+    assert call(lse=OUT + 16) == _lib.ATTN_ERR_ALIASING
+    assert call(out=K - 16) == _lib.ATTN_ERR_ALIASING
+
+
+def test_validation_order():
+    # null pointer reported before the GQA ratio, GQA before head dim, ...
+    assert call(q=0, Hkv=3) == _lib.ATTN_ERR_NULL_POINTER
+    assert call(Hkv=3, d=100) == _lib.ATTN_ERR_GQA_RATIO
+    assert call(d=100, dtype=9) == _lib.ATTN_ERR_UNSUPPORTED_HDIM
+    assert call(dtype=9, scale=float("nan")) == _lib.ATTN_ERR_UNSUPPORTED_DTYPE
+    assert call(scale=float("nan"), q=Q + 2) == _lib.ATTN_ERR_BAD_SCALE
+    assert call(q=Q + 2, out=Q) == _lib.ATTN_ERR_MISALIGNED
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a HIP device is visible here")
+def test_no_device_reported_without_gpu():
+    assert call() == _lib.ATTN_ERR_NO_DEVICE
+    assert call(causal=False, dtype=_lib.ATTN_DTYPE_F16, d=64) == _lib.ATTN_ERR_NO_DEVICE
+
+
+def test_python_binding_rejects_bad_tensors():
+    from exact_tiled_attention_35_amd import attn_fwd
+
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn_fwd(q, q[:, :, :1], q, causal=False)  # k/v shape mismatch
+    with pytest.raises(ValueError):
+        attn_fwd(q.float(), q.float(), q.float())  # fp32 is not an ABI dtype
+    with pytest.raises(ValueError):
+        attn_fwd(q, q, q)  # CPU tensors

@@ -1,0 +1,214 @@
+"""GPU parity: the HIP kernel (through the C ABI) against the fp64 oracle.
+
+Tolerances, fixed in advance: on O (bf16/fp16 outputs, widened to fp64) the
+max-abs error is at most 1e-2 and the mean-abs error at most 1e-3, compared
+with the unrounded fp64 oracle; logsumexp within 1e-3; rows without a
+visible key must give O = 0 and lse = -inf exactly.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attn_workloads import WORKLOADS, make_qkv, make_workload
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS, LSE_ABS = 1e-2, 1e-3, 1e-3
+
+
+def gpu_attn(q, k, v, scale, causal):
+    from exact_tiled_attention_35_amd import attn_fwd
+
+    out, lse = attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale, causal)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def assert_close(out, lse, O, L, what=""):
+    o = out.double().numpy()
+    lg = lse.double().numpy()
+    err = np.abs(o - O)
+    assert np.all(np.isfinite(o)), what
+    assert err.max() <= MAX_ABS, f"{what}: max-abs {err.max():.3e}"
+    assert err.mean() <= MEAN_ABS, f"{what}: mean-abs {err.mean():.3e}"
+    fin = np.isfinite(L)
+    assert np.array_equal(np.isfinite(lg), fin), what
+    assert np.all(lg[~fin] == -np.inf), what
+    if fin.any():
+        lerr = np.abs(lg[fin] - L[fin]).max()
+        assert lerr <= LSE_ABS, f"{what}: lse max-abs {lerr:.3e}"
+    return float(err.max()), float(err.mean())
+
+
+# (B, Hq, Hkv, Nq, Nk, d, dtype, causal): several tiles, ragged tails,
+# Nq != Nk both ways, MQA/GQA, all head dims and both dtypes.
+SMALL = [
+    (1, 1, 1, 1, 1, 64, "bf16", False),
+    (1, 1, 1, 1, 1, 128, "bf16", True),
+    (1, 2, 1, 2, 3, 64, "fp16", False),
+    (1, 2, 2, 3, 2, 128, "bf16", True),
+    (1, 1, 1, 17, 17, 128, "bf16", True),
+    (2, 4, 2, 63, 65, 128, "bf16", False),
+    (1, 4, 4, 64, 64, 64, "fp16", True),
+    (1, 2, 1, 65, 127, 128, "bf16", True),
+    (1, 8, 1, 127, 128, 128, "bf16", False),
+    (1, 2, 2, 128, 129, 256, "fp16", True),
+    (1, 2, 2, 129, 128, 256, "bf16", False),
+    (2, 8, 2, 255, 255, 64, "bf16", True),
+    (1, 2, 1, 1000, 1000, 128, "bf16", True),
+    (1, 4, 2, 1000, 255, 256, "fp16", False),
+    (1, 2, 2, 300, 1000, 128, "bf16", True),
+    (1, 2, 2, 1000, 300, 64, "bf16", True),
+    (1, 2, 2, 257, 513, 256, "bf16", True),
+    (3, 6, 3, 129, 200, 64, "fp16", False),
+    (1, 4, 1, 511, 511, 128, "fp16", True),
+    (1, 16, 16, 128, 128, 128, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dH%d-%dN%dx%dd%d%s%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], "c" if c[7] else ""))
+def test_small_grid_against_oracle(case):
+    B, Hq, Hkv, Nq, Nk, d, dt, causal = case
+    q, k, v = make_qkv(B, Nq, Nk, Hq, Hkv, d, dt, 1.0, 200 + SMALL.index(case))
+    scale = 1.0 / math.sqrt(d)
+    out, lse = gpu_attn(q, k, v, scale, causal)
+    O, L = oracle.attention(q, k, v, scale, causal)
+    assert_close(out, lse, O, L, str(case))
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 1.0, 0.02])
+@pytest.mark.parametrize("causal", [False, True])
+def test_unusual_scales(scale, causal):
+    # negative scale (softmax of negated scores), zero (uniform weights),
+    # large (near one-hot rows: stresses the running-max updates), tiny.
+    q, k, v = make_qkv(1, 300, 300, 2, 1, 128, "bf16", 1.0, 300)
+    out, lse = gpu_attn(q, k, v, scale, causal)
+    O, L = oracle.attention(q, k, v, scale, causal)
+    assert_close(out, lse, O, L, f"scale={scale}")
+
+
+def test_pages_sdpa_example_shape():
+    # The PyTorch example on tokenwerk.de ("Ein begrenztes SDPA-Beispiel
+    # lesen"): q, k, v of shape (1, 4, 128, 64) fp16 in [B, H, N, d], no mask.
+    q, k, v = make_qkv(1, 128, 128, 4, 4, 64, "fp16", 1.0, 20)
+    out, lse = gpu_attn(q, k, v, 1.0 / 8.0, False)
+    O, L = oracle.attention(q, k, v, 1.0 / 8.0, False)
+    assert tuple(out.transpose(1, 2).shape) == (1, 4, 128, 64)
+    assert_close(out, lse, O, L)
+
+
+# ---------------------------------------------------------------------------
+# Invariants of the method, checked on the kernel.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,dt", [(64, "bf16"), (128, "bf16"), (256, "fp16")])
+def test_causal_row0_is_exactly_v0(d, dt):
+    q, k, v = make_qkv(2, 300, 300, 4, 2, d, dt, 1.0, 400)
+    out, lse = gpu_attn(q, k, v, 1.0 / math.sqrt(d), True)
+    G = 2
+    for h in range(4):
+        assert torch.equal(out[:, 0, h], v[:, 0, h // G])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_q_gives_mean_of_v(causal):
+    _, k, v = make_qkv(1, 200, 200, 2, 2, 128, "bf16", 1.0, 401)
+    q = torch.zeros(1, 200, 2, 128, dtype=torch.bfloat16)
+    out, lse = gpu_attn(q, k, v, 0.088, causal)
+    vv = v.double()[0]
+    for i in [0, 1, 2, 63, 64, 65, 127, 128, 199]:
+        n = i + 1 if causal else 200
+        mean = vv[:n].mean(dim=0)  # [H, d]
+        err = (out[0, i].double() - mean).abs()
+        assert torch.all(err <= mean.abs() * 2.0 ** -8 + 1e-5), (i, err.max())
+        assert abs(lse[0, :, i].double() - math.log(n)).max() <= 1e-5
+
+
+def test_constant_v_gives_constant_output():
+    q, k, _ = make_qkv(1, 500, 500, 2, 2, 128, "bf16", 1.0, 402)
+    v = torch.ones(1, 500, 2, 128, dtype=torch.bfloat16)
+    for causal in (False, True):
+        out, _ = gpu_attn(q, k, v, 1.0 / math.sqrt(128), causal)
+        assert (out.double() - 1.0).abs().max() <= 4e-3
+
+
+def test_one_hot_dominant_key():
+    Nq = Nk = 200
+    q, k, v = make_qkv(1, Nq, Nk, 1, 1, 128, "bf16", 1.0, 403)
+    i, jstar = 150, 77
+    k = k.clone()
+    k[0, jstar, 0] = (q[0, i, 0].float() * 4.0).to(torch.bfloat16)  # score gap >> 40 at scale 1
+    out, _ = gpu_attn(q, k, v, 1.0, False)
+    assert (out[0, i, 0].double() - v[0, jstar, 0].double()).abs().max() <= 1e-6
+
+
+def test_run_to_run_bitwise_determinism():
+    q, k, v = make_qkv(2, 700, 700, 8, 2, 128, "bf16", 1.0, 404)
+    a = gpu_attn(q, k, v, 0.088, True)
+    b = gpu_attn(q, k, v, 0.088, True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size, in the launch configuration the bench uses.
+# ---------------------------------------------------------------------------
+
+def sample_rows(N, rng, extra=24):
+    fixed = [0, 1, 2, 3, 31, 32, 63, 64, 65, 127, 128, 129, 255, 256, N // 2, N - 129, N - 2, N - 1]
+    rows = set(r for r in fixed if 0 <= r < N)
+    rows.update(int(x) for x in rng.integers(0, N, size=extra))
+    return sorted(rows)
+
+
+def sample_heads(w):
+    heads = {(0, 0), (w.B - 1, w.Hq - 1), (0, w.Hq // 2)}
+    if w.Hkv != w.Hq:
+        G = w.Hq // w.Hkv
+        heads.update({(0, G - 1), (0, G)})
+    return sorted(heads)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_full_size(name):
+    w = WORKLOADS[name]
+    print(f"[parity] workload {name}", flush=True)
+    q, k, v = make_workload(w)
+    out, lse = gpu_attn(q, k, v, w.scale, w.causal)
+    rng = np.random.default_rng(w.seed)
+    errs, means = [], []
+    if w.B * w.Hq * w.Nq * w.Nk <= 2 ** 22:  # small enough: every row
+        O, L = oracle.attention(q, k, v, w.scale, w.causal)
+        errs.append(assert_close(out, lse, O, L, name))
+    else:
+        for (b, h) in sample_heads(w):
+            rows = sample_rows(w.Nq, rng)
+            O, L = oracle.attention_rows(q, k, v, w.scale, w.causal, b, h, rows)
+            mx, mn = assert_close(out[b, rows, h], lse[b, h, rows], O, L, f"{name} b{b} h{h}")
+            errs.append((mx, mn))
+    print(f"[parity] {name}: worst sampled max-abs {max(e[0] for e in errs):.3e}", flush=True)
+
+    # Properties of every row at full size: outputs are convex combinations of
+    # the visible V rows (within rounding), and every lse is finite and at
+    # least the score of key 0 (which every causal row with Nq == Nk sees).
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    G = w.Hq // w.Hkv
+    vf = v.float().repeat_interleave(G, dim=2)  # [B, Nk, Hq, d]
+    if w.causal:
+        vmax = torch.cummax(vf, dim=1).values
+        vmin = torch.cummin(vf, dim=1).values
+    else:
+        vmax = vf.amax(dim=1, keepdim=True)
+        vmin = vf.amin(dim=1, keepdim=True)
+    of = out.float()
+    tol = 1e-2
+    assert torch.all(of <= vmax + tol) and torch.all(of >= vmin - tol)
+    del vf, vmax, vmin
+    qf = q.float()
+    k0 = k[:, 0].float().repeat_interleave(G, dim=1)  # [B, Hq, d]
+    s0 = torch.einsum("bihd,bhd->bhi", qf, k0) * w.scale
+    assert torch.all(lse >= s0 - 1e-3)
