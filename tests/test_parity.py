@@ -81,15 +81,57 @@ def test_small_grid_against_oracle(case):
     assert_close(out, lse, O, L, str(case))
 
 
+def lowp_baseline(q, k, v, scale, causal):
+    """Plain low-precision attention (CPU, fp32): scores and softmax in fp32
+    from the rounded inputs, P rounded to the element type, fp32 PV, output
+    rounded.  Only the yardstick of the page's test criterion below."""
+    B, Nq, Hq, d = q.shape
+    G = Hq // k.shape[2]
+    qf = q.float().transpose(1, 2)
+    kf = k.float().transpose(1, 2).repeat_interleave(G, 1)
+    vf = v.float().transpose(1, 2).repeat_interleave(G, 1)
+    s = (qf @ kf.transpose(-1, -2).contiguous()) * float(np.float32(scale))
+    if causal:
+        Nk = k.shape[1]
+        vis = torch.arange(Nk)[None, :] <= torch.arange(Nq)[:, None] + (Nk - Nq)
+        s = s.masked_fill(~vis, float("-inf"))
+    p = torch.softmax(s, -1).nan_to_num(0.0).to(q.dtype).float()
+    return (p @ vf).to(q.dtype).transpose(1, 2).double().numpy()
+
+
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 1.0, 0.02])
 @pytest.mark.parametrize("causal", [False, True])
 def test_unusual_scales(scale, causal):
-    # negative scale (softmax of negated scores), zero (uniform weights),
+    # Negative scale (softmax of negated scores), zero (uniform weights),
     # large (near one-hot rows: stresses the running-max updates), tiny.
+    # Away from the workloads' score distribution the 1e-2 bound can sit
+    # below the output's own rounding (|O| in [4, 8) has a bf16 half-ulp of
+    # 1.56e-2), so these cases use the criterion FlashAttention's tests use
+    # (hysenlabs.com page, section "Tests, BSD-3-Clause und Zitierpraxis"):
+    # the max error is at most twice that of a plain low-precision attention
+    # against the same fp64 reference.  The mean bound is kept as well.
     q, k, v = make_qkv(1, 300, 300, 2, 1, 128, "bf16", 1.0, 300)
     out, lse = gpu_attn(q, k, v, scale, causal)
     O, L = oracle.attention(q, k, v, scale, causal)
-    assert_close(out, lse, O, L, f"scale={scale}")
+    base = np.abs(lowp_baseline(q, k, v, scale, causal) - O)
+    err = np.abs(out.double().numpy() - O)
+    assert err.max() <= 2.0 * base.max(), (err.max(), base.max())
+    assert err.mean() <= max(MEAN_ABS, 2.0 * base.mean())
+    lerr = np.abs(lse.double().numpy() - L).max()
+    assert lerr <= LSE_ABS
+
+
+@pytest.mark.parametrize("case", SMALL[::3], ids=str)
+def test_small_grid_page_criterion(case):
+    # The same page criterion on part of the small grid: at most 2x the
+    # plain low-precision attention's max error.
+    B, Hq, Hkv, Nq, Nk, d, dt, causal = case
+    q, k, v = make_qkv(B, Nq, Nk, Hq, Hkv, d, dt, 1.0, 200 + SMALL.index(case))
+    scale = 1.0 / math.sqrt(d)
+    out, _ = gpu_attn(q, k, v, scale, causal)
+    O, _ = oracle.attention(q, k, v, scale, causal)
+    base = np.abs(lowp_baseline(q, k, v, scale, causal) - O).max()
+    assert np.abs(out.double().numpy() - O).max() <= 2.0 * base
 
 
 def test_pages_sdpa_example_shape():
