@@ -107,15 +107,97 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     }
 
 
+def calibration_copy(mib: int):
+    """One elementwise kernel that reads mib MiB and writes mib MiB (a negated
+    copy), the yardstick that scales FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+
+    n = mib * 2**20 // 4
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def _pmc_rows(path: str, counter: str):
+    """(kernel name, counter value) per dispatch from rocprofv3 output: a
+    counter_collection.csv, or the SQLite database rocprofv3 writes by default."""
+    rows = []
+    if path.endswith(".db"):
+        import sqlite3
+
+        con = sqlite3.connect(path)
+        q = "select kernel_name, value from counters_collection where counter_name = ? order by start"
+        rows = [(k, float(v)) for (k, v) in con.execute(q, (counter,))]
+        con.close()
+        return rows
+    import csv
+
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def write_traffic_summary(fetch_csv: str, write_csv: str, copy_mib, workload=None):
+    """Per-launch HBM bytes of the attention kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by the factor that maps the same counter
+    onto a plain copy of known size."""
+    from attn_workloads import HEADLINE, WORKLOADS
+
+    copy_bytes = int(copy_mib) * 2**20
+    name = workload or HEADLINE
+    w = WORKLOADS[name]
+    out = {"kernel_source_hash": kernel_source_hash(), "workloads": {}}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            old = json.load(f)
+        if old.get("kernel_source_hash") == out["kernel_source_hash"]:
+            out = old
+    rec = {}
+    for csv_path, counter, key in ((fetch_csv, "FETCH_SIZE", "read"), (write_csv, "WRITE_SIZE", "written")):
+        rows = _pmc_rows(csv_path, counter)
+        attn = [v for (k, v) in rows if "attn_fwd_kernel" in k]
+        copy = [v for (k, v) in rows if "neg_kernel" in k]
+        if not attn or not copy:
+            raise SystemExit(f"{csv_path}: need both attention and copy dispatches for {counter}")
+        copy_kib = max(copy)
+        factor = copy_bytes / (copy_kib * 1024.0)
+        kib = sum(attn) / len(attn)
+        rec[f"{counter}_KiB_per_launch"] = kib
+        rec[f"{counter}_copy_scale"] = factor
+        rec[f"bytes_{key}_per_launch"] = kib * 1024.0 * factor
+    rec["hbm_bytes_per_launch"] = rec["bytes_read_per_launch"] + rec["bytes_written_per_launch"]
+    rec["algorithmic_bytes"] = algorithmic_bytes(w)
+    out["workloads"][name] = rec
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=2)
+    print(json.dumps(rec, indent=2))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run one plain elementwise copy kernel that "
+                         "reads and writes MIB MiB (the reference for scaling HBM byte counters "
+                         "under rocprofv3 --pmc)")
+    ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_OUT", "WRITE_OUT", "COPY_MIB"),
+                    help="turn the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE outputs (.db or "
+                         "counter_collection.csv) of runs made with --calibration-copy-mib "
+                         "COPY_MIB into the committed per-launch traffic summary, then exit")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        write_traffic_summary(*args.traffic_from, workload=args.workload)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -200,6 +282,9 @@ def main():
         "context": "FlexAttention with the FA4 backend reports 1.2x-3.2x speedups on NVIDIA "
                    "Hopper/Blackwell (liora.io news item); other hardware, not a target",
     }
+    if args.calibration_copy_mib:
+        calibration_copy(args.calibration_copy_mib)
+        result["calibration_copy_bytes"] = args.calibration_copy_mib * 2**20
     if not args.no_cpu_baseline:
         del dq, dk, dv
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)

@@ -30,6 +30,13 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Finite test on the bits, independent of floating-point compile flags.
+bool finite_bits(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, sizeof u);
+  return ((u >> 23) & 0xffu) != 0xffu;
+}
+
 int check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_NO_DEVICE;
@@ -87,6 +94,12 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
   // Element counts must fit comfortably in 64-bit byte offsets.
   const double q_elems = (double)B * Nq * Hq * d, kv_elems = (double)B * Nk * Hkv * d;
   if (q_elems > 0x1p60 || kv_elems > 0x1p60) return ATTN_ERR_BAD_SHAPE;
+  // The kernels address a 128-row window of q/out and a 64-row tile of k/v
+  // with 32-bit byte offsets.
+  if ((double)128 * Hq * d * 2 >= 0x1p31 || (double)64 * Hkv * d * 2 >= 0x1p31)
+    return ATTN_ERR_BAD_SHAPE;
+  // The grid holds one workgroup per 128 query rows of every (b, head).
+  if ((double)B * Hq * ((Nq + 127) / 128) > 0x7fffffff) return ATTN_ERR_BAD_SHAPE;
   // 3. null pointers
   if (!q || !k || !v || !out || !lse) return ATTN_ERR_NULL_POINTER;
   // 4. GQA ratio
@@ -96,7 +109,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
   // 6. element type
   if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
   // 7. scale
-  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  if (!finite_bits(scale)) return ATTN_ERR_BAD_SCALE;
   // 8. alignment (16-byte vector loads and stores)
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
     return ATTN_ERR_MISALIGNED;

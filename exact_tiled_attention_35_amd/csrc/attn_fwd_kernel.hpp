@@ -126,6 +126,42 @@ __device__ __forceinline__ f32x8_t unpack8(u32x4_t x) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(max(a, b), c): one v_max3_f32.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+}
+
+// Raw buffer resources.  Every global access goes through a descriptor whose
+// range covers exactly the valid rows of the current tile: the hardware
+// returns 0 for loads past the range and drops stores past it, so ragged
+// tails need no branches, and per-thread byte offsets stay loop-invariant
+// (only the scalar base address moves from tile to tile).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFlags);
+}
+
+__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, int voff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store8(u32x2_t v, rsrc_t r, int voff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store4(float v, rsrc_t r, int voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, 0, 0);
+}
+
+// Bytes from row r0 to the end of the last valid row of a [rows, D] window
+// of a tensor with row stride rs (elements), given N valid rows in total.
+__device__ __forceinline__ int span_bytes(int r0, int rows, int N, int64_t rs, int D) {
+  const int valid = min(rows, N - r0);
+  return valid > 0 ? (int)(((int64_t)(valid - 1) * rs + D) * 2) : 0;
+}
+
 // Position of key k (within a tile) in a V^T row: bits 2 and 3 of k are
 // swapped, so keys {4h..4h+3, 8+4h..8+4h+3} of each 16-key group -- the keys
 // lane half h feeds to one PV MFMA -- are contiguous.
@@ -173,7 +209,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::kStage];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
 
   const WorkItem w = map_workgroup<CAUSAL>(blockIdx.x, total, nqb, Hq);
   const int hkv = w.hq / (Hq / Hkv);
@@ -183,19 +220,18 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int diag = Nk - Nq;  // causal: key j visible to row i iff j <= i + diag
 
   const int64_t q_rs = (int64_t)Hq * D, kv_rs = (int64_t)Hkv * D;
-  const uint16_t* Qb = Q + ((int64_t)w.b * Nq * Hq + w.hq) * D;
-  const uint16_t* Kb = K + ((int64_t)w.b * Nk * Hkv + hkv) * D;
-  const uint16_t* Vb = V + ((int64_t)w.b * Nk * Hkv + hkv) * D;
+  // Row qw0 of (b, hq) in q / out; row 0 of (b, hkv) in k / v.
+  const int64_t qo_off = ((int64_t)w.b * Nq + qw0) * q_rs + (int64_t)w.hq * D;
+  const uint16_t* Kh = K + ((int64_t)w.b * Nk * Hkv + hkv) * D;
+  const uint16_t* Vh = V + ((int64_t)w.b * Nk * Hkv + hkv) * D;
 
   // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop.
   u32x4_t qf[NKS];
   {
-    const bool in = my_q < Nq;
-    const uint16_t* qrow = Qb + (int64_t)(in ? my_q : 0) * q_rs + 8 * hh;
+    const rsrc_t qr = make_rsrc(Q + qo_off, span_bytes(qw0, 32, Nq, q_rs, D));
+    const int voff = (int)(l32 * q_rs * 2) + 16 * hh;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      qf[ks] = in ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * ks) : u32x4_t{0, 0, 0, 0};
-    }
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = buf_load16(qr, voff + 32 * ks);
   }
 
   // ---- Key range of the workgroup and of this wave.
@@ -206,58 +242,68 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int w_end = rows_end > qw0 ? Nk : 0;
   if (CAUSAL && rows_end > qw0) w_end = min(Nk, rows_end + diag);
 
-  // ---- Tile staging: global -> registers -> LDS.
+  // ---- Tile staging: global -> registers -> LDS, with loop-invariant offsets.
+  int koff[C::kKChunksPerThread], kls[C::kKChunksPerThread];
+#pragma unroll
+  for (int i = 0; i < C::kKChunksPerThread; ++i) {
+    const int c = tid + C::kThreads * i;
+    const int row = c / KCPR, cc = c % KCPR;
+    koff[i] = (int)(row * kv_rs * 2) + 16 * cc;
+    kls[i] = row * KS + 8 * cc;
+  }
+  int voff[C::kVBlocksPerThread][4], vls[C::kVBlocksPerThread];
+#pragma unroll
+  for (int i = 0; i < C::kVBlocksPerThread; ++i) {
+    // Consecutive lanes take consecutive 4-key groups of one 8-column chunk:
+    // the lanes of one LDS write pass then fill one V^T row without bank
+    // conflicts, and each global load still reads whole 64-byte runs.
+    const int blk = tid + C::kThreads * i;
+    const int kg = blk % (BN / 4);
+    const int cc = blk / (BN / 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) voff[i][j] = (int)((4 * kg + j) * kv_rs * 2) + 16 * cc;
+    vls[i] = C::kKElems + (8 * cc) * VS + vt_pos(4 * kg);
+  }
+  // V blocks exist for whole waves only (kVBlocks is a multiple of 64).
+  auto has_vblock = [&](int i) {
+    return (C::kVBlocks % C::kThreads == 0) || (wave * 64 + C::kThreads * i < C::kVBlocks);
+  };
+
   u32x4_t kreg[C::kKChunksPerThread];
   u32x4_t vreg[C::kVBlocksPerThread][4];
 
   auto load_tile = [&](int j0) {
+    const int bytes = span_bytes(j0, BN, Nk, kv_rs, D);
+    const rsrc_t kr = make_rsrc(Kh + (int64_t)j0 * kv_rs, bytes);
+    const rsrc_t vr = make_rsrc(Vh + (int64_t)j0 * kv_rs, bytes);
 #pragma unroll
-    for (int i = 0; i < C::kKChunksPerThread; ++i) {
-      const int c = tid + C::kThreads * i;
-      const int row = c / KCPR, cc = c % KCPR;
-      const int key = j0 + row;
-      kreg[i] = key < Nk ? *reinterpret_cast<const u32x4_t*>(Kb + (int64_t)key * kv_rs + 8 * cc)
-                         : u32x4_t{0, 0, 0, 0};
-    }
+    for (int i = 0; i < C::kKChunksPerThread; ++i) kreg[i] = buf_load16(kr, koff[i]);
 #pragma unroll
     for (int i = 0; i < C::kVBlocksPerThread; ++i) {
-      const int blk = tid + C::kThreads * i;
-      const int cc = (blk & 3) + 4 * ((blk >> 2) / (BN / 4));
-      const int kg = (blk >> 2) % (BN / 4);
+      if (has_vblock(i)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = j0 + 4 * kg + j;
-        vreg[i][j] = (blk < C::kVBlocks && key < Nk)
-                         ? *reinterpret_cast<const u32x4_t*>(Vb + (int64_t)key * kv_rs + 8 * cc)
-                         : u32x4_t{0, 0, 0, 0};
+        for (int j = 0; j < 4; ++j) vreg[i][j] = buf_load16(vr, voff[i][j]);
       }
     }
   };
 
-  auto store_tile = [&](uint16_t* Ks) {
-    uint16_t* Vs = Ks + C::kKElems;
+  auto store_tile = [&](uint16_t* st) {
 #pragma unroll
-    for (int i = 0; i < C::kKChunksPerThread; ++i) {
-      const int c = tid + C::kThreads * i;
-      const int row = c / KCPR, cc = c % KCPR;
-      *reinterpret_cast<u32x4_t*>(Ks + row * KS + 8 * cc) = kreg[i];
-    }
+    for (int i = 0; i < C::kKChunksPerThread; ++i)
+      *reinterpret_cast<u32x4_t*>(st + kls[i]) = kreg[i];
 #pragma unroll
     for (int i = 0; i < C::kVBlocksPerThread; ++i) {
-      const int blk = tid + C::kThreads * i;
-      if (blk < C::kVBlocks) {
-        const int cc = (blk & 3) + 4 * ((blk >> 2) / (BN / 4));
-        const int kg = (blk >> 2) % (BN / 4);
-        uint16_t* dst = Vs + (8 * cc) * VS + vt_pos(4 * kg);
+      if (has_vblock(i)) {
+        uint16_t* dst = st + vls[i];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {  // element pair (2p, 2p+1) of the 8 columns
           const uint32_t r0 = vreg[i][0][p], r1 = vreg[i][1][p];
           const uint32_t r2 = vreg[i][2][p], r3 = vreg[i][3][p];
           u32x2_t even, odd;
-          even[0] = (r0 & 0xffffu) | (r1 << 16);
-          even[1] = (r2 & 0xffffu) | (r3 << 16);
-          odd[0] = (r0 >> 16) | (r1 & 0xffff0000u);
-          odd[1] = (r2 >> 16) | (r3 & 0xffff0000u);
+          even[0] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);
+          even[1] = __builtin_amdgcn_perm(r3, r2, 0x05040100u);
+          odd[0] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);
+          odd[1] = __builtin_amdgcn_perm(r3, r2, 0x07060302u);
           *reinterpret_cast<u32x2_t*>(dst + (2 * p) * VS) = even;
           *reinterpret_cast<u32x2_t*>(dst + (2 * p + 1) * VS) = odd;
         }
@@ -273,10 +319,11 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float lsum = 0.f;     // this lane half's share of the running sum
   const float ce = prescale ? 1.0f : c_log2;
 
-  if (nt > 0) {
-    load_tile(0);
-    store_tile(smem);
-  }
+  // Tile 0 is staged even when no tile is needed (nt == 0): the access is in
+  // range (Nk >= 1), and it leaves no load outstanding when the loop starts.
+  load_tile(0);
+  store_tile(smem);
+  __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tile 0 have landed
   __syncthreads();
 
   for (int t = 0; t < nt; ++t) {
@@ -323,9 +370,9 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(s[kb][r], s[kb][r + 1]));
+        for (int r = 0; r < 16; r += 2) tmax = max3(tmax, s[kb][r], s[kb][r + 1]);
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
       const float tm = tmax * ce;
       if (tm > m + kRescaleThreshold) {  // raise m; rescale what was accumulated
         const float alpha = exp2_fast(m - tm);
@@ -378,26 +425,25 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     __syncthreads();
   }
 
-  // ---- Epilogue: normalise, round, store O and the logsumexp.
+  // ---- Epilogue: normalise, round, store O and the logsumexp.  Stores of
+  // rows >= Nq fall outside the descriptors' ranges and are dropped.
   const float lt = lsum + __shfl_xor(lsum, 32);
-  if (my_q < Nq) {
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    uint16_t* orow = O + (((int64_t)w.b * Nq + my_q) * Hq + w.hq) * D + 4 * hh;
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const rsrc_t orr = make_rsrc(O + qo_off, span_bytes(qw0, 32, Nq, q_rs, D));
+  const int ovoff = (int)(l32 * q_rs * 2) + 8 * hh;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+  for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4_t o4;
+    for (int g = 0; g < 4; ++g) {
+      f32x4_t o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * g + e] * inv;
-        *reinterpret_cast<u32x2_t*>(orow + 32 * db + 8 * g) = pack4<BF16>(o4);
-      }
-    }
-    if (hh == 0) {
-      LSE[((int64_t)w.b * Hq + w.hq) * Nq + my_q] =
-          lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+      for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * g + e] * inv;
+      buf_store8(pack4<BF16>(o4), orr, ovoff + 2 * (32 * db + 8 * g));
     }
   }
+  const int nrows = max(0, min(32, Nq - qw0));
+  const rsrc_t lr = make_rsrc(LSE + ((int64_t)w.b * Hq + w.hq) * Nq + qw0, nrows * 4);
+  buf_store4(lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY, lr, 4 * l32);
 }
 
 }  // namespace eta

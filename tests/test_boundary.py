@@ -62,6 +62,10 @@ def test_bad_shape(field, value):
 
 def test_too_large_is_bad_shape():
     assert call(B=1 << 30, Nq=1 << 30, Hq=1 << 8, Hkv=1, d=256) == _lib.ATTN_ERR_BAD_SHAPE
+    # a head count whose 128-row q window exceeds 32-bit byte offsets
+    assert call(Hq=1 << 16, Hkv=1 << 16, d=128) == _lib.ATTN_ERR_BAD_SHAPE
+    # too many workgroups for one grid
+    assert call(B=1 << 16, Hq=1 << 10, Hkv=1, Nq=1 << 20, d=64) == _lib.ATTN_ERR_BAD_SHAPE
 
 
 @pytest.mark.parametrize("field", ["B", "Nq"])
