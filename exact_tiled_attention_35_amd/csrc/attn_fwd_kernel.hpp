@@ -64,24 +64,36 @@ constexpr float kLn2 = 0.693147180559945309417f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p <= 256 between rescales
 
 // Tile shape per head dimension.
+//
+// LDS holds two stages; each stage has a K region and a V region, both
+// row-major [BN keys][D] with padded rows.  The K row stride is 4 dwords past
+// a multiple of 32 banks, so the 8 lanes of one ds_read_b128 pass (8 rows)
+// hit distinct banks; the V row stride is 8 dwords past, so the 4 rows x 32
+// bytes that one 16-lane ds_read_b64_tr_b16 pass touches hit distinct banks.
+// Tiles are filled by direct global->LDS buffer loads, 64 lanes x 16 bytes
+// per instruction, one 16-byte "slot" per lane; pad slots receive a duplicate
+// chunk that is never read.
 template <int D>
 struct TileCfg {
   static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int BM = 32 * kWaves;                 // query rows per workgroup
   static constexpr int BN = (D >= 256) ? 32 : 64;        // keys per K/V tile
-  static constexpr int KS = D + 8;                       // K row stride in LDS (elements)
-  static constexpr int VS = BN + 8;                      // V^T row stride in LDS (elements)
-  static constexpr int kKElems = BN * KS;
-  static constexpr int kVElems = D * VS;
-  static constexpr int kStage = kKElems + kVElems;       // one LDS buffer (elements)
-  static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kKChunks = BN * D / 8;            // 16-byte chunks per K tile
-  static constexpr int kKChunksPerThread = kKChunks / kThreads;
-  static constexpr int kVBlocks = BN * D / 32;           // 4 keys x 8 columns per block
-  static constexpr int kVBlocksPerThread = (kVBlocks + kThreads - 1) / kThreads;
+  static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
+  static constexpr int KCP = kChunks + 1;                // K row, in 16-byte slots
+  static constexpr int VCP = kChunks + 2;                // V row, in 16-byte slots
+  static constexpr int KS = 8 * KCP;                     // K row stride (elements)
+  static constexpr int VS = 8 * VCP;                     // V row stride (elements)
+  static constexpr int kKInst = (BN * KCP + 63) / 64;    // direct-load instructions per K tile
+  static constexpr int kVInst = (BN * VCP + 63) / 64;    // ... per V tile
+  static constexpr int kKElems = kKInst * 64 * 8;        // K region (elements)
+  static constexpr int kVElems = kVInst * 64 * 8;        // V region (elements)
+  static constexpr int kStage = kKElems + kVElems;       // one stage (elements)
+  static constexpr int kKInstPerWave = (kKInst + kWaves - 1) / kWaves;
+  static constexpr int kVInstPerWave = (kVInst + kWaves - 1) / kWaves;
   static constexpr int kMinWavesPerEU = (D >= 256) ? 1 : 2;
-  static_assert(kKChunks % kThreads == 0, "K tile must split evenly over the workgroup");
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile sizes must be multiples of 32");
+  static_assert((KS / 2) % 32 == 4 && (VS / 2) % 32 == 8, "bank-conflict-free strides");
 };
 
 template <bool BF16>
@@ -155,18 +167,29 @@ __device__ __forceinline__ void buf_store4(float v, rsrc_t r, int voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, 0, 0);
 }
 
+// Direct global->LDS load: each lane's 16 bytes land at lds_dst + 16 * lane.
+__device__ __forceinline__ void buf_load_lds16(rsrc_t r, uint16_t* lds_dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, 0, 0, 0);
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each 16-lane
+// group, lane 4a+b receives element b of the 4-element rows addressed by
+// lanes a, a+4, a+8, a+12.  With lane i addressing row (i/4) at column
+// 4*(i%4) of a row-major [key][d] block, lane i receives 4 consecutive keys
+// at column i: one quarter of a 32x32x16 A operand of V^T.
+__device__ __forceinline__ u32x2_t lds_read_tr4(const uint16_t* p) {
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p));
+}
+
 // Bytes from row r0 to the end of the last valid row of a [rows, D] window
 // of a tensor with row stride rs (elements), given N valid rows in total.
 __device__ __forceinline__ int span_bytes(int r0, int rows, int N, int64_t rs, int D) {
   const int valid = min(rows, N - r0);
   return valid > 0 ? (int)(((int64_t)(valid - 1) * rs + D) * 2) : 0;
-}
-
-// Position of key k (within a tile) in a V^T row: bits 2 and 3 of k are
-// swapped, so keys {4h..4h+3, 8+4h..8+4h+3} of each 16-key group -- the keys
-// lane half h feeds to one PV MFMA -- are contiguous.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3);
 }
 
 // Work item of one workgroup.
@@ -206,7 +229,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int NKK = BN / 16; // 16-key steps of the PV product
   constexpr int KCPR = D / 8;  // 16-byte chunks per row
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::kStage];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -242,74 +265,42 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int w_end = rows_end > qw0 ? Nk : 0;
   if (CAUSAL && rows_end > qw0) w_end = min(Nk, rows_end + diag);
 
-  // ---- Tile staging: global -> registers -> LDS, with loop-invariant offsets.
-  int koff[C::kKChunksPerThread], kls[C::kKChunksPerThread];
+  // ---- Direct global->LDS tile loads.  This wave issues the K (V) tile's
+  // instructions j = wave, wave + 4, ...; lane -> 16-byte slot 64 j + lane ->
+  // (row, chunk) of the padded layout; offsets are loop-invariant.
+  int koff[C::kKInstPerWave], voff[C::kVInstPerWave];
 #pragma unroll
-  for (int i = 0; i < C::kKChunksPerThread; ++i) {
-    const int c = tid + C::kThreads * i;
-    const int row = c / KCPR, cc = c % KCPR;
-    koff[i] = (int)(row * kv_rs * 2) + 16 * cc;
-    kls[i] = row * KS + 8 * cc;
+  for (int i = 0; i < C::kKInstPerWave; ++i) {
+    const int sl = 64 * (wave + C::kWaves * i) + lane;
+    const int row = min(sl / C::KCP, BN - 1), c = min(sl % C::KCP, C::kChunks - 1);
+    koff[i] = (int)(row * kv_rs * 2) + 16 * c;
   }
-  int voff[C::kVBlocksPerThread][4], vls[C::kVBlocksPerThread];
 #pragma unroll
-  for (int i = 0; i < C::kVBlocksPerThread; ++i) {
-    // Consecutive lanes take consecutive 4-key groups of one 8-column chunk:
-    // the lanes of one LDS write pass then fill one V^T row without bank
-    // conflicts, and each global load still reads whole 64-byte runs.
-    const int blk = tid + C::kThreads * i;
-    const int kg = blk % (BN / 4);
-    const int cc = blk / (BN / 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) voff[i][j] = (int)((4 * kg + j) * kv_rs * 2) + 16 * cc;
-    vls[i] = C::kKElems + (8 * cc) * VS + vt_pos(4 * kg);
+  for (int i = 0; i < C::kVInstPerWave; ++i) {
+    const int sl = 64 * (wave + C::kWaves * i) + lane;
+    const int row = min(sl / C::VCP, BN - 1), c = min(sl % C::VCP, C::kChunks - 1);
+    voff[i] = (int)(row * kv_rs * 2) + 16 * c;
   }
-  // V blocks exist for whole waves only (kVBlocks is a multiple of 64).
-  auto has_vblock = [&](int i) {
-    return (C::kVBlocks % C::kThreads == 0) || (wave * 64 + C::kThreads * i < C::kVBlocks);
-  };
-
-  u32x4_t kreg[C::kKChunksPerThread];
-  u32x4_t vreg[C::kVBlocksPerThread][4];
-
-  auto load_tile = [&](int j0) {
+  auto issue_tile = [&](int j0, uint16_t* stage) {
     const int bytes = span_bytes(j0, BN, Nk, kv_rs, D);
     const rsrc_t kr = make_rsrc(Kh + (int64_t)j0 * kv_rs, bytes);
     const rsrc_t vr = make_rsrc(Vh + (int64_t)j0 * kv_rs, bytes);
 #pragma unroll
-    for (int i = 0; i < C::kKChunksPerThread; ++i) kreg[i] = buf_load16(kr, koff[i]);
+    for (int i = 0; i < C::kKInstPerWave; ++i) {
+      const int j = wave + C::kWaves * i;
+      if (j < C::kKInst) buf_load_lds16(kr, stage + 512 * j, koff[i]);
+    }
 #pragma unroll
-    for (int i = 0; i < C::kVBlocksPerThread; ++i) {
-      if (has_vblock(i)) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vreg[i][j] = buf_load16(vr, voff[i][j]);
-      }
+    for (int i = 0; i < C::kVInstPerWave; ++i) {
+      const int j = wave + C::kWaves * i;
+      if (j < C::kVInst) buf_load_lds16(vr, stage + C::kKElems + 512 * j, voff[i]);
     }
   };
 
-  auto store_tile = [&](uint16_t* st) {
-#pragma unroll
-    for (int i = 0; i < C::kKChunksPerThread; ++i)
-      *reinterpret_cast<u32x4_t*>(st + kls[i]) = kreg[i];
-#pragma unroll
-    for (int i = 0; i < C::kVBlocksPerThread; ++i) {
-      if (has_vblock(i)) {
-        uint16_t* dst = st + vls[i];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {  // element pair (2p, 2p+1) of the 8 columns
-          const uint32_t r0 = vreg[i][0][p], r1 = vreg[i][1][p];
-          const uint32_t r2 = vreg[i][2][p], r3 = vreg[i][3][p];
-          u32x2_t even, odd;
-          even[0] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);
-          even[1] = __builtin_amdgcn_perm(r3, r2, 0x05040100u);
-          odd[0] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);
-          odd[1] = __builtin_amdgcn_perm(r3, r2, 0x07060302u);
-          *reinterpret_cast<u32x2_t*>(dst + (2 * p) * VS) = even;
-          *reinterpret_cast<u32x2_t*>(dst + (2 * p + 1) * VS) = odd;
-        }
-      }
-    }
-  };
+  // ---- Operand reads from LDS (loop-invariant parts of the element offsets).
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int k_rd = l32 * KS + 8 * hh;
+  const int v_rd = C::kKElems + (4 * hh + (i16 >> 2)) * VS + 16 * (g16 & 1) + 4 * (i16 & 3);
 
   // ---- Running state (per lane = per query row).
   f32x16_t oacc[NDB];
@@ -319,18 +310,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float lsum = 0.f;     // this lane half's share of the running sum
   const float ce = prescale ? 1.0f : c_log2;
 
-  // Tile 0 is staged even when no tile is needed (nt == 0): the access is in
-  // range (Nk >= 1), and it leaves no load outstanding when the loop starts.
-  load_tile(0);
-  store_tile(smem);
+  if (nt > 0) issue_tile(0, smem);
   __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tile 0 have landed
   __syncthreads();
 
   for (int t = 0; t < nt; ++t) {
     const int j0 = t * BN;
-    if (t + 1 < nt) load_tile(j0 + BN);
-    const uint16_t* Ks = smem + (t & 1) * C::kStage;
-    const uint16_t* Vs = Ks + C::kKElems;
+    // Tile t+1 streams into the other stage while this one is computed (that
+    // stage was last read in iteration t-1, before the barrier that ended it).
+    if (t + 1 < nt) issue_tile(j0 + BN, smem + ((t + 1) & 1) * C::kStage);
+    const uint16_t* st = smem + (t & 1) * C::kStage;
 
     if (j0 < w_end) {  // wave-uniform: skip tiles above this wave's diagonal
       // S^T = K Q^T for BN keys x 32 queries.
@@ -341,8 +330,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          const u32x4_t a =
-              *reinterpret_cast<const u32x4_t*>(Ks + (kb * 32 + l32) * KS + 16 * ks + 8 * hh);
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(st + k_rd + kb * 32 * KS + 16 * ks);
           s[kb] = mfma_32x32x16<BF16>(a, qf[ks], s[kb]);
         }
       }
@@ -399,8 +387,10 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       }
       lsum += ps0 + ps1;
 
-      // O^T += V^T P^T.  One 16-key step uses registers 8*(kk%2)..+7 of
-      // S^T block kk/2: keys {4hh..4hh+3, 8+4hh..8+4hh+3} of the 16-group.
+      // O^T += V^T P^T.  PV step kk covers keys 16kk..16kk+15; lane half hh
+      // feeds keys {4hh..4hh+3, 8+4hh..8+4hh+3}, which registers
+      // 8*(kk%2)..+7 of S^T block kk/2 hold.  The A operand (V^T, 8 keys at
+      // one column) comes from two LDS transpose reads of row-major V.
       const bool split = CAUSAL && need_mask;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
@@ -413,15 +403,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         if (split) plo = pack8<BF16>(pv - unpack8<BF16>(phi));
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const u32x4_t a =
-              *reinterpret_cast<const u32x4_t*>(Vs + (db * 32 + l32) * VS + 16 * kk + 8 * hh);
+          const u32x2_t x0 = lds_read_tr4(st + v_rd + 16 * kk * VS + 32 * db);
+          const u32x2_t x1 = lds_read_tr4(st + v_rd + (16 * kk + 8) * VS + 32 * db);
+          const u32x4_t a = {x0[0], x0[1], x1[0], x1[1]};
           oacc[db] = mfma_32x32x16<BF16>(a, phi, oacc[db]);
           if (split) oacc[db] = mfma_32x32x16<BF16>(a, plo, oacc[db]);
         }
       }
     }
 
-    if (t + 1 < nt) store_tile(smem + ((t + 1) & 1) * C::kStage);
+    __builtin_amdgcn_s_waitcnt(0);  // tile t+1 has landed in LDS
     __syncthreads();
   }
 
