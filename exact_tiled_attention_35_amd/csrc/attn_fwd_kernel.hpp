@@ -66,13 +66,14 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units: p <= 256 between resca
 // Tile shape per head dimension.
 //
 // LDS holds two stages; each stage has a K region and a V region, both
-// row-major [BN keys][D] with padded rows.  The K row stride is 4 dwords past
-// a multiple of 32 banks, so the 8 lanes of one ds_read_b128 pass (8 rows)
-// hit distinct banks; the V row stride is 8 dwords past, so the 4 rows x 32
-// bytes that one 16-lane ds_read_b64_tr_b16 pass touches hit distinct banks.
-// Tiles are filled by direct global->LDS buffer loads, 64 lanes x 16 bytes
-// per instruction, one 16-byte "slot" per lane; pad slots receive a duplicate
-// chunk that is never read.
+// row-major [BN keys][D] with padded rows.  gfx950's LDS has 64 banks of 4
+// bytes (256 bytes per clock, measured).  A ds_read_b128 pass serves 16 lanes
+// (16 rows here), so the K row stride is an odd multiple of 4 dwords; a
+// ds_read_b64_tr_b16 pass serves 32 lanes (4 rows x 64 bytes here), so the V
+// row stride is an odd multiple of 16 dwords.  Both make the operand reads
+// bank-conflict free.  Tiles are filled by direct global->LDS buffer loads,
+// 64 lanes x 16 bytes per instruction, one 16-byte "slot" per lane; pad slots
+// receive a duplicate chunk that is never read.
 template <int D>
 struct TileCfg {
   static constexpr int kWaves = 4;
@@ -81,7 +82,7 @@ struct TileCfg {
   static constexpr int BN = (D >= 256) ? 32 : 64;        // keys per K/V tile
   static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
   static constexpr int KCP = kChunks + 1;                // K row, in 16-byte slots
-  static constexpr int VCP = kChunks + 2;                // V row, in 16-byte slots
+  static constexpr int VCP = kChunks + 4;                // V row, in 16-byte slots
   static constexpr int KS = 8 * KCP;                     // K row stride (elements)
   static constexpr int VS = 8 * VCP;                     // V row stride (elements)
   static constexpr int kKInst = (BN * KCP + 63) / 64;    // direct-load instructions per K tile
@@ -93,7 +94,7 @@ struct TileCfg {
   static constexpr int kVInstPerWave = (kVInst + kWaves - 1) / kWaves;
   static constexpr int kMinWavesPerEU = (D >= 256) ? 1 : 2;
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile sizes must be multiples of 32");
-  static_assert((KS / 2) % 32 == 4 && (VS / 2) % 32 == 8, "bank-conflict-free strides");
+  static_assert((KS / 2) % 8 == 4 && (VS / 2) % 32 == 16, "bank-conflict-free strides");
 };
 
 template <bool BF16>
