@@ -25,12 +25,11 @@
 //    ONE query row: the running max / sum / rescale factor are per-lane
 //    scalars and a row reduction is an in-lane reduction plus one exchange
 //    between lanes l and l+32.
-//  * K tiles are staged row-major in LDS, V tiles transposed (d-major) with
-//    the keys of each 16-key group stored in the order that makes one lane's
-//    8 B-operand keys one contiguous 16-byte LDS read.  Rows are padded by
-//    16 bytes so that 16 consecutive lanes reading 16 different rows hit
-//    distinct banks.  K/V tiles are double-buffered: the global loads of tile
-//    t+1 are in flight while tile t is computed, one barrier per tile.
+//  * K and V tiles are copied HBM -> LDS by direct buffer loads (no register
+//    staging), row-major with padded rows that make every operand read
+//    bank-conflict free; V reaches the MFMA as V^T through the LDS transpose
+//    read ds_read_b64_tr_b16.  Two stages: the loads of tile t+1 are in
+//    flight while tile t is computed, one barrier per tile.
 //  * Online softmax in the log2 domain: t = s * scale * log2(e), p = 2^(t - m).
 //    The running maximum m is only raised when a tile's maximum exceeds it
 //    by more than RESCALE_THRESHOLD (p then stays <= 2^threshold).  Because
