@@ -41,6 +41,9 @@ def compile_flags() -> list:
         # Device code only: no NaN operands are expected, so max() needs no
         # NaN-quieting copies of its inputs.
         "-Xarch_device", "-fno-honor-nans",
+        # Keep MFMA accumulators in architectural VGPRs (the softmax reads and
+        # rescales them with VALU instructions; AGPR copies would cost more).
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-I", os.path.join(ROOT, "include"),
         "-I", os.path.join(PKG, "csrc"),
     ]

@@ -47,6 +47,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace eta {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -91,6 +93,13 @@ struct TileCfg {
   static constexpr int kStage = kKElems + kVElems;       // one stage (elements)
   static constexpr int kKInstPerWave = (kKInst + kWaves - 1) / kWaves;
   static constexpr int kVInstPerWave = (kVInst + kWaves - 1) / kWaves;
+  // d = 256: the Q tile lives in LDS (read as the B operand like K), so that
+  // the 128 O accumulators fit in architectural VGPRs next to S and P.
+  static constexpr bool kQInLds = (D >= 256);
+  static constexpr int kQInst = (BM * KCP + 63) / 64;     // direct-load instructions for Q
+  static constexpr int kQInstPerWave = (kQInst + kWaves - 1) / kWaves;
+  static constexpr int kQElems = kQInLds ? kQInst * 64 * 8 : 0;
+  static constexpr int kLdsElems = 2 * kStage + kQElems;
   static constexpr int kMinWavesPerEU = (D >= 256) ? 1 : 2;
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile sizes must be multiples of 32");
   static_assert((KS / 2) % 8 == 4 && (VS / 2) % 32 == 16, "bank-conflict-free strides");
@@ -229,7 +238,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int NKK = BN / 16; // 16-key steps of the PV product
   constexpr int KCPR = D / 8;  // 16-byte chunks per row
 
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::kLdsElems];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -248,14 +257,28 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const uint16_t* Kh = K + ((int64_t)w.b * Nk * Hkv + hkv) * D;
   const uint16_t* Vh = V + ((int64_t)w.b * Nk * Hkv + hkv) * D;
 
-  // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop.
-  u32x4_t qf[NKS];
-  {
+  // ---- Q (B operand of S^T = K Q^T): fragments resident in VGPRs for the
+  // whole loop, or (d = 256) the workgroup's Q tile in LDS.  Rows past Nq
+  // read as zero (outside the descriptor's range).
+  u32x4_t qf[C::kQInLds ? 1 : NKS];
+  uint16_t* const qs = smem + 2 * C::kStage;
+  if constexpr (!C::kQInLds) {
     const rsrc_t qr = make_rsrc(Q + qo_off, span_bytes(qw0, 32, Nq, q_rs, D));
     const int voff = (int)(l32 * q_rs * 2) + 16 * hh;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = buf_load16(qr, voff + 32 * ks);
+  } else {
+    const int64_t q0_off = ((int64_t)w.b * Nq + q0) * q_rs + (int64_t)w.hq * D;
+    const rsrc_t qr = make_rsrc(Q + q0_off, span_bytes(q0, BM, Nq, q_rs, D));
+#pragma unroll
+    for (int i = 0; i < C::kQInstPerWave; ++i) {
+      const int j = wave + C::kWaves * i;
+      const int sl = 64 * j + lane;
+      const int row = min(sl / C::KCP, BM - 1), c = min(sl % C::KCP, C::kChunks - 1);
+      if (j < C::kQInst) buf_load_lds16(qr, qs + 512 * j, (int)(row * q_rs * 2) + 16 * c);
+    }
   }
+  const int q_rd = (wave * 32 + l32) * KS + 8 * hh;  // this lane's Q row in LDS
 
   // ---- Key range of the workgroup and of this wave.
   int kv_end = Nk;
@@ -331,7 +354,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           const u32x4_t a = *reinterpret_cast<const u32x4_t*>(st + k_rd + kb * 32 * KS + 16 * ks);
-          s[kb] = mfma_32x32x16<BF16>(a, qf[ks], s[kb]);
+          u32x4_t b;
+          if constexpr (C::kQInLds)
+            b = *reinterpret_cast<const u32x4_t*>(qs + q_rd + 16 * ks);
+          else
+            b = qf[ks];
+          s[kb] = mfma_32x32x16<BF16>(a, b, s[kb]);
         }
       }
       if (prescale) {  // scale <= 0: take the max of s*c directly
@@ -391,25 +419,32 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       // feeds keys {4hh..4hh+3, 8+4hh..8+4hh+3}, which registers
       // 8*(kk%2)..+7 of S^T block kk/2 hold.  The A operand (V^T, 8 keys at
       // one column) comes from two LDS transpose reads of row-major V.
-      const bool split = CAUSAL && need_mask;
+      // Causal tiles that cross the diagonal feed P as hi + lo halves (two
+      // MFMAs per step); the choice is made once per tile, not per MFMA.
+      auto pv_product = [&](auto with_lo) {
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const int kb = kk >> 1, r0 = 8 * (kk & 1);
-        f32x8_t pv;
+        for (int kk = 0; kk < NKK; ++kk) {
+          const int kb = kk >> 1, r0 = 8 * (kk & 1);
+          f32x8_t pv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = s[kb][r0 + e];
-        const u32x4_t phi = pack8<BF16>(pv);
-        u32x4_t plo = u32x4_t{0, 0, 0, 0};
-        if (split) plo = pack8<BF16>(pv - unpack8<BF16>(phi));
+          for (int e = 0; e < 8; ++e) pv[e] = s[kb][r0 + e];
+          const u32x4_t phi = pack8<BF16>(pv);
+          u32x4_t plo;
+          if constexpr (decltype(with_lo)::value) plo = pack8<BF16>(pv - unpack8<BF16>(phi));
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const u32x2_t x0 = lds_read_tr4(st + v_rd + 16 * kk * VS + 32 * db);
-          const u32x2_t x1 = lds_read_tr4(st + v_rd + (16 * kk + 8) * VS + 32 * db);
-          const u32x4_t a = {x0[0], x0[1], x1[0], x1[1]};
-          oacc[db] = mfma_32x32x16<BF16>(a, phi, oacc[db]);
-          if (split) oacc[db] = mfma_32x32x16<BF16>(a, plo, oacc[db]);
+          for (int db = 0; db < NDB; ++db) {
+            const u32x2_t x0 = lds_read_tr4(st + v_rd + 16 * kk * VS + 32 * db);
+            const u32x2_t x1 = lds_read_tr4(st + v_rd + (16 * kk + 8) * VS + 32 * db);
+            const u32x4_t a = {x0[0], x0[1], x1[0], x1[1]};
+            oacc[db] = mfma_32x32x16<BF16>(a, phi, oacc[db]);
+            if constexpr (decltype(with_lo)::value) oacc[db] = mfma_32x32x16<BF16>(a, plo, oacc[db]);
+          }
         }
-      }
+      };
+      if (CAUSAL && need_mask)
+        pv_product(std::true_type{});
+      else
+        pv_product(std::false_type{});
     }
 
     __builtin_amdgcn_s_waitcnt(0);  // tile t+1 has landed in LDS
