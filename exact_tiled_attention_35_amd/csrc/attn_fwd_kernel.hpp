@@ -337,7 +337,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tile 0 have landed
   __syncthreads();
 
-  for (int t = 0; t < nt; ++t) {
+  // Tile t: tiles before nf are visible to every row of the workgroup and
+  // take a body without any masking code; the rest (causal diagonal, ragged
+  // end) take the masked body.  Separate loops keep the lean body's register
+  // allocation free of the masked body's extra state.
+  auto tile = [&](int t, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
     const int j0 = t * BN;
     // Tile t+1 streams into the other stage while this one is computed (that
     // stage was last read in iteration t-1, before the barrier that ended it).
@@ -368,7 +373,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       }
 
       // Mask keys past the end and (causal) above the diagonal.
-      const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + diag);
+      const bool need_mask =
+          kMasked && ((j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + diag));
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -449,7 +455,13 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     __builtin_amdgcn_s_waitcnt(0);  // tile t+1 has landed in LDS
     __syncthreads();
-  }
+  };
+  int nf = Nk / BN;
+  if (CAUSAL) nf = min(nf, max(0, (q0 + diag + 1) / BN));
+  nf = min(nf, nt);
+  int t = 0;
+  for (; t < nf; ++t) tile(t, std::false_type{});
+  for (; t < nt; ++t) tile(t, std::true_type{});
 
   // ---- Epilogue: normalise, round, store O and the logsumexp.  Stores of
   // rows >= Nq fall outside the descriptors' ranges and are dropped.
