@@ -63,6 +63,9 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p <= 256 between rescales
+// Unmasked tiles keep the current running max unless a row's tile sum
+// exceeds this (every p then stays far inside the fp16 range of P).
+constexpr float kSumLimit = 32768.0f;
 
 // Tile shape per head dimension.
 //
@@ -101,6 +104,9 @@ struct TileCfg {
   static constexpr int kQElems = kQInLds ? kQInst * 64 * 8 : 0;
   static constexpr int kLdsElems = 2 * kStage + kQElems;
   static constexpr int kMinWavesPerEU = (D >= 256) ? 1 : 2;
+  // Unmasked tiles skip the tile maximum (see the kernel); at d = 256 the
+  // extra live state of that body costs more than the maximum it saves.
+  static constexpr bool kLeanTiles = (D <= 128);
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile sizes must be multiples of 32");
   static_assert((KS / 2) % 8 == 4 && (VS / 2) % 32 == 16, "bank-conflict-free strides");
 };
@@ -337,12 +343,80 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tile 0 have landed
   __syncthreads();
 
-  // Tile t: tiles before nf are visible to every row of the workgroup and
-  // take a body without any masking code; the rest (causal diagonal, ragged
-  // end) take the masked body.  Separate loops keep the lean body's register
-  // allocation free of the masked body's extra state.
-  auto tile = [&](int t, auto masked) {
-    constexpr bool kMasked = decltype(masked)::value;
+  // S^T = K Q^T for BN keys x 32 queries, from the K tile at `st`.
+  auto compute_s = [&](const uint16_t* st, f32x16_t (&s)[NKB]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(st + k_rd + kb * 32 * KS + 16 * ks);
+        u32x4_t b;
+        if constexpr (C::kQInLds)
+          b = *reinterpret_cast<const u32x4_t*>(qs + q_rd + 16 * ks);
+        else
+          b = qf[ks];
+        s[kb] = mfma_32x32x16<BF16>(a, b, s[kb]);
+      }
+    }
+    if (prescale) {  // scale <= 0: take the max of s*c directly
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] *= c_log2;
+    }
+  };
+
+  // Tile row maximum (in-lane, then across the two lane halves); m is raised
+  // when the tile max exceeds it by more than `threshold`, and what was
+  // accumulated is rescaled.
+  auto raise_max = [&](const f32x16_t (&s)[NKB], float threshold) {
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) tmax = max3(tmax, s[kb][r], s[kb][r + 1]);
+    }
+    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float tm = tmax * ce;
+    if (tm > m + threshold) {
+      const float alpha = exp2_fast(m - tm);
+      m = tm;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+  };
+
+  // p = 2^(s*c - m) in place; returns this lane half's sum of the unrounded p.
+  auto exponentiate = [&](f32x16_t (&s)[NKB], auto m_finite) {
+    const float mb = (decltype(m_finite)::value || m != -INFINITY) ? m : 0.f;
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = exp2_fast(__builtin_fmaf(s[kb][r], ce, -mb));
+        const float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], ce, -mb));
+        s[kb][r] = p0;
+        s[kb][r + 1] = p1;
+        ps0 += p0;
+        ps1 += p1;
+      }
+    }
+    return ps0 + ps1;
+  };
+
+  // Tile t.  Mode kLean: every key visible to every row and m already
+  // finite -- the scores are exponentiated against the current m without a
+  // tile maximum; a partial row sum above kSumLimit (a score far above m,
+  // rare) sends the wave through the maximum path for this tile, recomputing S
+  // from the K tile still in LDS.  Mode kFull: every key visible, tile
+  // maximum first.  Mode kMasked: tile maximum first, per-element masking
+  // where the tile crosses the causal diagonal or the ragged end.  The same m
+  // enters the row sum and O in every case, so both are exact.
+  constexpr int kLean = 0, kFull = 1, kMasked = 2;
+  auto tile = [&](int t, auto mode) {
+    constexpr int kMode = decltype(mode)::value;
     const int j0 = t * BN;
     // Tile t+1 streams into the other stage while this one is computed (that
     // stage was last read in iteration t-1, before the barrier that ended it).
@@ -350,76 +424,36 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* st = smem + (t & 1) * C::kStage;
 
     if (j0 < w_end) {  // wave-uniform: skip tiles above this wave's diagonal
-      // S^T = K Q^T for BN keys x 32 queries.
       f32x16_t s[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(st + k_rd + kb * 32 * KS + 16 * ks);
-          u32x4_t b;
-          if constexpr (C::kQInLds)
-            b = *reinterpret_cast<const u32x4_t*>(qs + q_rd + 16 * ks);
-          else
-            b = qf[ks];
-          s[kb] = mfma_32x32x16<BF16>(a, b, s[kb]);
+      compute_s(st, s);
+      bool need_mask = false;
+      float psum;
+      if constexpr (kMode == kLean) {
+        psum = exponentiate(s, std::true_type{});
+        if (__builtin_amdgcn_ballot_w64(!(psum <= kSumLimit)) != 0) {
+          compute_s(st, s);
+          raise_max(s, 0.0f);
+          psum = exponentiate(s, std::true_type{});
         }
-      }
-      if (prescale) {  // scale <= 0: take the max of s*c directly
+      } else {
+        // Mask keys past the end and (causal) above the diagonal.
+        need_mask = kMode == kMasked &&
+                    ((j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + diag));
+        if (need_mask) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[kb] *= c_log2;
-      }
-
-      // Mask keys past the end and (causal) above the diagonal.
-      const bool need_mask =
-          kMasked && ((j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + diag));
-      if (need_mask) {
+          for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool vis = j < Nk && (!CAUSAL || j <= my_q + diag);
-            s[kb][r] = vis ? s[kb][r] : -INFINITY;
+            for (int r = 0; r < 16; ++r) {
+              const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+              const bool vis = j < Nk && (!CAUSAL || j <= my_q + diag);
+              s[kb][r] = vis ? s[kb][r] : -INFINITY;
+            }
           }
         }
+        raise_max(s, kRescaleThreshold);
+        psum = exponentiate(s, std::false_type{});
       }
-
-      // Tile row maximum: in-lane, then across the two lane halves.
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) tmax = max3(tmax, s[kb][r], s[kb][r + 1]);
-      }
-      tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float tm = tmax * ce;
-      if (tm > m + kRescaleThreshold) {  // raise m; rescale what was accumulated
-        const float alpha = exp2_fast(m - tm);
-        m = tm;
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      }
-      const float mb = (m == -INFINITY) ? 0.f : m;
-
-      // p = 2^(s*c - m); partial row sums from the unrounded p.
-      float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = exp2_fast(__builtin_fmaf(s[kb][r], ce, -mb));
-          const float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], ce, -mb));
-          s[kb][r] = p0;
-          s[kb][r + 1] = p1;
-          ps0 += p0;
-          ps1 += p1;
-        }
-      }
-      lsum += ps0 + ps1;
+      lsum += psum;
 
       // O^T += V^T P^T.  PV step kk covers keys 16kk..16kk+15; lane half hh
       // feeds keys {4hh..4hh+3, 8+4hh..8+4hh+3}, which registers
@@ -456,12 +490,24 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     __builtin_amdgcn_s_waitcnt(0);  // tile t+1 has landed in LDS
     __syncthreads();
   };
+  // Tiles before nf are visible to every row of the workgroup: the first of
+  // them (m still -inf) takes the full body, the rest the lean one; tiles
+  // from nf on take the masked body.  Separate loops keep each body's
+  // register allocation free of the others' state.
   int nf = Nk / BN;
   if (CAUSAL) nf = min(nf, max(0, (q0 + diag + 1) / BN));
   nf = min(nf, nt);
+  using LeanMode = std::integral_constant<int, kLean>;
+  using FullMode = std::integral_constant<int, kFull>;
+  using MaskedMode = std::integral_constant<int, kMasked>;
   int t = 0;
-  for (; t < nf; ++t) tile(t, std::false_type{});
-  for (; t < nt; ++t) tile(t, std::true_type{});
+  if constexpr (C::kLeanTiles) {
+    if (nf > 0) tile(t++, FullMode{});
+    for (; t < nf; ++t) tile(t, LeanMode{});
+  } else {
+    for (; t < nf; ++t) tile(t, FullMode{});
+  }
+  for (; t < nt; ++t) tile(t, MaskedMode{});
 
   // ---- Epilogue: normalise, round, store O and the logsumexp.  Stores of
   // rows >= Nq fall outside the descriptors' ranges and are dropped.

@@ -189,6 +189,28 @@ def test_one_hot_dominant_key():
     assert (out[0, i, 0].double() - v[0, jstar, 0].double()).abs().max() <= 1e-6
 
 
+@pytest.mark.parametrize("d,dt", [(64, "fp16"), (128, "bf16"), (256, "fp16")])
+@pytest.mark.parametrize("slope", [-0.5, 0.05, 0.4, 3.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores(d, dt, slope, causal):
+    # Scores that climb along the key axis by `slope` (log2 units per key) on
+    # top of the random ones: every later tile holds scores above the running
+    # maximum, by a little (0.05), by a lot per tile (0.4) or by a lot per key
+    # (3.0), so the running maximum, and with it O and the row sum, must be
+    # raised again and again; -0.5 keeps the first tile's maximum throughout.
+    N = 300
+    q, k, v = make_qkv(1, N, N, 2, 1, d, dt, 1.0, 405)
+    scale = 1.0 / math.sqrt(d)
+    q = q.clone()
+    k = k.clone()
+    q[..., 0] = 1.0
+    ramp = slope * torch.arange(N, dtype=torch.float64) / (scale * math.log2(math.e))
+    k[0, :, 0, 0] = ramp.to(k.dtype)
+    out, lse = gpu_attn(q, k, v, scale, causal)
+    O, L = oracle.attention(q, k, v, scale, causal)
+    assert_close(out, lse, O, L, f"slope {slope}")
+
+
 def test_run_to_run_bitwise_determinism():
     q, k, v = make_qkv(2, 700, 700, 8, 2, 128, "bf16", 1.0, 404)
     a = gpu_attn(q, k, v, 0.088, True)
