@@ -425,7 +425,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     if (j0 < w_end) {  // wave-uniform: skip tiles above this wave's diagonal
       f32x16_t s[NKB];
+      // The matrix phases (S^T here, O^T below) run at raised wave priority,
+      // so that on a SIMD shared with a wave in its softmax phase the MFMA
+      // issues first and that wave's VALU work fills the remaining slots.
+      __builtin_amdgcn_s_setprio(1);
       compute_s(st, s);
+      __builtin_amdgcn_s_setprio(0);
       bool need_mask = false;
       float psum;
       if constexpr (kMode == kLean) {
@@ -481,10 +486,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           }
         }
       };
+      __builtin_amdgcn_s_setprio(1);
       if (CAUSAL && need_mask)
         pv_product(std::true_type{});
       else
         pv_product(std::false_type{});
+      __builtin_amdgcn_s_setprio(0);
     }
 
     __builtin_amdgcn_s_waitcnt(0);  // tile t+1 has landed in LDS
