@@ -38,10 +38,11 @@ def assert_close(out, lse, O, L, what=""):
     fin = np.isfinite(L)
     assert np.array_equal(np.isfinite(lg), fin), what
     assert np.all(lg[~fin] == -np.inf), what
+    lerr = 0.0
     if fin.any():
         lerr = np.abs(lg[fin] - L[fin]).max()
         assert lerr <= LSE_ABS, f"{what}: lse max-abs {lerr:.3e}"
-    return float(err.max()), float(err.mean())
+    return float(err.max()), float(err.mean()), float(lerr)
 
 
 # (B, Hq, Hkv, Nq, Nk, d, dtype, causal): several tiles, ragged tails,
@@ -252,9 +253,9 @@ def test_workload_full_size(name):
         for (b, h) in sample_heads(w):
             rows = sample_rows(w.Nq, rng)
             O, L = oracle.attention_rows(q, k, v, w.scale, w.causal, b, h, rows)
-            mx, mn = assert_close(out[b, rows, h], lse[b, h, rows], O, L, f"{name} b{b} h{h}")
-            errs.append((mx, mn))
-    print(f"[parity] {name}: worst sampled max-abs {max(e[0] for e in errs):.3e}", flush=True)
+            errs.append(assert_close(out[b, rows, h], lse[b, h, rows], O, L, f"{name} b{b} h{h}"))
+    print(f"[parity] {name}: worst sampled max-abs {max(e[0] for e in errs):.3e}, "
+          f"mean-abs {max(e[1] for e in errs):.3e}, lse {max(e[2] for e in errs):.3e}", flush=True)
 
     # Properties of every row at full size: outputs are convex combinations of
     # the visible V rows (within rounding), and every lse is finite and at
