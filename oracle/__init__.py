@@ -15,6 +15,7 @@ written out, per (batch, query head).
 
 from .exact import (  # noqa: F401
     attention,
+    attention_backward,
     attention_rows,
     kv_head_of,
     allowed_keys,

@@ -37,6 +37,16 @@ Readings where the pages are silent (each is listed in the design notes):
 * logsumexp: natural log of the sum of exp over the scaled, masked scores.
 * a query row with no visible key (causal, Nq > Nk) has output 0 and
   logsumexp -inf (the empty-sum limit).
+
+The backward pass (``attention_backward``): the pages say the library
+computes gradients (hysenlabs.com page, section "GPU-Abdeckung: Ampere,
+Hopper und AMD-Backends" on the backward pass for head dimension 256;
+section "Von 2.0 bis 2.7" on a deterministic backward pass) and that its tests compare outputs *and
+gradients* with a reference (section "Tests, BSD-3-Clause und
+Zitierpraxis"); they do not write the gradients out.  Those are fixed by the
+mathematics: the derivatives of the forward definition above with respect
+to q, k and v for the loss L = sum(dout * out), written out by the chain
+rule with the full probability matrix (no tiling, no recomputation).
 """
 
 from __future__ import annotations
@@ -46,6 +56,7 @@ import numpy as np
 __all__ = [
     "attention",
     "attention_rows",
+    "attention_backward",
     "kv_head_of",
     "allowed_keys",
     "materialised_score_bytes",
@@ -197,3 +208,59 @@ def attention_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows):
     sigma = float(np.float32(scale))
     O, lse, _, _ = _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, False)
     return O, lse
+
+
+def _softmax_rows_backward(P, dP):
+    """Row-wise softmax Jacobian applied to dP: for p = softmax(s),
+    ds_j = p_j (dp_j - sum_k p_k dp_k).  Returns (dS, D) with D the row sums
+    sum_k p_k dp_k."""
+    D = (P * dP).sum(axis=1)
+    return P * (dP - D[:, None]), D
+
+
+def attention_backward(q, k, v, dout, scale: float, causal: bool = False):
+    """Exact gradients of L = sum(dout * attention(q, k, v)) in fp64.
+
+    Per (b, h) with KV head g, probabilities P (rows over the visible keys,
+    exactly as in ``attention``) and upstream gradient dO = dout[b, :, h, :]:
+
+      dV_g += P^T dO                      (the output is P V)
+      dP    = dO V_g^T                    (gradient w.r.t. the probabilities)
+      D_i   = sum_j P_ij dP_ij            (= dO_i . O_i)
+      dS    = P * (dP - D[:, None])       (softmax Jacobian applied row-wise)
+      dQ    = sigma * dS K_g              (s_ij = sigma q_i . k_j)
+      dK_g += sigma * dS^T Q
+
+    KV heads shared by a group of query heads (GQA/MQA) receive the sum over
+    the group.  Masked keys have P = 0, so they get no gradient, and rows with
+    no visible key contribute nothing.
+
+    Args: q [B, Nq, Hq, d]; k, v [B, Nk, Hkv, d]; dout like q (numpy arrays
+    or CPU torch tensors); scale as passed to the library (an fp32 value).
+
+    Returns (dq [B, Nq, Hq, d], dk [B, Nk, Hkv, d], dv [B, Nk, Hkv, d],
+    delta [B, Hq, Nq]) in fp64, where delta holds D.
+    """
+    q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    B, Nq, Nk, Hq, Hkv, d = _check_shapes(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError(f"dout{dout.shape} must match q{q.shape}")
+    sigma = float(np.float32(scale))
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    delta = np.zeros((B, Hq, Nq))
+    rows = np.arange(Nq)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            qh, kg, vg = q[b, :, h, :], k[b, :, g, :], v[b, :, g, :]
+            dO = dout[b, :, h, :]
+            _, _, _, P = _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, True)
+            dv[b, :, g, :] += P.T @ dO
+            dP = dO @ vg.T
+            dS, D = _softmax_rows_backward(P, dP)
+            dq[b, :, h, :] = sigma * (dS @ kg)
+            dk[b, :, g, :] += sigma * (dS.T @ qh)
+            delta[b, h, :] = D
+    return dq, dk, dv, delta
