@@ -1,10 +1,19 @@
-"""Exact tiled attention forward for AMD MI355X (gfx950).
+"""Exact tiled attention (forward and backward) for AMD MI355X (gfx950).
 
 The computation runs in hand-written HIP kernels behind a C ABI
-(``include/attn.h``, built into ``libattn_fwd.so``); this package is the thin
+(``include/attn.h``, built into ``libattn.so``); this package is the thin
 Python binding over it.
 """
 
-from .attention import AttnError, attn_fwd, attn_fwd_ptr, attn_status_string, attn_version  # noqa: F401
+from .attention import (  # noqa: F401
+    AttnError,
+    attention,
+    attn_bwd,
+    attn_bwd_ptr,
+    attn_fwd,
+    attn_fwd_ptr,
+    attn_status_string,
+    attn_version,
+)
 
-__version__ = "0.1.0"
+__version__ = "0.2.0"

@@ -1,4 +1,4 @@
-"""ctypes loader for the HIP library ``libattn_fwd.so`` (C ABI in include/attn.h).
+"""ctypes loader for the HIP library ``libattn.so`` (C ABI in include/attn.h).
 
 There is no fallback: if the library is missing, ``load()`` raises.
 """
@@ -8,7 +8,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_fwd.so")
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 # attn_status values (include/attn.h).
 ATTN_OK = 0
@@ -42,6 +42,8 @@ def load() -> ctypes.CDLL:
     vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp]
     lib.attn_fwd.restype = ci
+    lib.attn_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, ci, ci, cf, ci, ci, vp]
+    lib.attn_bwd.restype = ci
     lib.attn_status_string.argtypes = [ci]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []

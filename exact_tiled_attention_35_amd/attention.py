@@ -1,9 +1,10 @@
 """Python binding of the C ABI: argument marshalling only.
 
-``attn_fwd`` checks that the torch tensors match the C ABI's layout
-contract, allocates the outputs with torch (device memory is torch's job),
-and calls the library's ``attn_fwd`` on torch's current HIP stream.  Every
-step of the computation runs in the HIP kernel.
+``attn_fwd`` and ``attn_bwd`` check that the torch tensors match the C
+ABI's layout contract, allocate the outputs with torch (device memory is
+torch's job), and call the library's entry points of the same names on
+torch's current HIP stream.  Every step of the computation runs in the HIP
+kernels.  ``attention`` wraps the two as a torch autograd function.
 """
 
 from __future__ import annotations
@@ -41,15 +42,7 @@ def attn_fwd_ptr(q: int, k: int, v: int, out: int, lse: int, B: int, Hq: int, Hk
                                 int(d), float(scale), int(bool(causal)), int(dtype), stream or None)
 
 
-def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: float | None = None,
-             causal: bool = False, out: torch.Tensor | None = None,
-             lse: torch.Tensor | None = None):
-    """Exact attention forward on the GPU.
-
-    q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d]; contiguous bf16 or fp16 tensors
-    on one HIP device.  ``softmax_scale`` defaults to 1/sqrt(d).
-    Returns (out [B, Nq, Hq, d] of q's dtype, lse [B, Hq, Nq] fp32).
-    """
+def _check_qkv(q, k, v):
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, N, H, d]")
     B, Nq, Hq, d = q.shape
@@ -63,6 +56,84 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: f
             raise ValueError(f"{name} must be on q's HIP device")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous [B, N, H, d]")
+    return B, Nq, Hq, Hkv, Nk, d
+
+
+def _check_like(name, t, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() \
+            or t.device != device:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+
+
+def attn_bwd_ptr(q: int, k: int, v: int, out: int, dout: int, lse: int, dq: int, dk: int,
+                 dv: int, delta: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
+                 scale: float, causal: bool, dtype: int, stream: int = 0) -> int:
+    """The C entry point with raw integer pointers; returns the attn_status."""
+    return _lib.load().attn_bwd(q or None, k or None, v or None, out or None, dout or None,
+                                lse or None, dq or None, dk or None, dv or None, delta or None,
+                                int(B), int(Hq), int(Hkv), int(Nq), int(Nk), int(d), float(scale),
+                                int(bool(causal)), int(dtype), stream or None)
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+             dout: torch.Tensor, lse: torch.Tensor, softmax_scale: float | None = None,
+             causal: bool = False):
+    """Exact attention backward on the GPU.
+
+    q, out, dout: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d]; lse: [B, Hq, Nq] fp32 --
+    ``out`` and ``lse`` as returned by ``attn_fwd`` for the same arguments.
+    Returns (dq like q, dk like k, dv like v, delta [B, Hq, Nq] fp32).
+    """
+    B, Nq, Hq, Hkv, Nk, d = _check_qkv(q, k, v)
+    _check_like("out", out, q.shape, q.dtype, q.device)
+    _check_like("dout", dout, q.shape, q.dtype, q.device)
+    _check_like("lse", lse, (B, Hq, Nq), torch.float32, q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        code = attn_bwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(), delta.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
+                            softmax_scale, causal, _DTYPE_CODE[q.dtype], stream)
+    if code != _lib.ATTN_OK:
+        raise AttnError(code)
+    return dq, dk, dv, delta
+
+
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, softmax_scale, causal):
+        out, lse = attn_fwd(q, k, v, softmax_scale, causal)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.softmax_scale, ctx.causal = softmax_scale, causal
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse = ctx.saved_tensors
+        dq, dk, dv, _ = attn_bwd(q, k, v, out, dout.contiguous(), lse, ctx.softmax_scale, ctx.causal)
+        return dq, dk, dv, None, None
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+              softmax_scale: float | None = None, causal: bool = False) -> torch.Tensor:
+    """Exact attention with autograd: ``attn_fwd`` forward, ``attn_bwd`` backward."""
+    return _Attention.apply(q, k, v, softmax_scale, causal)
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: float | None = None,
+             causal: bool = False, out: torch.Tensor | None = None,
+             lse: torch.Tensor | None = None):
+    """Exact attention forward on the GPU.
+
+    q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d]; contiguous bf16 or fp16 tensors
+    on one HIP device.  ``softmax_scale`` defaults to 1/sqrt(d).
+    Returns (out [B, Nq, Hq, d] of q's dtype, lse [B, Hq, Nq] fp32).
+    """
+    B, Nq, Hq, Hkv, Nk, d = _check_qkv(q, k, v)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
     if out is None:

@@ -1,4 +1,5 @@
-// C ABI of the exact tiled attention forward (declared in include/attn.h).
+// C ABI of the exact tiled attention forward, the status strings and the
+// version (declared in include/attn.h); the backward is in attn_bwd_api.hip.
 //
 // Host side only: argument validation (before any HIP call), a cached
 // per-device gfx950 check, choice of the kernel instance, grid size, and the
@@ -8,50 +9,20 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
-#include <cstring>
 
 #include "attn_fwd_kernel.hpp"
+#include "attn_host.hpp"
 
 namespace {
 
-constexpr const char* kVersion = "0.1.0 gfx950 exact-tiled-attention-fwd";
-constexpr int kMaxDevices = 64;
+using eta_host::aligned16;
+using eta_host::check_device;
+using eta_host::finite_bits;
+using eta_host::overlaps;
 
-// 0 = unknown, 1 = gfx950, 2 = other architecture.
-std::atomic<int> g_arch_state[kMaxDevices];
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
-  return pa < pb + nb && pb < pa + na;
-}
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-// Finite test on the bits, independent of floating-point compile flags.
-bool finite_bits(float x) {
-  uint32_t u;
-  std::memcpy(&u, &x, sizeof u);
-  return ((u >> 23) & 0xffu) != 0xffu;
-}
-
-int check_device() {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_NO_DEVICE;
-  int count = 0;
-  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0 || dev >= count) return ATTN_ERR_NO_DEVICE;
-  if (dev >= kMaxDevices) return ATTN_ERR_NO_DEVICE;
-  int st = g_arch_state[dev].load(std::memory_order_acquire);
-  if (st == 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_NO_DEVICE;
-    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
-    g_arch_state[dev].store(st, std::memory_order_release);
-  }
-  return st == 1 ? ATTN_OK : ATTN_ERR_NO_DEVICE;
-}
+constexpr const char* kVersion = "0.2.0 gfx950 exact-tiled-attention fwd+bwd";
 
 template <int D, bool BF16, bool CAUSAL>
 int launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,

@@ -1,0 +1,127 @@
+// C ABI of the exact tiled attention backward (declared in include/attn.h).
+//
+// Host side only: argument validation before any HIP call, the cached gfx950
+// check, and two asynchronous launches on the caller's stream: the dQ kernel
+// (which also writes delta) and then the dK/dV kernel (which reads it).
+// No device memory is allocated.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "attn.h"
+#include "attn_bwd_kernel.hpp"
+#include "attn_host.hpp"
+
+namespace {
+
+using eta_host::aligned16;
+using eta_host::check_device;
+using eta_host::finite_bits;
+using eta_host::overlaps;
+
+template <int D, bool BF16, bool CAUSAL>
+int launch_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
+               int Hkv, int Nq, int Nk, float scale, hipStream_t stream) {
+  using CQ = eta::DqCfg<D>;
+  using CK = eta::DkvCfg<D>;
+  const float c_log2 = scale * eta::kLog2e;
+  const int nqb = (Nq + CQ::BM - 1) / CQ::BM;
+  const int nkb = (Nk + CK::BK - 1) / CK::BK;
+  const int64_t tq = (int64_t)B * Hq * nqb, tk = (int64_t)B * Hkv * nkb;
+  if (tq > 0x7fffffff || tk > 0x7fffffff) return ATTN_ERR_BAD_SHAPE;
+  const auto* Q = static_cast<const uint16_t*>(q);
+  const auto* Kp = static_cast<const uint16_t*>(k);
+  const auto* Vp = static_cast<const uint16_t*>(v);
+  const auto* dO = static_cast<const uint16_t*>(dout);
+  if (tq > 0) {
+    hipLaunchKernelGGL((eta::attn_bwd_dq_kernel<D, BF16, CAUSAL>), dim3((int)tq),
+                       dim3(CQ::kThreads), 0, stream, Q, Kp, Vp, static_cast<const uint16_t*>(out),
+                       dO, lse, static_cast<uint16_t*>(dq), delta, Hq, Hkv, Nq, Nk, nqb, (int)tq,
+                       scale, c_log2);
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+  }
+  hipLaunchKernelGGL((eta::attn_bwd_dkdv_kernel<D, BF16, CAUSAL>), dim3((int)tk),
+                     dim3(CK::kThreads), 0, stream, Q, Kp, Vp, dO, lse, delta,
+                     static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), Hq, Hkv, Nq, Nk, nkb,
+                     (int)tk, scale, c_log2);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+template <int D>
+int dispatch_bwd(bool bf16, bool causal, const void* q, const void* k, const void* v,
+                 const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                 float* delta, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
+                 hipStream_t s) {
+#define ETA_BWD_ARGS q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, s
+  if (bf16) {
+    return causal ? launch_bwd<D, true, true>(ETA_BWD_ARGS) : launch_bwd<D, true, false>(ETA_BWD_ARGS);
+  }
+  return causal ? launch_bwd<D, false, true>(ETA_BWD_ARGS) : launch_bwd<D, false, false>(ETA_BWD_ARGS);
+#undef ETA_BWD_ARGS
+}
+
+}  // namespace
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        float* delta, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                        int causal, int dtype, void* stream) {
+  // 1. shape
+  if (B < 0 || Nq < 0 || Hq < 1 || Hkv < 1 || Nk < 1 || d < 1) return ATTN_ERR_BAD_SHAPE;
+  // 2. empty batch: nothing to do
+  if (B == 0) return ATTN_OK;
+  const double q_elems = (double)B * Nq * Hq * d, kv_elems = (double)B * Nk * Hkv * d;
+  if (q_elems > 0x1p60 || kv_elems > 0x1p60) return ATTN_ERR_BAD_SHAPE;
+  // The kernels address 128-row windows of q-shaped and k-shaped tensors
+  // with 32-bit byte offsets, and grids of one workgroup per 128 rows.
+  if ((double)128 * Hq * d * 2 >= 0x1p31 || (double)128 * Hkv * d * 2 >= 0x1p31)
+    return ATTN_ERR_BAD_SHAPE;
+  if ((double)B * Hq * ((Nq + 127) / 128) > 0x7fffffff ||
+      (double)B * Hkv * ((Nk + 127) / 128) > 0x7fffffff)
+    return ATTN_ERR_BAD_SHAPE;
+  // 3. null pointers (with Nq == 0 only k, v, dk and dv are touched)
+  if (!k || !v || !dk || !dv) return ATTN_ERR_NULL_POINTER;
+  const bool rows = Nq > 0;
+  if (rows && (!q || !out || !dout || !lse || !dq || !delta)) return ATTN_ERR_NULL_POINTER;
+  // 4. GQA ratio, 5. head dimension, 6. element type, 7. scale
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA_RATIO;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED_HDIM;
+  if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
+  if (!finite_bits(scale)) return ATTN_ERR_BAD_SCALE;
+  // 8. alignment
+  if (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_MISALIGNED;
+  if (rows && (!aligned16(q) || !aligned16(out) || !aligned16(dout) || !aligned16(lse) ||
+               !aligned16(dq) || !aligned16(delta)))
+    return ATTN_ERR_MISALIGNED;
+  // 9. aliasing: no output overlaps an input or another output
+  const size_t qb = rows ? (size_t)q_elems * 2 : 0, kvb = (size_t)kv_elems * 2;
+  const size_t vb = rows ? (size_t)B * Hq * Nq * sizeof(float) : 0;
+  const void* in_p[6] = {q, k, v, out, dout, lse};
+  const size_t in_n[6] = {qb, kvb, kvb, qb, qb, vb};
+  const void* out_p[4] = {dq, dk, dv, delta};
+  const size_t out_n[4] = {qb, kvb, kvb, vb};
+  for (int i = 0; i < 4; ++i) {
+    if (out_n[i] == 0) continue;
+    for (int j = 0; j < 6; ++j)
+      if (in_n[j] && overlaps(out_p[i], out_n[i], in_p[j], in_n[j])) return ATTN_ERR_ALIASING;
+    for (int j = i + 1; j < 4; ++j)
+      if (out_n[j] && overlaps(out_p[i], out_n[i], out_p[j], out_n[j])) return ATTN_ERR_ALIASING;
+  }
+  // 10. device
+  const int dev_status = check_device();
+  if (dev_status != ATTN_OK) return dev_status;
+  // 11. launch
+  const bool bf16 = dtype == ATTN_DTYPE_BF16;
+  const bool c = causal != 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (d) {
+    case 64:
+      return dispatch_bwd<64>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, s);
+    case 128:
+      return dispatch_bwd<128>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, s);
+    default:
+      return dispatch_bwd<256>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, s);
+  }
+}

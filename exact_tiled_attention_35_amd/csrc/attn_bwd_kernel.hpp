@@ -1,0 +1,481 @@
+// Exact attention backward for gfx950 (MI355X, CDNA4).
+//
+// Gradients of L = sum(dout * out) for out = softmax(Q K^T * scale) V, per
+// (batch, query head), from the forward's out and logsumexp.  The pages state
+// that the library computes gradients, that a deterministic backward pass
+// exists (hysenlabs.com, "FlashAttention: exakte Attention-Kernel fuer CUDA
+// und ROCm", section "Von 2.0 bis 2.7") and that its tests compare gradients
+// with a reference (section "Tests, BSD-3-Clause und Zitierpraxis"); the
+// formulas are the chain rule of the forward definition:
+//
+//   P = exp(S * scale - lse)            recomputed tile by tile, never stored
+//   D_i = sum_c dO_ic O_ic              (= sum_j P_ij dP_ij)
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),
+//   dQ = scale * dS K,   dK = scale * dS^T Q.
+//
+// Two kernels, no atomics and no workspace, so results are bitwise
+// reproducible run to run:
+//  * attn_bwd_dq_kernel: one workgroup per 128 query rows of one (b, head),
+//    4 waves x 32 rows, looping over key tiles.  Per tile and wave:
+//        S^T  = K Q^T    (A = K rows from LDS, B = Q^T in VGPRs)
+//        dP^T = V dO^T   (A = V rows from LDS, B = dO^T in VGPRs)
+//        dQ^T += K^T dS^T (A = K^T by LDS transpose reads, B = dS^T packed
+//                          from the accumulators)
+//    Each lane owns one query row, so lse and D are per-lane scalars.  The
+//    kernel first computes D for its rows and stores it (the dK/dV kernel
+//    reads it).
+//  * attn_bwd_dkdv_kernel: one workgroup per 128 keys of one (b, KV head),
+//    4 waves x 32 keys, looping over the query heads of the GQA group and
+//    their query tiles.  The roles of queries and keys are swapped relative
+//    to the dQ kernel:
+//        S    = Q K^T    (A = Q rows from LDS, B = K^T in VGPRs)
+//        dP   = dO V^T   (A = dO rows from LDS, B = V^T in VGPRs)
+//        dV^T += dO^T P  (A = dO^T by LDS transpose reads, B = P packed)
+//        dK^T += Q^T dS  (A = Q^T by LDS transpose reads, B = dS packed)
+//    Each lane owns one key; lse and D of the tile's query rows come from
+//    LDS.  The GQA group's sum happens in registers.
+// P is rounded to the element type for the dV product and dS for the dQ and
+// dK products (fp32 accumulation throughout).
+#pragma once
+
+#include <type_traits>
+
+#include "gfx950_ops.hpp"
+
+namespace eta {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// LDS row strides (16-byte chunks per row): "row" tiles feed ds_read_b128
+// operand reads (odd multiple of 4 dwords), "tr" tiles feed the transpose
+// reads (odd multiple of 16 dwords); see the forward kernel's tile notes.
+template <int D>
+struct BwdLayout {
+  static constexpr int kChunks = D / 8;
+  static constexpr int RCP = kChunks + 1;  // row tiles
+  static constexpr int TCP = kChunks + 4;  // transpose-read tiles
+  static constexpr int RS = 8 * RCP;       // row stride, elements
+  static constexpr int TS = 8 * TCP;
+  static_assert((RS / 2) % 8 == 4 && (TS / 2) % 32 == 16, "bank-conflict-free strides");
+  // Elements of an R-row tile filled by 64-lane direct loads.
+  template <int R>
+  static constexpr int row_elems() { return ((R * RCP + 63) / 64) * 512; }
+  template <int R>
+  static constexpr int tr_elems() { return ((R * TCP + 63) / 64) * 512; }
+};
+
+template <int D>
+struct DqCfg {
+  static constexpr int kWaves = 4, kThreads = 256, BM = 128;
+  static constexpr int BN = (D >= 256) ? 32 : 64;  // keys per tile
+  using L = BwdLayout<D>;
+  static constexpr int kKRow = L::template row_elems<BN>();
+  static constexpr int kKTr = L::template tr_elems<BN>();
+  static constexpr int kVRow = kKRow;
+  static constexpr int kStage = kKRow + kKTr + kVRow;
+  static constexpr int kLdsElems = 2 * kStage;
+  static constexpr int kMinWavesPerEU = 1;
+};
+
+template <int D>
+struct DkvCfg {
+  static constexpr int kWaves = 4, kThreads = 256, BK = 128;
+  static constexpr int BQ = (D >= 256) ? 32 : 64;  // query rows per tile
+  using L = BwdLayout<D>;
+  static constexpr int kRow = L::template row_elems<BQ>();
+  static constexpr int kTr = L::template tr_elems<BQ>();
+  static constexpr int kVec = 512;  // 1 KB: lse or D of the tile (64 lanes x 16 B)
+  static constexpr int kStage = 2 * kRow + 2 * kTr + 2 * kVec;
+  static constexpr int kLdsElems = 2 * kStage;
+  static constexpr int kMinWavesPerEU = 1;
+  static_assert(BQ * 4 <= kVec * 2, "lse/D slots cover the tile");
+};
+
+// Direct-load slot offsets for an R-row tile with CP chunks per row and a
+// global row stride of rs elements: this wave issues instructions
+// j = wave, wave + 4, ...; lane -> slot 64 j + lane -> (row, chunk).
+template <int R, int CP, int D, int NI>
+__device__ __forceinline__ void tile_offsets(int wave, int lane, int64_t rs, int (&off)[NI]) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int sl = 64 * (wave + 4 * i) + lane;
+    const int row = min(sl / CP, R - 1), c = min(sl % CP, D / 8 - 1);
+    off[i] = (int)(row * rs * 2) + 16 * c;
+  }
+}
+
+template <int NINST, int NI>
+__device__ __forceinline__ void tile_issue(rsrc_t r, uint16_t* dst, int wave, const int (&off)[NI]) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int j = wave + 4 * i;
+    if (j < NINST) buf_load_lds16(r, dst + 512 * j, off[i]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and D).
+// ---------------------------------------------------------------------------
+template <int D, bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(DqCfg<D>::kThreads, DqCfg<D>::kMinWavesPerEU)
+attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
+                   const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+                   uint16_t* __restrict__ dQ, float* __restrict__ Dlt, int Hq, int Hkv, int Nq,
+                   int Nk, int nqb, int total, float scale, float c_log2) {
+  using C = DqCfg<D>;
+  using L = typename C::L;
+  constexpr int BN = C::BN, BM = C::BM, RS = L::RS, TS = L::TS;
+  constexpr int NKS = D / 16, NKB = BN / 32, NDB = D / 32, NKK = BN / 16;
+  constexpr int kRowInst = C::kKRow / 512, kTrInst = C::kKTr / 512;
+  constexpr int kRowPW = (kRowInst + 3) / 4, kTrPW = (kTrInst + 3) / 4;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::kLdsElems];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const WorkItem w = map_workgroup<CAUSAL>(blockIdx.x, total, nqb, Hq);
+  const int hkv = w.hq / (Hq / Hkv);
+  const int q0 = w.qblk * BM, qw0 = q0 + wave * 32, my_q = qw0 + l32;
+  const int diag = Nk - Nq;
+
+  const int64_t q_rs = (int64_t)Hq * D, kv_rs = (int64_t)Hkv * D;
+  const int64_t qo_off = ((int64_t)w.b * Nq + qw0) * q_rs + (int64_t)w.hq * D;
+  const uint16_t* Kh = K + ((int64_t)w.b * Nk * Hkv + hkv) * D;
+  const uint16_t* Vh = V + ((int64_t)w.b * Nk * Hkv + hkv) * D;
+
+  // Q^T and dO^T fragments (B operands), O for D.  Rows >= Nq read as 0.
+  const int rspan = span_bytes(qw0, 32, Nq, q_rs, D);
+  const rsrc_t qr = make_rsrc(Q + qo_off, rspan);
+  const rsrc_t dor = make_rsrc(dO + qo_off, rspan);
+  const rsrc_t orr = make_rsrc(O + qo_off, rspan);
+  const int fvoff = (int)(l32 * q_rs * 2) + 16 * hh;
+  u32x4_t qf[NKS], df[NKS];
+  float dsum = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    qf[ks] = buf_load16(qr, fvoff + 32 * ks);
+    df[ks] = buf_load16(dor, fvoff + 32 * ks);
+    const u32x4_t o = buf_load16(orr, fvoff + 32 * ks);
+    const f32x8_t a = unpack8<BF16>(df[ks]), b = unpack8<BF16>(o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf(a[e], b[e], dsum);
+  }
+  const float Di = dsum + __shfl_xor(dsum, 32);
+  const int nrows = max(0, min(32, Nq - qw0));
+  const int64_t vec_off = ((int64_t)w.b * Hq + w.hq) * Nq + qw0;
+  if (hh == 0) buf_store4(Di, make_rsrc(Dlt + vec_off, nrows * 4), 4 * l32);
+  // lse in log2 units; an empty row (lse = -inf) has every key masked.
+  const float lse_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                    make_rsrc(LSE + vec_off, nrows * 4), 4 * l32, 0, 0));
+  const float lse2 = lse_v * kLog2e;
+
+  // Key range of the workgroup and of this wave.
+  int kv_end = Nk;
+  if (CAUSAL) kv_end = min(Nk, min(q0 + BM, Nq) + diag);
+  const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  const int rows_end = min(qw0 + 32, Nq);
+  int w_end = rows_end > qw0 ? Nk : 0;
+  if (CAUSAL && rows_end > qw0) w_end = min(Nk, rows_end + diag);
+
+  int roff[kRowPW], toff[kTrPW];
+  tile_offsets<BN, L::RCP, D>(wave, lane, kv_rs, roff);
+  tile_offsets<BN, L::TCP, D>(wave, lane, kv_rs, toff);
+  auto issue_tile = [&](int j0, uint16_t* st) {
+    const int bytes = span_bytes(j0, BN, Nk, kv_rs, D);
+    const rsrc_t kr = make_rsrc(Kh + (int64_t)j0 * kv_rs, bytes);
+    const rsrc_t vr = make_rsrc(Vh + (int64_t)j0 * kv_rs, bytes);
+    tile_issue<kRowInst>(kr, st, wave, roff);
+    tile_issue<kTrInst>(kr, st + C::kKRow, wave, toff);
+    tile_issue<kRowInst>(vr, st + C::kKRow + C::kKTr, wave, roff);
+  };
+
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int r_rd = l32 * RS + 8 * hh;
+  const int t_rd = (4 * hh + (i16 >> 2)) * TS + 16 * (g16 & 1) + 4 * (i16 & 3);
+
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+
+  if (nt > 0) issue_tile(0, smem);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int t = 0; t < nt; ++t) {
+    const int j0 = t * BN;
+    if (t + 1 < nt) issue_tile(j0 + BN, smem + ((t + 1) & 1) * C::kStage);
+    const uint16_t* st = smem + (t & 1) * C::kStage;
+    const uint16_t* krow = st;
+    const uint16_t* ktr = st + C::kKRow;
+    const uint16_t* vrow = st + C::kKRow + C::kKTr;
+
+    if (j0 < w_end) {
+      f32x16_t s[NKB], dp[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = dp[kb] = f32x16_t{};
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int a_off = r_rd + kb * 32 * RS + 16 * ks;
+          s[kb] = mfma_32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(krow + a_off), qf[ks], s[kb]);
+          dp[kb] = mfma_32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(vrow + a_off), df[ks], dp[kb]);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      // dS^T = P^T (dP^T - D), P^T = 2^(s c - lse2); keys past the end and
+      // (causal) above the diagonal get P = 0.
+      const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + diag);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = exp2_fast(__builtin_fmaf(s[kb][r], c_log2, -lse2));
+          if (need_mask) {
+            const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool vis = j < Nk && (!CAUSAL || j <= my_q + diag);
+            p = vis ? p : 0.f;
+          }
+          s[kb][r] = p * (dp[kb][r] - Di);
+        }
+      }
+      // dQ^T += K^T dS^T (same operand mapping as the forward's PV product).
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        f32x8_t pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = s[kk >> 1][8 * (kk & 1) + e];
+        const u32x4_t b = pack8<BF16>(pv);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const u32x2_t x0 = lds_read_tr4(ktr + t_rd + 16 * kk * TS + 32 * db);
+          const u32x2_t x1 = lds_read_tr4(ktr + t_rd + (16 * kk + 8) * TS + 32 * db);
+          acc[db] = mfma_32x32x16<BF16>(u32x4_t{x0[0], x0[1], x1[0], x1[1]}, b, acc[db]);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // dQ = scale * acc, rounded; rows >= Nq fall outside the store range.
+  const rsrc_t dqr = make_rsrc(dQ + qo_off, rspan);
+  const int ovoff = (int)(l32 * q_rs * 2) + 8 * hh;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4_t o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = acc[db][4 * g + e] * scale;
+      buf_store8(pack4<BF16>(o4), dqr, ovoff + 2 * (32 * db + 8 * g));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV.
+// ---------------------------------------------------------------------------
+// blockIdx -> (b, KV head, key block); causal launches run the first key
+// blocks (which see the most query rows) first, as the grid is dispatched in
+// order.
+__device__ __forceinline__ WorkItem map_key_block(int wg, int total, int nkb, int Hkv) {
+  int lid = wg;
+  if ((total & 7) == 0) lid = (wg & 7) * (total >> 3) + (wg >> 3);
+  WorkItem w;
+  w.qblk = lid % nkb;
+  const int bh = lid / nkb;
+  w.hq = bh % Hkv;
+  w.b = bh / Hkv;
+  return w;
+}
+
+template <int D, bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(DkvCfg<D>::kThreads, DkvCfg<D>::kMinWavesPerEU)
+attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                     const float* __restrict__ LSE, const float* __restrict__ Dlt,
+                     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv,
+                     int Nq, int Nk, int nkb, int total, float scale, float c_log2) {
+  using C = DkvCfg<D>;
+  using L = typename C::L;
+  constexpr int BQ = C::BQ, BK = C::BK, RS = L::RS, TS = L::TS;
+  constexpr int NKS = D / 16, NQB = BQ / 32, NDB = D / 32, NKK = BQ / 16;
+  constexpr int kRowInst = C::kRow / 512, kTrInst = C::kTr / 512;
+  constexpr int kRowPW = (kRowInst + 3) / 4, kTrPW = (kTrInst + 3) / 4;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::kLdsElems];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const WorkItem w = map_key_block(blockIdx.x, total, nkb, Hkv);
+  const int G = Hq / Hkv;
+  const int k0 = w.qblk * BK, kw0 = k0 + wave * 32, my_k = kw0 + l32;
+  const int diag = Nk - Nq;  // key j visible to query i iff j <= i + diag
+
+  const int64_t q_rs = (int64_t)Hq * D, kv_rs = (int64_t)Hkv * D;
+  const int64_t kv_off = ((int64_t)w.b * Nk + kw0) * kv_rs + (int64_t)w.hq * D;
+
+  // K^T and V^T fragments of this wave's 32 keys (B operands).
+  const int kspan = span_bytes(kw0, 32, Nk, kv_rs, D);
+  const rsrc_t kr = make_rsrc(K + kv_off, kspan);
+  const rsrc_t vr = make_rsrc(V + kv_off, kspan);
+  const int fvoff = (int)(l32 * kv_rs * 2) + 16 * hh;
+  u32x4_t kf[NKS], vf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    kf[ks] = buf_load16(kr, fvoff + 32 * ks);
+    vf[ks] = buf_load16(vr, fvoff + 32 * ks);
+  }
+
+  // Query tiles: every query head of the group, query rows from the first
+  // tile any key of the workgroup sees (causal) to the end.
+  const int nqt_all = (Nq + BQ - 1) / BQ;
+  int qt_begin = 0;
+  if (CAUSAL) qt_begin = min(nqt_all, max(0, k0 - diag) / BQ);
+  const int nqt = nqt_all - qt_begin;
+  const int nsteps = (k0 < Nk) ? G * nqt : 0;
+  // First query row this wave's keys see (causal), for skipping whole tiles.
+  const int w_first = CAUSAL ? kw0 - diag : -(1 << 30);
+  const bool w_live = kw0 < Nk;
+
+  int roff[kRowPW], toff[kTrPW];
+  tile_offsets<BQ, L::RCP, D>(wave, lane, q_rs, roff);
+  tile_offsets<BQ, L::TCP, D>(wave, lane, q_rs, toff);
+  // Step s: query head hq = hkv*G + s / nqt, query tile qt_begin + s % nqt.
+  auto step_rows = [&](int s) { return (qt_begin + s % nqt) * BQ; };
+  auto issue_step = [&](int s, uint16_t* st) {
+    const int h = w.hq * G + s / nqt;
+    const int i0 = step_rows(s);
+    const int64_t off = ((int64_t)w.b * Nq + i0) * q_rs + (int64_t)h * D;
+    const int bytes = span_bytes(i0, BQ, Nq, q_rs, D);
+    const rsrc_t qs = make_rsrc(Q + off, bytes);
+    const rsrc_t ds = make_rsrc(dO + off, bytes);
+    tile_issue<kRowInst>(qs, st, wave, roff);
+    tile_issue<kRowInst>(ds, st + C::kRow, wave, roff);
+    tile_issue<kTrInst>(qs, st + 2 * C::kRow, wave, toff);
+    tile_issue<kTrInst>(ds, st + 2 * C::kRow + C::kTr, wave, toff);
+    if (wave == 0) {
+      const int64_t voff = ((int64_t)w.b * Hq + h) * Nq + i0;
+      const int vb = max(0, min(BQ, Nq - i0)) * 4;
+      buf_load_lds16(make_rsrc(LSE + voff, vb), st + 2 * C::kRow + 2 * C::kTr, 16 * lane);
+      buf_load_lds16(make_rsrc(Dlt + voff, vb), st + 2 * C::kRow + 2 * C::kTr + C::kVec, 16 * lane);
+    }
+  };
+
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int r_rd = l32 * RS + 8 * hh;
+  const int t_rd = (4 * hh + (i16 >> 2)) * TS + 16 * (g16 & 1) + 4 * (i16 & 3);
+
+  f32x16_t dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16_t{};
+
+  if (nsteps > 0) issue_step(0, smem);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int s = 0; s < nsteps; ++s) {
+    if (s + 1 < nsteps) issue_step(s + 1, smem + ((s + 1) & 1) * C::kStage);
+    const uint16_t* st = smem + (s & 1) * C::kStage;
+    const uint16_t* qrow = st;
+    const uint16_t* drow = st + C::kRow;
+    const uint16_t* qtr = st + 2 * C::kRow;
+    const uint16_t* dtr = st + 2 * C::kRow + C::kTr;
+    const float* lse_t = reinterpret_cast<const float*>(st + 2 * C::kRow + 2 * C::kTr);
+    const float* dlt_t = lse_t + C::kVec / 2;
+    const int i0 = step_rows(s);
+
+    if (w_live && i0 + BQ - 1 >= w_first) {  // wave-uniform: some pair visible
+      f32x16_t sc[NQB], dp[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) sc[qb] = dp[qb] = f32x16_t{};
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const int a_off = r_rd + qb * 32 * RS + 16 * ks;
+          sc[qb] = mfma_32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(qrow + a_off), kf[ks], sc[qb]);
+          dp[qb] = mfma_32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(drow + a_off), vf[ks], dp[qb]);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      // P = 2^(s c - lse2) and dS = P (dP - D) for the rows this lane's
+      // registers hold: row 32 qb + 8 (r / 4) + 4 hh + r % 4.  Rows past Nq
+      // read lse = D = 0 with zero Q and dO rows: they add nothing.
+      const bool need_mask = (i0 + BQ > Nq) || (CAUSAL && i0 + diag < kw0 + 31);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int row0 = 32 * qb + 8 * g + 4 * hh;
+          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse_t + row0);
+          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dlt_t + row0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float p = exp2_fast(__builtin_fmaf(sc[qb][r], c_log2, -l4[e] * kLog2e));
+            if (need_mask) {
+              const int i = i0 + row0 + e;
+              const bool vis = i < Nq && my_k < Nk && (!CAUSAL || my_k <= i + diag);
+              p = vis ? p : 0.f;
+            }
+            sc[qb][r] = p;
+            dp[qb][r] = p * (dp[qb][r] - d4[e]);
+          }
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (the forward's PV operand mapping).
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        f32x8_t pv, sv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = sc[kk >> 1][8 * (kk & 1) + e];
+          sv[e] = dp[kk >> 1][8 * (kk & 1) + e];
+        }
+        const u32x4_t pb = pack8<BF16>(pv), sb = pack8<BF16>(sv);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int o0 = t_rd + 16 * kk * TS + 32 * db, o1 = t_rd + (16 * kk + 8) * TS + 32 * db;
+          const u32x2_t a0 = lds_read_tr4(dtr + o0), a1 = lds_read_tr4(dtr + o1);
+          dv[db] = mfma_32x32x16<BF16>(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, pb, dv[db]);
+          const u32x2_t b0 = lds_read_tr4(qtr + o0), b1 = lds_read_tr4(qtr + o1);
+          dk[db] = mfma_32x32x16<BF16>(u32x4_t{b0[0], b0[1], b1[0], b1[1]}, sb, dk[db]);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // dK = scale * dK^T, dV = dV^T, rounded; keys >= Nk fall outside the range.
+  const rsrc_t dkr = make_rsrc(dK + kv_off, kspan);
+  const rsrc_t dvr = make_rsrc(dV + kv_off, kspan);
+  const int ovoff = (int)(l32 * kv_rs * 2) + 8 * hh;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4_t k4, v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k4[e] = dk[db][4 * g + e] * scale;
+        v4[e] = dv[db][4 * g + e];
+      }
+      buf_store8(pack4<BF16>(k4), dkr, ovoff + 2 * (32 * db + 8 * g));
+      buf_store8(pack4<BF16>(v4), dvr, ovoff + 2 * (32 * db + 8 * g));
+    }
+  }
+}
+
+}  // namespace eta

@@ -1,5 +1,6 @@
 /*
- * attn.h -- C ABI of the exact tiled attention forward for AMD MI355X (gfx950).
+ * attn.h -- C ABI of exact tiled attention (forward and backward) for AMD
+ * MI355X (gfx950).
  *
  * What is computed.  For every batch b, query head h and query row i:
  *
@@ -83,6 +84,44 @@ typedef enum {
  * Returns an attn_status value.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d,
+             float scale, int causal, int dtype, void* stream);
+
+/*
+ * Exact attention backward: gradients of L = sum(dout * out) with respect to
+ * q, k and v, for out = attn_fwd(q, k, v, scale, causal).  The pages state
+ * that the library's backward pass computes these gradients, that it is
+ * deterministic since version 2.4 (hysenlabs.com page, section "Von 2.0 bis
+ * 2.7"), and that the tests compare gradients with a reference (section
+ * "Tests, BSD-3-Clause und Zitierpraxis"); the formulas are the chain rule of
+ * the forward definition above, with P the probabilities of attn_fwd:
+ *
+ *     delta[b,h,i] = sum_c dout[b,i,h,c] * out[b,i,h,c]
+ *     dS[i,j]      = P[i,j] * ( sum_c dout[b,i,h,c] v[b,j,g,c] - delta[b,h,i] )
+ *     dq[b,i,h,:]  = scale * sum_j dS[i,j] k[b,j,g,:]
+ *     dk[b,j,g,:]  = scale * sum_{h in group g} sum_i dS[i,j] q[b,i,h,:]
+ *     dv[b,j,g,:]  =         sum_{h in group g} sum_i P[i,j] dout[b,i,h,:]
+ *
+ * P is recomputed from q, k and the forward's lse; no N x N matrix is
+ * stored.  Masked pairs and rows without a visible key contribute nothing.
+ *   q, dout, out [B, Nq, Hq, d]  element type `dtype` (read); out and lse must
+ *                                be attn_fwd's outputs for these arguments
+ *   k, v         [B, Nk, Hkv, d] element type `dtype` (read)
+ *   lse          [B, Hq, Nq]     fp32                 (read)
+ *   dq           [B, Nq, Hq, d]  element type `dtype` (written)
+ *   dk, dv       [B, Nk, Hkv, d] element type `dtype` (written; KV heads
+ *                                shared by a GQA group get the group's sum)
+ *   delta        [B, Hq, Nq]     fp32                 (written)
+ * Two kernels are enqueued on `stream`; no atomics, so results are bitwise
+ * reproducible.  The library allocates nothing.
+ * Validation order as attn_fwd, with these differences: B == 0 is a no-op;
+ * Nq == 0 (B > 0) writes zeros to dk and dv, and then q, out, dout, lse, dq
+ * and delta may be NULL; ATTN_ERR_NULL_POINTER names any required pointer;
+ * ATTN_ERR_ALIASING means an output (dq, dk, dv, delta) overlaps an input
+ * or another output.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta,
              int B, int Hq, int Hkv, int Nq, int Nk, int d,
              float scale, int causal, int dtype, void* stream);
 

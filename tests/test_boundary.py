@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from exact_tiled_attention_35_amd import _lib
-from exact_tiled_attention_35_amd.attention import attn_fwd_ptr, attn_status_string, attn_version
+from exact_tiled_attention_35_amd.attention import attn_bwd_ptr, attn_fwd_ptr, attn_status_string, attn_version
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -40,7 +40,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
-    assert names == ["attn_fwd", "attn_status_string", "attn_version"]
+    assert names == ["attn_bwd", "attn_fwd", "attn_status_string", "attn_version"]
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -142,3 +142,88 @@ def test_python_binding_rejects_bad_tensors():
         attn_fwd(q.float(), q.float(), q.float())  # fp32 is not an ABI dtype
     with pytest.raises(ValueError):
         attn_fwd(q, q, q)  # CPU tensors
+
+
+# ---------------------------------------------------------------------------
+# attn_bwd
+# ---------------------------------------------------------------------------
+OUT_, DOUT, DQ, DK, DV, DELTA = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000, 0xB0000000
+GOOD_BWD = dict(q=Q, k=K, v=V, out=OUT_, dout=DOUT, lse=LSE, dq=DQ, dk=DK, dv=DV, delta=DELTA,
+                B=2, Hq=8, Hkv=2, Nq=100, Nk=120, d=128, scale=0.088, causal=True,
+                dtype=_lib.ATTN_DTYPE_BF16)
+BWD_ORDER = ["q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "delta",
+             "B", "Hq", "Hkv", "Nq", "Nk", "d", "scale", "causal", "dtype"]
+
+
+def call_bwd(**over):
+    a = dict(GOOD_BWD)
+    a.update(over)
+    return attn_bwd_ptr(*[a[n] for n in BWD_ORDER])
+
+
+@pytest.mark.parametrize("field,value", [("B", -1), ("Nq", -1), ("Hq", 0), ("Hkv", 0), ("Nk", 0), ("d", 0)])
+def test_bwd_bad_shape(field, value):
+    assert call_bwd(**{field: value}) == _lib.ATTN_ERR_BAD_SHAPE
+
+
+def test_bwd_too_large_is_bad_shape():
+    assert call_bwd(B=1 << 30, Nq=1 << 30, Hq=1 << 8, Hkv=1, d=256) == _lib.ATTN_ERR_BAD_SHAPE
+    assert call_bwd(Hq=1 << 16, Hkv=1 << 16, d=128) == _lib.ATTN_ERR_BAD_SHAPE
+
+
+def test_bwd_empty_batch_is_a_noop_with_null_pointers():
+    nulls = {n: 0 for n in BWD_ORDER[:10]}
+    assert call_bwd(B=0, dtype=99, d=7, **nulls) == _lib.ATTN_OK
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "delta"])
+def test_bwd_null_pointer(field):
+    assert call_bwd(**{field: 0}) == _lib.ATTN_ERR_NULL_POINTER
+
+
+@pytest.mark.parametrize("field", ["q", "out", "dout", "lse", "dq", "delta"])
+def test_bwd_no_query_rows_allows_null_row_buffers(field):
+    # Nq == 0 passes validation with these NULL and fails later only for the
+    # missing device; k, v, dk and dv stay required.
+    code = call_bwd(Nq=0, **{field: 0})
+    assert code in (_lib.ATTN_ERR_NO_DEVICE, _lib.ATTN_OK)
+    assert call_bwd(Nq=0, dk=0) == _lib.ATTN_ERR_NULL_POINTER
+
+
+def test_bwd_validation_order():
+    assert call_bwd(q=0, Hkv=3) == _lib.ATTN_ERR_NULL_POINTER
+    assert call_bwd(Hkv=3, d=100) == _lib.ATTN_ERR_GQA_RATIO
+    assert call_bwd(d=100, dtype=9) == _lib.ATTN_ERR_UNSUPPORTED_HDIM
+    assert call_bwd(dtype=9, scale=float("inf")) == _lib.ATTN_ERR_UNSUPPORTED_DTYPE
+    assert call_bwd(scale=float("nan"), dq=DQ + 4) == _lib.ATTN_ERR_BAD_SCALE
+    assert call_bwd(dq=DQ + 4, dk=Q) == _lib.ATTN_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "delta"])
+def test_bwd_misaligned(field):
+    assert call_bwd(**{field: GOOD_BWD[field] + 8}) == _lib.ATTN_ERR_MISALIGNED
+
+
+def test_bwd_aliasing():
+    assert call_bwd(dq=Q) == _lib.ATTN_ERR_ALIASING          # output over an input
+    assert call_bwd(dk=V + 16) == _lib.ATTN_ERR_ALIASING
+    assert call_bwd(delta=LSE) == _lib.ATTN_ERR_ALIASING
+    assert call_bwd(dv=DK) == _lib.ATTN_ERR_ALIASING         # two outputs
+    assert call_bwd(delta=DQ + 64) == _lib.ATTN_ERR_ALIASING
+    # inputs may share memory (k and v both views of one buffer, say)
+    assert call_bwd(v=K) in (_lib.ATTN_ERR_NO_DEVICE, _lib.ATTN_OK)
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a HIP device is visible here")
+def test_bwd_no_device_reported_without_gpu():
+    assert call_bwd() == _lib.ATTN_ERR_NO_DEVICE
+    assert call_bwd(causal=False, dtype=_lib.ATTN_DTYPE_F16, d=64) == _lib.ATTN_ERR_NO_DEVICE
+
+
+def test_python_binding_rejects_bad_backward_tensors():
+    from exact_tiled_attention_35_amd import attn_bwd
+
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 4)
+    with pytest.raises(ValueError):
+        attn_bwd(q, q, q, q, q, lse)  # CPU tensors
