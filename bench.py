@@ -13,6 +13,11 @@ average duration (HIP events around every launch inside the timed region,
 on the launch stream) with MI355X's dense bf16/fp16 MFMA peak.
 ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
 workload (rank 0 only).
+
+``--op bwd`` measures the backward pass instead: one step = one ``attn_bwd``
+call (its two kernels) from the forward's out and lse, with a seeded dout;
+flops = 10*B*Hq*Nq*Nk*d (the five products S, dP, dV, dK, dQ; halved for
+causal).  The default (forward) is the headline metric.
 """
 
 from __future__ import annotations
@@ -30,9 +35,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (bf16, d=128) and % of MI355X bf16 MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # MI355X dense MFMA, published
+METRIC_BWD = ("attention bwd TFLOP/s (10*B*Hq*Nq*Nk*d per call, halved for causal) and % of "
+              "MI355X bf16 MFMA peak")
+# Sources of the forward kernel and its launch code (the committed HBM
+# traffic figures are valid only for these).
 KERNEL_SOURCES = [
-    os.path.join(ROOT, "exact_tiled_attention_35_amd", "csrc", "attn_fwd_kernel.hpp"),
-    os.path.join(ROOT, "exact_tiled_attention_35_amd", "csrc", "attn_api.hip"),
+    os.path.join(ROOT, "exact_tiled_attention_35_amd", "csrc", n)
+    for n in ("gfx950_ops.hpp", "attn_fwd_kernel.hpp", "attn_api.hip", "attn_host.hpp")
 ]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
 
@@ -44,6 +53,18 @@ def log(*a):
 def flops(w) -> float:
     f = 4.0 * w.B * w.Hq * w.Nq * w.Nk * w.d
     return f / 2 if w.causal else f
+
+
+def bwd_flops(w) -> float:
+    """Five products of the forward's size: S, dP, dV, dK, dQ."""
+    return 2.5 * flops(w)
+
+
+def bwd_algorithmic_bytes(w) -> int:
+    el = 2
+    return (w.B * w.Nq * w.Hq * w.d * el * 4          # q, out, dout read; dq written
+            + w.B * w.Nk * w.Hkv * w.d * el * 4       # k, v read; dk, dv written
+            + w.B * w.Hq * w.Nq * 4 * 2)              # lse read, delta written
 
 
 def algorithmic_bytes(w) -> int:
@@ -104,6 +125,41 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} (batch, head) pairs, all {w.Nq} query rows each, "
                   f"fp64 NumPy, {dt:.1f} s wall",
+    }
+
+
+def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
+    """Time the fp64 backward oracle on whole KV groups until ``budget_s`` is spent."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        blas_threads = os.cpu_count() or 1
+    G = w.Hq // w.Hkv
+    groups = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    done = 0
+    t0 = time.perf_counter()
+    for (b, g) in groups:
+        hs = slice(g * G, (g + 1) * G)
+        oracle.attention_backward(q[b:b + 1, :, hs], k[b:b + 1, :, g:g + 1], v[b:b + 1, :, g:g + 1],
+                                  do[b:b + 1, :, hs], w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    f = bwd_flops(w) * done / len(groups)
+    return {
+        "value": f / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(groups)} (batch, KV head) groups, all rows, fp64 NumPy, "
+                  f"{dt:.1f} s wall",
     }
 
 
@@ -183,6 +239,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
+    ap.add_argument("--op", choices=("fwd", "bwd"), default="fwd",
+                    help="fwd: attn_fwd (the headline metric); bwd: attn_bwd, the backward pass")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0, metavar="MIB",
@@ -207,7 +265,8 @@ def main():
     import torch
 
     from attn_workloads import HEADLINE, WORKLOADS, make_workload
-    from exact_tiled_attention_35_amd import attn_fwd, attn_version
+    from exact_tiled_attention_35_amd import attn_bwd_ptr, attn_fwd, attn_version
+    from exact_tiled_attention_35_amd.attention import _DTYPE_CODE
 
     w = WORKLOADS[args.workload or HEADLINE]
     if not torch.cuda.is_available():
@@ -222,8 +281,25 @@ def main():
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    if args.op == "fwd":
+        def step():
+            attn_fwd(dq, dk, dv, w.scale, w.causal, out=out, lse=lse)
+    else:
+        from attn_workloads import make_qkv
+
+        do = make_qkv(w.B, w.Nq, w.Nq, w.Hq, w.Hq, w.d, w.dtype, w.sigma, w.seed + 100)[0]
+        ddo = do.to(dev)
         attn_fwd(dq, dk, dv, w.scale, w.causal, out=out, lse=lse)
+        gq, gk, gv = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+        delta = torch.empty_like(lse)
+        ptrs = [t.data_ptr() for t in (dq, dk, dv, out, ddo, lse, gq, gk, gv, delta)]
+        code_dt = _DTYPE_CODE[dq.dtype]
+
+        def step():
+            code = attn_bwd_ptr(*ptrs, w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.scale, w.causal,
+                                code_dt, stream.cuda_stream)
+            if code != 0:
+                raise SystemExit(f"attn_bwd failed with status {code}")
 
     for _ in range(args.warmup):
         step()
@@ -244,16 +320,16 @@ def main():
     avg_kernel_s = sum(kernel_ms) / K / 1e3
     ms_per_step = wall / K * 1e3
 
-    F = flops(w)
+    F = flops(w) if args.op == "fwd" else bwd_flops(w)
     value = F / (wall / K) / 1e12
     achieved = F / avg_kernel_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name) if args.op == "fwd" else None
     log(f"[bench] {K} steps: {ms_per_step:.4f} ms/step wall, kernel avg {avg_kernel_s*1e6:.1f} us "
         f"(min {min(kernel_ms)*1e3:.1f} us), {achieved:.1f} TFLOP/s = {100*achieved/peak:.1f}% of peak")
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if args.op == "fwd" else METRIC_BWD,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -275,7 +351,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "algorithmic_bytes": algorithmic_bytes(w),
+            "algorithmic_bytes": algorithmic_bytes(w) if args.op == "fwd" else bwd_algorithmic_bytes(w),
             "kernel_avg_us": round(avg_kernel_s * 1e6, 2),
         },
         "cpu_baseline": None,
@@ -285,9 +361,16 @@ def main():
     if args.calibration_copy_mib:
         calibration_copy(args.calibration_copy_mib)
         result["calibration_copy_bytes"] = args.calibration_copy_mib * 2**20
+    if args.op == "bwd":
+        result["roofline"]["unit_of_work"] = ("one attn_bwd call: the dQ kernel and the dK/dV "
+                                              "kernel back to back")
+        result["context"] = "backward pass; the headline metric is the forward (--op fwd)"
     if not args.no_cpu_baseline:
         del dq, dk, dv
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+        if args.op == "fwd":
+            result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+        else:
+            result["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do, args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 
