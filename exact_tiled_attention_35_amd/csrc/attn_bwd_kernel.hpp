@@ -67,27 +67,29 @@ struct BwdLayout {
 template <int D>
 struct DqCfg {
   static constexpr int kWaves = 4, kThreads = 256, BM = 128;
-  static constexpr int BN = (D >= 256) ? 32 : 64;  // keys per tile
+  // 32-key tiles keep the LDS of a workgroup under half of the CU's, so two
+  // workgroups (two waves per SIMD) share a CU.
+  static constexpr int BN = 32;  // keys per tile
   using L = BwdLayout<D>;
   static constexpr int kKRow = L::template row_elems<BN>();
   static constexpr int kKTr = L::template tr_elems<BN>();
   static constexpr int kVRow = kKRow;
   static constexpr int kStage = kKRow + kKTr + kVRow;
   static constexpr int kLdsElems = 2 * kStage;
-  static constexpr int kMinWavesPerEU = 1;
+  static constexpr int kMinWavesPerEU = (D >= 256) ? 1 : 2;
 };
 
 template <int D>
 struct DkvCfg {
   static constexpr int kWaves = 4, kThreads = 256, BK = 128;
-  static constexpr int BQ = (D >= 256) ? 32 : 64;  // query rows per tile
+  static constexpr int BQ = 32;  // query rows per tile (two workgroups per CU at d <= 128)
   using L = BwdLayout<D>;
   static constexpr int kRow = L::template row_elems<BQ>();
   static constexpr int kTr = L::template tr_elems<BQ>();
   static constexpr int kVec = 512;  // 1 KB: lse or D of the tile (64 lanes x 16 B)
   static constexpr int kStage = 2 * kRow + 2 * kTr + 2 * kVec;
   static constexpr int kLdsElems = 2 * kStage;
-  static constexpr int kMinWavesPerEU = 1;
+  static constexpr int kMinWavesPerEU = (D >= 256) ? 1 : 2;
   static_assert(BQ * 4 <= kVec * 2, "lse/D slots cover the tile");
 };
 
