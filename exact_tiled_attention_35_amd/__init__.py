@@ -10,6 +10,10 @@ from .attention import (  # noqa: F401
     attention,
     attn_bwd,
     attn_bwd_ptr,
+    attn_decode,
+    attn_decode_num_splits,
+    attn_decode_ptr,
+    attn_decode_workspace_size,
     attn_fwd,
     attn_fwd_ptr,
     attn_status_string,

@@ -22,6 +22,7 @@ ATTN_ERR_MISALIGNED = -7
 ATTN_ERR_ALIASING = -8
 ATTN_ERR_NO_DEVICE = -9
 ATTN_ERR_LAUNCH = -10
+ATTN_ERR_WORKSPACE = -11
 
 # attn_dtype values.
 ATTN_DTYPE_F16 = 0
@@ -44,6 +45,12 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd.restype = ci
     lib.attn_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, ci, ci, cf, ci, ci, vp]
     lib.attn_bwd.restype = ci
+    lib.attn_decode.argtypes = [vp] * 9 + [ctypes.c_size_t] + [ci] * 7 + [cf, ci, ci, ci, vp]
+    lib.attn_decode.restype = ci
+    lib.attn_decode_num_splits.argtypes = [ci] * 6
+    lib.attn_decode_num_splits.restype = ci
+    lib.attn_decode_workspace_size.argtypes = [ci] * 5
+    lib.attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.attn_status_string.argtypes = [ci]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []

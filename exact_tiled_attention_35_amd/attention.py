@@ -103,6 +103,66 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     return dq, dk, dv, delta
 
 
+def attn_decode_ptr(q: int, k_cache: int, v_cache: int, cache_seqlens: int, k_new: int, v_new: int,
+                    out: int, lse: int, workspace: int, workspace_bytes: int, B: int, Hq: int,
+                    Hkv: int, Nq: int, Ncap: int, Nnew: int, d: int, scale: float, causal: bool,
+                    dtype: int, num_splits: int = 0, stream: int = 0) -> int:
+    """The C entry point with raw integer pointers; returns the attn_status."""
+    return _lib.load().attn_decode(q or None, k_cache or None, v_cache or None,
+                                   cache_seqlens or None, k_new or None, v_new or None,
+                                   out or None, lse or None, workspace or None,
+                                   int(workspace_bytes), int(B), int(Hq), int(Hkv), int(Nq),
+                                   int(Ncap), int(Nnew), int(d), float(scale),
+                                   int(bool(causal)), int(dtype), int(num_splits), stream or None)
+
+
+def attn_decode_num_splits(B: int, Hq: int, Hkv: int, Nq: int, Ncap: int, d: int) -> int:
+    return int(_lib.load().attn_decode_num_splits(B, Hq, Hkv, Nq, Ncap, d))
+
+
+def attn_decode_workspace_size(B: int, Hq: int, Nq: int, d: int, num_splits: int) -> int:
+    return int(_lib.load().attn_decode_workspace_size(B, Hq, Nq, d, num_splits))
+
+
+def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                cache_seqlens: torch.Tensor, k_new: torch.Tensor | None = None,
+                v_new: torch.Tensor | None = None, softmax_scale: float | None = None,
+                causal: bool = True, num_splits: int = 0):
+    """KV-cache decode forward on the GPU (the caches are updated in place).
+
+    q: [B, Nq, Hq, d]; k_cache, v_cache: [B, Ncap, Hkv, d]; cache_seqlens:
+    int32 [B] on the device (rows already in the cache); k_new, v_new:
+    [B, Nnew, Hkv, d] or None.  Returns (out [B, Nq, Hq, d], lse [B, Hq, Nq]).
+    """
+    B, Nq, Hq, Hkv, Ncap, d = _check_qkv(q, k_cache, v_cache)
+    _check_like("cache_seqlens", cache_seqlens, (B,), torch.int32, q.device)
+    Nnew = 0
+    if k_new is not None or v_new is not None:
+        if k_new is None or v_new is None:
+            raise ValueError("k_new and v_new go together")
+        Nnew = k_new.shape[1]
+        _check_like("k_new", k_new, (B, Nnew, Hkv, d), q.dtype, q.device)
+        _check_like("v_new", v_new, (B, Nnew, Hkv, d), q.dtype, q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    splits = num_splits or attn_decode_num_splits(B, Hq, Hkv, Nq, Ncap, d)
+    ws_bytes = attn_decode_workspace_size(B, Hq, Nq, d, splits)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        code = attn_decode_ptr(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                               cache_seqlens.data_ptr(),
+                               k_new.data_ptr() if Nnew else 0, v_new.data_ptr() if Nnew else 0,
+                               out.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws_bytes, B, Hq, Hkv,
+                               Nq, Ncap, Nnew, d, softmax_scale, causal, _DTYPE_CODE[q.dtype],
+                               splits, stream)
+    if code != _lib.ATTN_OK:
+        raise AttnError(code)
+    return out, lse
+
+
 class _Attention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, softmax_scale, causal):

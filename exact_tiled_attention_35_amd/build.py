@@ -1,7 +1,7 @@
 """Build the HIP library in-tree: ``python -m exact_tiled_attention_35_amd.build``.
 
-Compiles ``csrc/attn_api.hip`` and ``csrc/attn_bwd_api.hip`` (C ABI +
-kernels) for gfx950 into
+Compiles ``csrc/attn_api.hip``, ``csrc/attn_bwd_api.hip`` and
+``csrc/attn_decode_api.hip`` (C ABI + kernels) for gfx950 into
 ``libattn.so`` next to this file, and writes the compiler's per-kernel
 resource report (VGPRs, AGPRs, LDS, scratch, occupancy) to
 ``_build/resource_usage.txt``.
@@ -19,9 +19,10 @@ ROOT = os.path.dirname(PKG)
 LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = [os.path.join(PKG, "csrc", n) for n in ("attn_api.hip", "attn_bwd_api.hip")]
+SOURCES = [os.path.join(PKG, "csrc", n) for n in ("attn_api.hip", "attn_bwd_api.hip", "attn_decode_api.hip")]
 HEADERS = [os.path.join(PKG, "csrc", n) for n in ("gfx950_ops.hpp", "attn_fwd_kernel.hpp",
-                                                  "attn_bwd_kernel.hpp", "attn_host.hpp")] + [
+                                                  "attn_bwd_kernel.hpp", "attn_decode_kernel.hpp",
+                                                  "attn_host.hpp")] + [
     os.path.join(ROOT, "include", "attn.h")]
 
 

@@ -119,6 +119,7 @@ extern "C" const char* attn_status_string(int status) {
     case ATTN_ERR_ALIASING: return "ATTN_ERR_ALIASING: out and lse must not overlap the inputs or each other";
     case ATTN_ERR_NO_DEVICE: return "ATTN_ERR_NO_DEVICE: no HIP device, or the current device is not gfx950";
     case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: kernel launch failed";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace smaller than attn_decode_workspace_size";
     default: return "unknown attn status";
   }
 }

@@ -1,0 +1,367 @@
+// KV-cache decode forward for gfx950 (MI355X, CDNA4).
+//
+// The inference path of the hysenlabs.com page "FlashAttention: exakte
+// Attention-Kernel fuer CUDA und ROCm" (section "Die Schnittstellen von
+// flash_attn_func bis KV-Cache"): a few new query rows attend to a long
+// key/value cache; the new keys and values are written into the cache in
+// place first, and there is no backward pass.  Per batch b the cache holds
+// cache_seqlens[b] valid rows before the append and cache_seqlens[b] + Nnew
+// after it; the query rows attend to all of those (causal: bottom-right
+// aligned, as everywhere in this library).
+//
+// Three kernels:
+//  * kv_append_kernel: copies k_new / v_new rows into the cache at row
+//    cache_seqlens[b] + t (16 bytes per thread).
+//  * attn_decode_kernel: one workgroup per (b, KV head, block of 128 packed
+//    query rows, key split).  The query heads of a GQA group are packed into
+//    the rows of one MFMA tile (packed row r = (head g*G + r / Nq, query
+//    r % Nq)), so each KV head's cache is streamed once per split for the
+//    whole group.  The keys of (b, KV head) are cut into `splits` ranges of
+//    whole tiles, one per workgroup, so that short query blocks still fill
+//    the GPU; K/V tiles stream through a 4-stage LDS ring (three tiles in
+//    flight) because the loop is bound by HBM, not by the matrix cores.  The
+//    products, the online softmax and the masking are the forward kernel's
+//    (S^T = K Q^T and O^T = V^T P^T on 32x32x16 MFMAs, one query row per
+//    lane, exp2 with the running maximum).  With one split the result goes
+//    straight to out/lse; otherwise each workgroup writes its normalised
+//    fp32 partial O and its logsumexp to the workspace.
+//  * attn_decode_merge_kernel: per query row, lse = log sum_s exp(lse_s) and
+//    O = sum_s exp(lse_s - lse) O_s -- the same merge that combines key
+//    ranges across devices.
+#pragma once
+
+#include <type_traits>
+
+#include "gfx950_ops.hpp"
+
+namespace eta {
+
+template <int D>
+struct DecCfg {
+  static constexpr int kWaves = 4, kThreads = 256, BM = 128;
+  static constexpr int BN = 32;       // keys per tile
+  static constexpr int kStages = 4;   // LDS ring: three tiles in flight
+  static constexpr int kChunks = D / 8;
+  static constexpr int KCP = kChunks + 1, VCP = kChunks + 4;
+  static constexpr int KS = 8 * KCP, VS = 8 * VCP;
+  static constexpr int kKInst = (BN * KCP + 63) / 64, kVInst = (BN * VCP + 63) / 64;
+  static constexpr int kKElems = kKInst * 512, kVElems = kVInst * 512;
+  static constexpr int kStage = kKElems + kVElems;
+  static constexpr int kLdsElems = kStages * kStage;
+  static constexpr int kKInstPerWave = (kKInst + 3) / 4, kVInstPerWave = (kVInst + 3) / 4;
+  static constexpr int kMinWavesPerEU = (D >= 256) ? 1 : 2;
+  static_assert((KS / 2) % 8 == 4 && (VS / 2) % 32 == 16, "bank-conflict-free strides");
+};
+
+// Appends Nnew rows per (b, KV head) to the caches: row cache_seqlens[b] + t.
+// Rows that would land at or past Ncap are dropped (the range of the
+// destination descriptor ends there).
+template <int D>
+__global__ void __launch_bounds__(256)
+kv_append_kernel(const uint16_t* __restrict__ Kn, const uint16_t* __restrict__ Vn,
+                 uint16_t* __restrict__ Kc, uint16_t* __restrict__ Vc,
+                 const int* __restrict__ seqlens, int B, int Nnew, int Hkv, int Ncap) {
+  constexpr int kChunks = D / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)B * Nnew * Hkv * kChunks;
+  if (idx >= total) return;
+  const int c = (int)(idx % kChunks);
+  const int64_t row = idx / kChunks;  // (b, t, h) of the new rows
+  const int h = (int)(row % Hkv);
+  const int t = (int)((row / Hkv) % Nnew);
+  const int b = (int)(row / ((int64_t)Hkv * Nnew));
+  const int pos = seqlens[b] + t;
+  const int64_t cache_b = (int64_t)b * Ncap * Hkv * D;
+  const int cache_bytes = (int)((int64_t)Ncap * Hkv * D * 2);
+  const int dst = pos >= 0 && pos < Ncap ? (int)((((int64_t)pos * Hkv + h) * D + 8 * c) * 2) : cache_bytes;
+  const int src = (int)((row * D + 8 * c) * 2);
+  const rsrc_t kn = make_rsrc(Kn, (int)(total * 16)), vn = make_rsrc(Vn, (int)(total * 16));
+  const rsrc_t kc = make_rsrc(Kc + cache_b, cache_bytes), vc = make_rsrc(Vc + cache_b, cache_bytes);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(kn, src, 0, 0), kc, dst, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(vn, src, 0, 0), vc, dst, 0, 0);
+}
+
+template <int D, bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(DecCfg<D>::kThreads, DecCfg<D>::kMinWavesPerEU)
+attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ V, const int* __restrict__ seqlens,
+                   uint16_t* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Opart,
+                   float* __restrict__ Lpart, int B, int Hq, int Hkv, int Nq, int Ncap, int Nnew,
+                   int nrb, int splits, float c_log2, int prescale) {
+  using C = DecCfg<D>;
+  constexpr int BN = C::BN, BM = C::BM, KS = C::KS, VS = C::VS, NS = C::kStages;
+  constexpr int NKS = D / 16, NKB = BN / 32, NDB = D / 32, NKK = BN / 16;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::kLdsElems];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+
+  // blockIdx -> (b, KV head, row block, split).
+  int lid = blockIdx.x;
+  const int s = lid % splits;
+  lid /= splits;
+  const int rb = lid % nrb;
+  lid /= nrb;
+  const int hkv = lid % Hkv;
+  const int b = lid / Hkv;
+  const int G = Hq / Hkv;
+  const int rows = G * Nq;
+
+  // This lane's packed row -> (query head, query row).
+  const int rw0 = rb * BM + wave * 32;
+  const int r = rw0 + l32;
+  const bool row_ok = r < rows;
+  const int h = hkv * G + (row_ok ? r / Nq : 0);
+  const int i = row_ok ? r % Nq : 0;
+  const bool wave_live = rw0 < rows;
+
+  // Keys of batch b and of this split (whole tiles).
+  const int nk = min(Ncap, max(0, seqlens[b] + Nnew));
+  const int diag = nk - Nq;
+  const int tiles = (nk + BN - 1) / BN;
+  const int tps = (tiles + splits - 1) / splits;
+  const int t0 = min(tiles, s * tps), t1 = min(tiles, t0 + tps);
+  // (Causal never shortens the range: query row Nq - 1 sees every key.)
+  const int kv_end = min(nk, t1 * BN);
+  const int nt = kv_end > t0 * BN ? (kv_end - t0 * BN + BN - 1) / BN : 0;
+
+  const int64_t q_rs = (int64_t)Hq * D, kv_rs = (int64_t)Hkv * D;
+  const uint16_t* Kh = K + ((int64_t)b * Ncap * Hkv + hkv) * D;
+  const uint16_t* Vh = V + ((int64_t)b * Ncap * Hkv + hkv) * D;
+
+  // Q^T fragments of this lane's row; rows past the packed rows read 0.
+  const int qbytes = (int)((int64_t)Nq * q_rs * 2);
+  const rsrc_t qr = make_rsrc(Q + (int64_t)b * Nq * q_rs, qbytes);
+  const int qoff = row_ok ? (int)(((int64_t)i * q_rs + (int64_t)h * D) * 2) + 16 * hh : qbytes;
+  u32x4_t qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qf[ks] = buf_load16(qr, qoff + (row_ok ? 32 * ks : 0));
+
+  int koff[C::kKInstPerWave], voff[C::kVInstPerWave];
+#pragma unroll
+  for (int k = 0; k < C::kKInstPerWave; ++k) {
+    const int sl = 64 * (wave + 4 * k) + lane;
+    const int row = min(sl / C::KCP, BN - 1), c = min(sl % C::KCP, C::kChunks - 1);
+    koff[k] = (int)(row * kv_rs * 2) + 16 * c;
+  }
+#pragma unroll
+  for (int k = 0; k < C::kVInstPerWave; ++k) {
+    const int sl = 64 * (wave + 4 * k) + lane;
+    const int row = min(sl / C::VCP, BN - 1), c = min(sl % C::VCP, C::kChunks - 1);
+    voff[k] = (int)(row * kv_rs * 2) + 16 * c;
+  }
+  auto issue_tile = [&](int t, uint16_t* st) {
+    const int j0 = (t0 + t) * BN;
+    const int bytes = span_bytes(j0, BN, nk, kv_rs, D);
+    const rsrc_t kr = make_rsrc(Kh + (int64_t)j0 * kv_rs, bytes);
+    const rsrc_t vr = make_rsrc(Vh + (int64_t)j0 * kv_rs, bytes);
+#pragma unroll
+    for (int k = 0; k < C::kKInstPerWave; ++k) {
+      const int j = wave + 4 * k;
+      if (j < C::kKInst) buf_load_lds16(kr, st + 512 * j, koff[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < C::kVInstPerWave; ++k) {
+      const int j = wave + 4 * k;
+      if (j < C::kVInst) buf_load_lds16(vr, st + C::kKElems + 512 * j, voff[k]);
+    }
+  };
+
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int k_rd = l32 * KS + 8 * hh;
+  const int v_rd = C::kKElems + (4 * hh + (i16 >> 2)) * VS + 16 * (g16 & 1) + 4 * (i16 & 3);
+
+  f32x16_t oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16_t{};
+  float m = -INFINITY, lsum = 0.f;
+  const float ce = prescale ? 1.0f : c_log2;
+
+  // Every wave issues at least kMinLoads load instructions per tile, so
+  // "at most kMinLoads * (NS - 2) loads outstanding" implies that tile t,
+  // issued before the NS - 2 newer ones, has landed (loads complete in
+  // order).  s_waitcnt operand: vmcnt in bits 3:0 and 15:14, expcnt and
+  // lgkmcnt left at their maxima.
+  constexpr int kMinLoads = C::kKInst / 4 + C::kVInst / 4;
+  constexpr int kVm = kMinLoads * (NS - 2);
+  static_assert(kVm < 64, "vmcnt range");
+  constexpr int kWaitNewerTiles = (kVm & 0xf) | (0x7 << 4) | (0xf << 8) | ((kVm >> 4) << 14);
+
+  // Prologue: NS - 1 tiles in flight.
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < nt) issue_tile(t, smem + t * C::kStage);
+
+  for (int t = 0; t < nt; ++t) {
+    // Tile t has landed once at most NS - 2 newer tiles are outstanding;
+    // every wave waits for its own loads, then the barrier publishes them
+    // and ends all reads of the slot the next load reuses.
+    if (t + NS - 2 < nt) {
+      __builtin_amdgcn_s_waitcnt(kWaitNewerTiles);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    if (t + NS - 1 < nt) issue_tile(t + NS - 1, smem + ((t + NS - 1) % NS) * C::kStage);
+    const uint16_t* st = smem + (t % NS) * C::kStage;
+    const int j0 = (t0 + t) * BN;
+
+    if (wave_live) {
+      f32x16_t sacc[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          sacc[kb] = mfma_32x32x16<BF16>(
+              *reinterpret_cast<const u32x4_t*>(st + k_rd + kb * 32 * KS + 16 * ks), qf[ks], sacc[kb]);
+      }
+      if (prescale) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sacc[kb] *= c_log2;
+      }
+      // Mask keys past the end and (causal) above the diagonal.
+      const bool need_mask = (j0 + BN > kv_end) || CAUSAL;
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (need_mask) {
+            const int j = j0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+            const bool vis = j < kv_end && (!CAUSAL || j <= i + diag);
+            sacc[kb][e] = vis ? sacc[kb][e] : -INFINITY;
+          }
+          tmax = __builtin_fmaxf(tmax, sacc[kb][e]);
+        }
+      }
+      tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float tm = tmax * ce;
+      if (tm > m) {
+        const float alpha = exp2_fast(m - tm);
+        m = tm;
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      }
+      const float mb = m == -INFINITY ? 0.f : m;
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2_fast(__builtin_fmaf(sacc[kb][e], ce, -mb));
+          sacc[kb][e] = p;
+          ps += p;
+        }
+      }
+      lsum += ps;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        f32x8_t pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = sacc[kk >> 1][8 * (kk & 1) + e];
+        const u32x4_t phi = pack8<BF16>(pv), plo = pack8<BF16>(pv - unpack8<BF16>(phi));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const u32x2_t x0 = lds_read_tr4(st + v_rd + 16 * kk * VS + 32 * db);
+          const u32x2_t x1 = lds_read_tr4(st + v_rd + (16 * kk + 8) * VS + 32 * db);
+          const u32x4_t a = {x0[0], x0[1], x1[0], x1[1]};
+          oacc[db] = mfma_32x32x16<BF16>(a, phi, oacc[db]);
+          oacc[db] = mfma_32x32x16<BF16>(a, plo, oacc[db]);
+        }
+      }
+    }
+  }
+
+  // Epilogue: this split's normalised output and natural-log logsumexp.
+  const float lt = lsum + __shfl_xor(lsum, 32);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float lse = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+  if (!row_ok) return;
+  const int64_t row_id = ((int64_t)b * Hq + h) * Nq + i;  // [B, Hq, Nq] order
+  if (splits == 1) {
+    const int obytes = (int)((int64_t)Nq * q_rs * 2);
+    const rsrc_t orr = make_rsrc(O + (int64_t)b * Nq * q_rs, obytes);
+    const int ooff = (int)(((int64_t)i * q_rs + (int64_t)h * D) * 2) + 8 * hh;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4_t o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * g + e] * inv;
+        buf_store8(pack4<BF16>(o4), orr, ooff + 2 * (32 * db + 8 * g));
+      }
+    }
+    if (hh == 0) LSE[row_id] = lse;
+  } else {
+    const int64_t prow = (int64_t)s * B * Hq * Nq + row_id;
+    float* op = Opart + prow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4_t o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * g + e] * inv;
+        *reinterpret_cast<f32x4_t*>(op + 32 * db + 8 * g + 4 * hh) = o4;
+      }
+    }
+    if (hh == 0) Lpart[prow] = lse;
+  }
+}
+
+// One wave per query row: lse = log sum_s exp(lse_s), O = sum_s w_s O_s with
+// w_s = exp(lse_s - lse); rows no split saw get O = 0 and lse = -inf.
+template <int D, bool BF16>
+__global__ void __launch_bounds__(256)
+attn_decode_merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpart,
+                         uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Nq,
+                         int splits) {
+  constexpr int PER = D / 64;  // elements per lane
+  const int64_t nrow = (int64_t)B * Hq * Nq;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= nrow) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < splits; ++s) mx = __builtin_fmaxf(mx, Lpart[(int64_t)s * nrow + row]);
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float den = 0.f;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float ls = Lpart[(int64_t)s * nrow + row];
+      const float wgt = ls == -INFINITY ? 0.f : exp2_fast((ls - mx) * 1.44269504088896340736f);
+      den += wgt;
+      const float* op = Opart + ((int64_t)s * nrow + row) * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = __builtin_fmaf(wgt, op[e], acc[e]);
+    }
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  // row = (b * Hq + h) * Nq + i -> out[b, i, h, :]
+  const int i = (int)(row % Nq);
+  const int64_t bh = row / Nq;
+  const int h = (int)(bh % Hq);
+  const int64_t b = bh / Hq;
+  uint16_t* out = O + ((b * Nq + i) * Hq + h) * D + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    float o = acc[e] * inv;
+    uint16_t bits;
+    if constexpr (BF16) {
+      bits = __builtin_bit_cast(uint16_t, (__bf16)o);
+    } else {
+      bits = __builtin_bit_cast(uint16_t, (_Float16)o);
+    }
+    out[e] = bits;
+  }
+  if (lane == 0) LSE[row] = den > 0.f ? mx + __builtin_amdgcn_logf(den) * kLn2 : -INFINITY;
+}
+
+}  // namespace eta

@@ -49,6 +49,8 @@
 #ifndef EXACT_TILED_ATTENTION_ATTN_H
 #define EXACT_TILED_ATTENTION_ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -68,7 +70,8 @@ typedef enum {
   ATTN_ERR_MISALIGNED = -7,        /* a base pointer is not 16-byte aligned              */
   ATTN_ERR_ALIASING = -8,          /* out or lse overlaps an input, or each other        */
   ATTN_ERR_NO_DEVICE = -9,         /* no HIP device, or the current device is not gfx950 */
-  ATTN_ERR_LAUNCH = -10            /* the kernel launch failed                            */
+  ATTN_ERR_LAUNCH = -10,           /* the kernel launch failed                            */
+  ATTN_ERR_WORKSPACE = -11         /* attn_decode: workspace smaller than required       */
 } attn_status;
 
 /*
@@ -124,6 +127,55 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              const float* lse, void* dq, void* dk, void* dv, float* delta,
              int B, int Hq, int Hkv, int Nq, int Nk, int d,
              float scale, int causal, int dtype, void* stream);
+
+/*
+ * KV-cache decode forward: new query rows against a key/value cache that is
+ * updated in place, as the interface section of the hysenlabs.com page
+ * describes the inference function ("Die Schnittstellen von flash_attn_func
+ * bis KV-Cache": it writes the new keys and values into k_cache and v_cache
+ * directly and has no backward pass).
+ *
+ * For each batch b, with L = cache_seqlens[b] (device memory, read by the
+ * kernels) and n_b = L + Nnew:
+ *   1. k_cache[b, L + t] = k_new[b, t] and v_cache[b, L + t] = v_new[b, t]
+ *      for t < Nnew (rows at or past Ncap are not written; the caller keeps
+ *      L + Nnew <= Ncap);
+ *   2. out[b, i, h] and lse[b, h, i] as attn_fwd computes them for query
+ *      rows i < Nq against the keys and values [0, n_b) of the updated
+ *      cache (causal: key j visible to row i iff j <= i + n_b - Nq).
+ * cache_seqlens is not modified.
+ *   q             [B, Nq, Hq, d]    element type `dtype` (read)
+ *   k_cache, v_cache [B, Ncap, Hkv, d] element type `dtype` (read, rows
+ *                                   [L, L + Nnew) written)
+ *   cache_seqlens [B] int32, device (read)
+ *   k_new, v_new  [B, Nnew, Hkv, d] element type `dtype` (read; may be NULL
+ *                                   when Nnew == 0)
+ *   out, lse      as attn_fwd (written)
+ *   workspace     device scratch owned by the caller, at least
+ *                 attn_decode_workspace_size(B, Hq, Nq, d, splits) bytes,
+ *                 16-byte aligned (may be NULL when that size is 0); its
+ *                 contents are undefined afterwards.  Calls sharing one
+ *                 workspace must not overlap in time.
+ *   num_splits    key ranges per (batch, KV head) computed by separate
+ *                 workgroups and merged by logsumexp; 0 = the library's choice
+ *                 (attn_decode_num_splits), otherwise 1..128.
+ * The query heads of a GQA group share one pass over their KV head's cache.
+ * Validation as attn_fwd; B == 0, or Nq == 0 with Nnew == 0, is a no-op;
+ * ATTN_ERR_WORKSPACE when workspace_bytes is too small; ATTN_ERR_ALIASING
+ * when a written buffer (caches, out, lse, workspace) overlaps another
+ * buffer.  Up to three kernels are enqueued on `stream`.
+ */
+int attn_decode(const void* q, void* k_cache, void* v_cache, const int* cache_seqlens,
+                const void* k_new, const void* v_new, void* out, float* lse,
+                void* workspace, size_t workspace_bytes,
+                int B, int Hq, int Hkv, int Nq, int Ncap, int Nnew, int d,
+                float scale, int causal, int dtype, int num_splits, void* stream);
+
+/* The split count attn_decode uses for num_splits == 0 (always >= 1). */
+int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Ncap, int d);
+
+/* Workspace bytes attn_decode needs for `num_splits` splits (0 for one split). */
+size_t attn_decode_workspace_size(int B, int Hq, int Nq, int d, int num_splits);
 
 /* A fixed, static message for a status code (never NULL). */
 const char* attn_status_string(int status);
