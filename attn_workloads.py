@@ -63,6 +63,18 @@ WORKLOADS = {
 WORKLOAD_ORDER = list(WORKLOADS)
 HEADLINE = "mha_b4_h16_n4096_d128_bf16"
 
+# KV-cache decode: one new query row per sequence against a full cache of Nk
+# rows (Nk - 1 already cached, one appended by the call), GQA 32/8, d = 128.
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("decode_b16_hq32_hkv8_cache32768_d128_bf16", 16, 32, 8, 1, 32768, 128, "bf16",
+                 True, 1.0, 6),
+        Workload("decode_b1_hq32_hkv8_cache131072_d128_bf16", 1, 32, 8, 1, 131072, 128, "bf16",
+                 True, 1.0, 7),
+    ]
+}
+
 
 def make_qkv(B, Nq, Nk, Hq, Hkv, d, dtype="bf16", sigma=1.0, seed=0):
     """Draw q [B,Nq,Hq,d], k and v [B,Nk,Hkv,d] on the CPU, rounded to ``dtype``."""

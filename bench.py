@@ -55,6 +55,16 @@ def flops(w) -> float:
     return f / 2 if w.causal else f
 
 
+def decode_bytes(w) -> int:
+    """HBM bytes one decode step must move: the whole K/V cache of every
+    (batch, KV head) read once, q and the new K/V rows read, out, lse and the
+    appended cache rows written."""
+    el = 2
+    return (w.B * w.Nk * w.Hkv * w.d * el * 2
+            + w.B * w.Nq * w.Hq * w.d * el * 2 + w.B * w.Hq * w.Nq * 4
+            + w.B * 1 * w.Hkv * w.d * el * 4)
+
+
 def bwd_flops(w) -> float:
     """Five products of the forward's size: S, dP, dV, dK, dQ."""
     return 2.5 * flops(w)
@@ -163,6 +173,33 @@ def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
     }
 
 
+def cpu_baseline_decode(w, q, kc, vc, budget_s: float):
+    """Time the fp64 oracle on whole sequences of the decode workload."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        blas_threads = os.cpu_count() or 1
+    done = 0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        oracle.attention(q[b:b + 1], kc[b:b + 1], vc[b:b + 1], w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": decode_bytes(w) * done / w.B / dt / 1e9,
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B} sequences, every query head, fp64 NumPy, {dt:.1f} s wall",
+    }
+
+
 def calibration_copy(mib: int):
     """One elementwise kernel that reads mib MiB and writes mib MiB (a negated
     copy), the yardstick that scales FETCH_SIZE / WRITE_SIZE to bytes."""
@@ -239,8 +276,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
-    ap.add_argument("--op", choices=("fwd", "bwd"), default="fwd",
-                    help="fwd: attn_fwd (the headline metric); bwd: attn_bwd, the backward pass")
+    ap.add_argument("--op", choices=("fwd", "bwd", "decode"), default="fwd",
+                    help="fwd: attn_fwd (the headline metric); bwd: attn_bwd, the backward pass; "
+                         "decode: attn_decode on a KV-cache decode workload")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0, metavar="MIB",
@@ -264,17 +302,22 @@ def main():
 
     import torch
 
-    from attn_workloads import HEADLINE, WORKLOADS, make_workload
+    from attn_workloads import DECODE_WORKLOADS, HEADLINE, WORKLOADS, make_workload
     from exact_tiled_attention_35_amd import attn_bwd_ptr, attn_fwd, attn_version
     from exact_tiled_attention_35_amd.attention import _DTYPE_CODE
 
-    w = WORKLOADS[args.workload or HEADLINE]
+    if args.op == "decode":
+        w = DECODE_WORKLOADS[args.workload or next(iter(DECODE_WORKLOADS))]
+    else:
+        w = WORKLOADS[args.workload or HEADLINE]
     if not torch.cuda.is_available():
         log("no GPU visible")
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"[bench] workload {w.name}; library {attn_version()}")
+    if args.op == "decode":
+        return bench_decode(args, w, dev)
     q, k, v = make_workload(w)
     dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
     out = torch.empty_like(dq)
@@ -371,6 +414,100 @@ def main():
             result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
         else:
             result["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(args, w, dev):
+    """One step = one attn_decode call: append one K/V row per sequence at row
+    Nk - 1 of a cache holding Nk - 1 rows, then attend over all Nk rows."""
+    import torch
+
+    from attn_workloads import make_qkv
+    from exact_tiled_attention_35_amd import (attn_decode_num_splits, attn_decode_ptr,
+                                              attn_decode_workspace_size)
+    from exact_tiled_attention_35_amd.attention import _DTYPE_CODE
+
+    q = make_qkv(w.B, w.Nq, w.Nq, w.Hq, w.Hq, w.d, w.dtype, w.sigma, w.seed)[0]
+    _, kc, vc = make_qkv(w.B, 1, w.Nk, 1, w.Hkv, w.d, w.dtype, w.sigma, w.seed + 1)
+    _, kn, vn = make_qkv(w.B, 1, 1, 1, w.Hkv, w.d, w.dtype, w.sigma, w.seed + 2)
+    stream = torch.cuda.current_stream(dev)
+    gq, gkc, gvc, gkn, gvn = (t.to(dev) for t in (q, kc, vc, kn, vn))
+    sl = torch.full((w.B,), w.Nk - 1, dtype=torch.int32, device=dev)
+    out = torch.empty_like(gq)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    splits = attn_decode_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+    ws_bytes = attn_decode_workspace_size(w.B, w.Hq, w.Nq, w.d, splits)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    args_c = [t.data_ptr() for t in (gq, gkc, gvc, sl, gkn, gvn, out, lse, ws)]
+
+    def step():
+        code = attn_decode_ptr(*args_c, ws_bytes, w.B, w.Hq, w.Hkv, w.Nq, w.Nk, 1, w.d, w.scale,
+                               w.causal, _DTYPE_CODE[gq.dtype], splits, stream.cuda_stream)
+        if code != 0:
+            raise SystemExit(f"attn_decode failed with status {code}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_s = sum(kernel_ms) / K / 1e3
+    nbytes = decode_bytes(w)
+    value = nbytes / (wall / K) / 1e9
+    achieved = nbytes / avg_s / 1e9
+    peak = 8000.0
+    log(f"[bench] {K} steps: {wall / K * 1e3:.4f} ms/step wall, call avg {avg_s * 1e6:.1f} us "
+        f"(min {min(kernel_ms) * 1e3:.1f} us), {achieved:.1f} GB/s = {100 * achieved / peak:.1f}% "
+        f"of HBM peak, {splits} splits")
+    result = {
+        "metric": "attention decode GB/s (K/V cache read once plus q, out, lse and the appended "
+                  "rows, per call) and % of MI355X HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0, sigma^2) inputs rounded to the element type)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
+                   "cache_rows": w.Nk, "appended_rows": 1, "d": w.d, "causal": w.causal,
+                   "splits": splits, "seed": w.seed, "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "GB/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "algorithmic_bytes": nbytes,
+            "kernel_avg_us": round(avg_s * 1e6, 2),
+            "unit_of_work": "one attn_decode call: append, split attention and merge kernels",
+        },
+        "cpu_baseline": None,
+        "context": "KV-cache decode; the headline metric is the forward (--op fwd)",
+    }
+    if not args.no_cpu_baseline:
+        del gq, gkc, gvc
+        kcf = kc.clone()
+        kcf[:, w.Nk - 1] = kn[:, 0]
+        vcf = vc.clone()
+        vcf[:, w.Nk - 1] = vn[:, 0]
+        result["cpu_baseline"] = cpu_baseline_decode(w, q, kcf, vcf, args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 

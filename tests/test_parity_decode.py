@@ -106,3 +106,34 @@ def test_decode_matches_forward_when_cache_is_full():
     o2, l2 = attn_fwd(q, k, v, None, True)
     assert (o1.double() - o2.double()).abs().max() <= 1.6e-2
     assert (l1 - l2).abs().max() <= 1e-4
+
+
+@pytest.mark.parametrize("name", ["decode_b16_hq32_hkv8_cache32768_d128_bf16",
+                                  "decode_b1_hq32_hkv8_cache131072_d128_bf16"])
+def test_decode_workload_full_size(name):
+    # The benchmark's decode workloads, in the launch configuration bench.py
+    # times (library-chosen splits), checked on every query head of a few
+    # sequences against the oracle.
+    from attn_workloads import DECODE_WORKLOADS
+    from exact_tiled_attention_35_amd import attn_decode
+
+    w = DECODE_WORKLOADS[name]
+    q = make_qkv(w.B, w.Nq, w.Nq, w.Hq, w.Hq, w.d, w.dtype, w.sigma, w.seed)[0]
+    _, kc, vc = make_qkv(w.B, 1, w.Nk, 1, w.Hkv, w.d, w.dtype, w.sigma, w.seed + 1)
+    _, kn, vn = make_qkv(w.B, 1, 1, 1, w.Hkv, w.d, w.dtype, w.sigma, w.seed + 2)
+    sl = torch.full((w.B,), w.Nk - 1, dtype=torch.int32)
+    kg, vg = kc.cuda(), vc.cuda()
+    out, lse = attn_decode(q.cuda(), kg, vg, sl.cuda(), kn.cuda(), vn.cuda(), w.scale, w.causal, 0)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().double().numpy(), lse.cpu().double().numpy()
+    kc[:, w.Nk - 1] = kn[:, 0]
+    vc[:, w.Nk - 1] = vn[:, 0]
+    assert torch.equal(kg[:, w.Nk - 1].cpu(), kn[:, 0]) and torch.equal(vg[:, w.Nk - 1].cpu(), vn[:, 0])
+    worst = 0.0
+    for b in sorted({0, w.B // 2, w.B - 1}):
+        O, L = oracle.attention(q[b:b + 1], kc[b:b + 1], vc[b:b + 1], w.scale, w.causal)
+        err = np.abs(out[b:b + 1] - O)
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
+        assert np.abs(lse[b:b + 1] - L).max() <= LSE_ABS
+        worst = max(worst, float(err.max()))
+    print(f"[parity-decode] {name}: worst max-abs {worst:.3e}", flush=True)
