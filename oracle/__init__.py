@@ -20,4 +20,5 @@ from .exact import (  # noqa: F401
     kv_head_of,
     allowed_keys,
     materialised_score_bytes,
+    visible_range,
 )

@@ -37,6 +37,13 @@ Readings where the pages are silent (each is listed in the design notes):
 * logsumexp: natural log of the sum of exp over the scaled, masked scores.
 * a query row with no visible key (causal, Nq > Nk) has output 0 and
   logsumexp -inf (the empty-sum limit).
+* score variants (the interface section lists ``window_size`` and
+  ``alibi_slopes`` among the parameters; section "Von 2.0 bis 2.7" dates
+  sliding windows to 2.3, ALiBi to 2.4 and softcapping to 2.6): with
+  diag = Nk - Nq, a window (left, right) keeps key j for row i iff
+  i + diag - left <= j <= i + diag + right (a negative bound is no bound);
+  softcapping replaces the scaled score t by cap * tanh(t / cap); ALiBi then
+  adds -slope_h * |i + diag - j|.  The softmax runs over the result.
 
 The backward pass (``attention_backward``): the pages say the library
 computes gradients (hysenlabs.com page, section "GPU-Abdeckung: Ampere,
@@ -59,6 +66,7 @@ __all__ = [
     "attention_backward",
     "kv_head_of",
     "allowed_keys",
+    "visible_range",
     "materialised_score_bytes",
 ]
 
@@ -85,6 +93,19 @@ def allowed_keys(i: int, Nq: int, Nk: int, causal: bool) -> int:
     if not causal:
         return Nk
     return int(max(0, min(Nk, i + (Nk - Nq) + 1)))
+
+
+def visible_range(i: int, Nq: int, Nk: int, causal: bool, window=(-1, -1)):
+    """Keys [lo, hi) visible to query row ``i``: the causal bound of
+    ``allowed_keys`` intersected with a (left, right) window around the
+    bottom-right aligned diagonal key i + (Nk - Nq)."""
+    left, right = window
+    diag = Nk - Nq
+    hi = allowed_keys(i, Nq, Nk, causal)
+    if right >= 0:
+        hi = min(hi, max(0, min(Nk, i + diag + right + 1)))
+    lo = max(0, i + diag - left) if left >= 0 else 0
+    return lo, max(lo, hi)
 
 
 def materialised_score_bytes(Nq: int, Nk: int, bytes_per_cell: int = 2) -> int:
@@ -114,7 +135,8 @@ def _check_shapes(q: np.ndarray, k: np.ndarray, v: np.ndarray):
     return B, Nq, Nk, Hq, Hkv, d
 
 
-def _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, want_p):
+def _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, want_p,
+                      window=(-1, -1), slope=0.0, softcap=0.0):
     """Exact attention for the query rows ``rows`` of one (b, h) pair.
 
     qh: [Nq, d]; kg, vg: [Nk, d] (already the KV head this query head reads).
@@ -123,9 +145,15 @@ def _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, want_p):
     rows = np.asarray(rows, dtype=np.int64)
     # Scores over ALL keys: s_ij = sigma * <q_i, k_j>.
     S = sigma * (qh[rows] @ kg.T)
-    # Mask: key j visible to row i iff j < allowed_keys(i).
-    counts = np.array([allowed_keys(int(i), Nq, Nk, causal) for i in rows], dtype=np.int64)
-    visible = np.arange(Nk)[None, :] < counts[:, None]
+    if softcap > 0.0:
+        S = softcap * np.tanh(S / softcap)
+    if slope != 0.0:
+        S = S - slope * np.abs(rows[:, None] + (Nk - Nq) - np.arange(Nk)[None, :])
+    # Mask: key j visible to row i iff lo(i) <= j < hi(i).
+    rng = np.array([visible_range(int(i), Nq, Nk, causal, window) for i in rows],
+                   dtype=np.int64).reshape(len(rows), 2)
+    kidx = np.arange(Nk)[None, :]
+    visible = (kidx >= rng[:, :1]) & (kidx < rng[:, 1:])
     S = np.where(visible, S, -np.inf)
     # Row-wise softmax over keys.  Subtracting the row maximum is the usual
     # stable evaluation; it does not change the value.
@@ -143,7 +171,8 @@ def _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, want_p):
 
 def attention(q, k, v, scale: float, causal: bool = False, *,
               return_scores: bool = False, return_probs: bool = False,
-              slab_rows: int = 512):
+              slab_rows: int = 512, window=(-1, -1), alibi_slopes=None,
+              softcap: float = 0.0):
     """Exact attention in fp64.
 
     Args:
@@ -156,6 +185,9 @@ def attention(q, k, v, scale: float, causal: bool = False, *,
          S and the probabilities P, shaped [B, Hq, Nq, Nk] (small inputs only).
       slab_rows: how many query rows are written out at once.  Every row is
          independent of the others, so this only bounds memory.
+      window: (left, right) sliding window around the diagonal; -1 = none.
+      alibi_slopes: one slope per query head (fp32 values), or None.
+      softcap: cap > 0 applies cap * tanh(t / cap) to the scaled scores.
 
     Returns:
       (O [B, Nq, Hq, d] fp64, lse [B, Hq, Nq] fp64[, S][, P]).
@@ -163,6 +195,9 @@ def attention(q, k, v, scale: float, causal: bool = False, *,
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     B, Nq, Nk, Hq, Hkv, d = _check_shapes(q, k, v)
     sigma = float(np.float32(scale))
+    cap = float(np.float32(softcap))
+    slopes = (np.zeros(Hq) if alibi_slopes is None
+              else np.asarray(alibi_slopes, dtype=np.float32).astype(np.float64).reshape(Hq))
     O = np.zeros((B, Nq, Hq, d))
     lse = np.full((B, Hq, Nq), -np.inf)
     S_all = np.full((B, Hq, Nq, Nk), -np.inf) if return_scores else None
@@ -174,7 +209,8 @@ def attention(q, k, v, scale: float, causal: bool = False, *,
             for r0 in range(0, Nq, max(1, slab_rows)):
                 rows = np.arange(r0, min(Nq, r0 + slab_rows))
                 Or, lr, Sr, Pr = _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk,
-                                                   causal, return_probs)
+                                                   causal, return_probs, tuple(window),
+                                                   float(slopes[h]), cap)
                 O[b, rows, h, :] = Or
                 lse[b, h, rows] = lr
                 if return_scores:
@@ -189,7 +225,8 @@ def attention(q, k, v, scale: float, causal: bool = False, *,
     return out
 
 
-def attention_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows):
+def attention_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows, *,
+                   window=(-1, -1), alibi_slopes=None, softcap: float = 0.0):
     """Exact attention for selected query rows of one (b, h) pair.
 
     Each output row depends only on its own query row and on all keys and
@@ -206,7 +243,9 @@ def attention_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows):
     kg = _as_f64(k[b, :, g, :])
     vg = _as_f64(v[b, :, g, :])
     sigma = float(np.float32(scale))
-    O, lse, _, _ = _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, False)
+    slope = 0.0 if alibi_slopes is None else float(np.float32(np.asarray(alibi_slopes).reshape(-1)[h]))
+    O, lse, _, _ = _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, False,
+                                     tuple(window), slope, float(np.float32(softcap)))
     return O, lse
 
 

@@ -277,8 +277,8 @@ def test_mutation_top_left_causal(monkeypatch):
 def test_mutation_transposed_value_rows(monkeypatch):
     real = oa._rows_of_one_head
 
-    def wrong(qh, kg, vg, sigma, rows, Nq, Nk, causal, want_p):
-        return real(qh, kg, vg[::-1].copy(), sigma, rows, Nq, Nk, causal, want_p)
+    def wrong(qh, kg, vg, sigma, rows, Nq, Nk, causal, want_p, *mods):
+        return real(qh, kg, vg[::-1].copy(), sigma, rows, Nq, Nk, causal, want_p, *mods)
 
     monkeypatch.setattr(oa, "_rows_of_one_head", wrong)
     assert not _pins_pass()
@@ -287,8 +287,8 @@ def test_mutation_transposed_value_rows(monkeypatch):
 def test_mutation_dropped_scale(monkeypatch):
     real = oa._rows_of_one_head
 
-    def wrong(qh, kg, vg, sigma, rows, Nq, Nk, causal, want_p):
-        return real(qh, kg, vg, 1.0, rows, Nq, Nk, causal, want_p)
+    def wrong(qh, kg, vg, sigma, rows, Nq, Nk, causal, want_p, *mods):
+        return real(qh, kg, vg, 1.0, rows, Nq, Nk, causal, want_p, *mods)
 
     monkeypatch.setattr(oa, "_rows_of_one_head", wrong)
     assert not _pins_pass()
