@@ -15,6 +15,7 @@ from .attention import (  # noqa: F401
     attn_decode_ptr,
     attn_decode_workspace_size,
     attn_fwd,
+    attn_fwd_ext_ptr,
     attn_fwd_ptr,
     attn_status_string,
     attn_version,

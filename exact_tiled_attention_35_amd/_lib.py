@@ -23,6 +23,7 @@ ATTN_ERR_ALIASING = -8
 ATTN_ERR_NO_DEVICE = -9
 ATTN_ERR_LAUNCH = -10
 ATTN_ERR_WORKSPACE = -11
+ATTN_ERR_BAD_ARGUMENT = -12
 
 # attn_dtype values.
 ATTN_DTYPE_F16 = 0
@@ -43,6 +44,9 @@ def load() -> ctypes.CDLL:
     vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp]
     lib.attn_fwd.restype = ci
+    lib.attn_fwd_ext.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, ci, vp, cf,
+                                 ci, vp]
+    lib.attn_fwd_ext.restype = ci
     lib.attn_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, ci, ci, cf, ci, ci, vp]
     lib.attn_bwd.restype = ci
     lib.attn_decode.argtypes = [vp] * 9 + [ctypes.c_size_t] + [ci] * 7 + [cf, ci, ci, ci, vp]

@@ -184,13 +184,29 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return _Attention.apply(q, k, v, softmax_scale, causal)
 
 
+def attn_fwd_ext_ptr(q: int, k: int, v: int, out: int, lse: int, B: int, Hq: int, Hkv: int,
+                     Nq: int, Nk: int, d: int, scale: float, causal: bool, window_left: int,
+                     window_right: int, alibi_slopes: int, softcap: float, dtype: int,
+                     stream: int = 0) -> int:
+    """The C entry point attn_fwd_ext with raw integer pointers."""
+    return _lib.load().attn_fwd_ext(q or None, k or None, v or None, out or None, lse or None,
+                                    int(B), int(Hq), int(Hkv), int(Nq), int(Nk), int(d),
+                                    float(scale), int(bool(causal)), int(window_left),
+                                    int(window_right), alibi_slopes or None, float(softcap),
+                                    int(dtype), stream or None)
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: float | None = None,
              causal: bool = False, out: torch.Tensor | None = None,
-             lse: torch.Tensor | None = None):
+             lse: torch.Tensor | None = None, window: tuple = (-1, -1),
+             alibi_slopes: torch.Tensor | None = None, softcap: float = 0.0):
     """Exact attention forward on the GPU.
 
     q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d]; contiguous bf16 or fp16 tensors
-    on one HIP device.  ``softmax_scale`` defaults to 1/sqrt(d).
+    on one HIP device.  ``softmax_scale`` defaults to 1/sqrt(d).  Score
+    variants (attn_fwd_ext): ``window`` = (left, right) keys around the
+    bottom-right diagonal (-1 = unbounded), ``alibi_slopes`` fp32 [Hq] on the
+    device, ``softcap`` > 0.
     Returns (out [B, Nq, Hq, d] of q's dtype, lse [B, Hq, Nq] fp32).
     """
     B, Nq, Hq, Hkv, Nk, d = _check_qkv(q, k, v)
@@ -205,11 +221,22 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: f
     if tuple(lse.shape) != (B, Hq, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() \
             or lse.device != q.device:
         raise ValueError("lse must be a contiguous fp32 tensor [B, Hq, Nq]")
+    left, right = (int(x) for x in window)
+    variants = left >= 0 or right >= 0 or alibi_slopes is not None or softcap != 0.0
+    if alibi_slopes is not None:
+        _check_like("alibi_slopes", alibi_slopes, (Hq,), torch.float32, q.device)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        code = attn_fwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                            lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, softmax_scale, causal,
-                            _DTYPE_CODE[q.dtype], stream)
+        if variants:
+            code = attn_fwd_ext_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, softmax_scale, causal,
+                                    left, right,
+                                    alibi_slopes.data_ptr() if alibi_slopes is not None else 0,
+                                    softcap, _DTYPE_CODE[q.dtype], stream)
+        else:
+            code = attn_fwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, softmax_scale, causal,
+                                _DTYPE_CODE[q.dtype], stream)
     if code != _lib.ATTN_OK:
         raise AttnError(code)
     return out, lse

@@ -24,40 +24,52 @@ using eta_host::overlaps;
 
 constexpr const char* kVersion = "0.2.0 gfx950 exact-tiled-attention fwd+bwd";
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool MODS>
 int launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
-           int Hkv, int Nq, int Nk, float scale, hipStream_t stream) {
+           int Hkv, int Nq, int Nk, float scale, const eta::ScoreMods& mods, hipStream_t stream) {
   using C = eta::TileCfg<D>;
   const int nqb = (Nq + C::BM - 1) / C::BM;
   const int64_t total64 = (int64_t)B * Hq * nqb;
   if (total64 > 0x7fffffff) return ATTN_ERR_BAD_SHAPE;
   const int total = (int)total64;
   const float c_log2 = scale * 1.44269504088896340736f;
-  const int prescale = scale > 0.f ? 0 : 1;
-  hipLaunchKernelGGL((eta::attn_fwd_kernel<D, BF16, CAUSAL>), dim3(total), dim3(C::kThreads), 0,
-                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+  // Score variants transform the raw scores themselves (no prescaling).
+  const int prescale = (!MODS && !(scale > 0.f)) ? 1 : 0;
+  hipLaunchKernelGGL((eta::attn_fwd_kernel<D, BF16, CAUSAL, MODS>), dim3(total), dim3(C::kThreads),
+                     0, stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq, Hkv, Nq,
-                     Nk, nqb, total, c_log2, prescale);
+                     Nk, nqb, total, c_log2, prescale, mods);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-template <int D>
+template <int D, bool MODS>
 int dispatch_dtype(bool bf16, bool causal, const void* q, const void* k, const void* v, void* out,
                    float* lse, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
-                   hipStream_t s) {
+                   const eta::ScoreMods& m, hipStream_t s) {
   if (bf16) {
-    return causal ? launch<D, true, true>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s)
-                  : launch<D, true, false>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s);
+    return causal ? launch<D, true, true, MODS>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, m, s)
+                  : launch<D, true, false, MODS>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, m, s);
   }
-  return causal ? launch<D, false, true>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s)
-                : launch<D, false, false>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s);
+  return causal ? launch<D, false, true, MODS>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, m, s)
+                : launch<D, false, false, MODS>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, m, s);
 }
 
-}  // namespace
+template <bool MODS>
+int dispatch_hdim(int d, bool bf16, bool c, const void* q, const void* k, const void* v, void* out,
+                  float* lse, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
+                  const eta::ScoreMods& m, hipStream_t s) {
+  switch (d) {
+    case 64: return dispatch_dtype<64, MODS>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, m, s);
+    case 128: return dispatch_dtype<128, MODS>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, m, s);
+    default: return dispatch_dtype<256, MODS>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, m, s);
+  }
+}
 
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
-                        int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
-                        void* stream) {
+// attn_fwd and attn_fwd_ext: validation in the documented order, then the
+// plain kernel or, when a score variant is active, its variant instance.
+int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+             int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+             const eta::ScoreMods* mods, void* stream) {
   // 1. shape
   if (B < 0 || Nq < 0 || Hq < 1 || Hkv < 1 || Nk < 1 || d < 1) return ATTN_ERR_BAD_SHAPE;
   // 2. empty problem: nothing to do
@@ -79,17 +91,23 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
   if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED_HDIM;
   // 6. element type
   if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
-  // 7. scale
+  // 7. scale, and the score variants' arguments
   if (!finite_bits(scale)) return ATTN_ERR_BAD_SCALE;
-  // 8. alignment (16-byte vector loads and stores)
+  if (mods && (mods->left < -1 || mods->right < -1 || !finite_bits(mods->cap) || mods->cap < 0.f))
+    return ATTN_ERR_BAD_ARGUMENT;
+  // 8. alignment (16-byte vector loads and stores; 4-byte slopes)
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
     return ATTN_ERR_MISALIGNED;
+  if (mods && mods->slopes && (reinterpret_cast<uintptr_t>(mods->slopes) & 3)) return ATTN_ERR_MISALIGNED;
   // 9. aliasing: outputs must not overlap inputs or each other
   const size_t qb = (size_t)q_elems * 2, kvb = (size_t)kv_elems * 2;
   const size_t lb = (size_t)B * Hq * Nq * sizeof(float);
   if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kvb) || overlaps(out, qb, v, kvb) ||
       overlaps(lse, lb, q, qb) || overlaps(lse, lb, k, kvb) || overlaps(lse, lb, v, kvb) ||
       overlaps(out, qb, lse, lb))
+    return ATTN_ERR_ALIASING;
+  if (mods && mods->slopes &&
+      (overlaps(out, qb, mods->slopes, Hq * 4) || overlaps(lse, lb, mods->slopes, Hq * 4)))
     return ATTN_ERR_ALIASING;
   // 10. device
   const int dev_status = check_device();
@@ -98,11 +116,26 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
   const bool bf16 = dtype == ATTN_DTYPE_BF16;
   const bool c = causal != 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (d) {
-    case 64: return dispatch_dtype<64>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s);
-    case 128: return dispatch_dtype<128>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s);
-    default: return dispatch_dtype<256>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, s);
-  }
+  const bool active = mods && (mods->left >= 0 || mods->right >= 0 || mods->slopes || mods->cap > 0.f);
+  if (active) return dispatch_hdim<true>(d, bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, *mods, s);
+  const eta::ScoreMods none{-1, -1, nullptr, 0.f, scale};
+  return dispatch_hdim<false>(d, bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, none, s);
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                        int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                        void* stream) {
+  return fwd_impl(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, nullptr, stream);
+}
+
+extern "C" int attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* lse,
+                            int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                            int window_left, int window_right, const float* alibi_slopes,
+                            float softcap, int dtype, void* stream) {
+  const eta::ScoreMods mods{window_left, window_right, alibi_slopes, softcap, scale};
+  return fwd_impl(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, &mods, stream);
 }
 
 extern "C" const char* attn_status_string(int status) {
@@ -120,6 +153,8 @@ extern "C" const char* attn_status_string(int status) {
     case ATTN_ERR_NO_DEVICE: return "ATTN_ERR_NO_DEVICE: no HIP device, or the current device is not gfx950";
     case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: kernel launch failed";
     case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace smaller than attn_decode_workspace_size";
+    case ATTN_ERR_BAD_ARGUMENT:
+      return "ATTN_ERR_BAD_ARGUMENT: window bounds must be >= -1 and softcap finite and >= 0";
     default: return "unknown attn status";
   }
 }

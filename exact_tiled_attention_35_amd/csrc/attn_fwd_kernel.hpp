@@ -53,6 +53,7 @@
 
 namespace eta {
 
+constexpr float kLog2e_f = 1.44269504088896340736f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p <= 256 between rescales
 // Unmasked tiles keep the current running max unless a row's tile sum
 // exceeds this (every p then stays far inside the fp16 range of P).
@@ -103,12 +104,28 @@ struct TileCfg {
 };
 
 
-template <int D, bool BF16, bool CAUSAL>
+// Score variants (the sliding window, ALiBi and softcapping of the pages'
+// interface and version history): with diag = Nk - Nq, key j is kept for row
+// i iff i + diag - left <= j <= i + diag + right (negative = no bound); the
+// scaled score t becomes cap * tanh(t / cap) when cap > 0, and then
+// t - slope[h] * |i + diag - j| when slopes is not NULL.
+struct ScoreMods {
+  int left, right;
+  const float* slopes;
+  float cap, sigma;
+};
+
+// tanh(x) = 1 - 2 / (2^(2x log2 e) + 1); saturates to +-1 for large |x|.
+__device__ __forceinline__ float tanh_fast(float x) {
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * 2.88539008177792681472f) + 1.0f);
+}
+
+template <int D, bool BF16, bool CAUSAL, bool MODS = false>
 __global__ void __launch_bounds__(TileCfg<D>::kThreads, TileCfg<D>::kMinWavesPerEU)
 attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                 float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int nqb,
-                int total, float c_log2, int prescale) {
+                int total, float c_log2, int prescale, ScoreMods mods) {
   using C = TileCfg<D>;
   constexpr int BN = C::BN, BM = C::BM, KS = C::KS, VS = C::VS;
   constexpr int NKS = D / 16;  // k-steps of the S^T product
@@ -162,10 +179,24 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // ---- Key range of the workgroup and of this wave.
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, min(q0 + BM, Nq) + diag);
-  const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   const int rows_end = min(qw0 + 32, Nq);
   int w_end = rows_end > qw0 ? Nk : 0;
   if (CAUSAL && rows_end > qw0) w_end = min(Nk, rows_end + diag);
+  // Window: keys right of the last row's window are never loaded, tiles left
+  // of the first row's window are skipped (jb = first tile), and a wave skips
+  // tiles outside its own rows' windows.
+  int jb = 0, w_begin = 0;
+  if constexpr (MODS) {
+    if (mods.right >= 0) {
+      kv_end = min(kv_end, max(0, min(q0 + BM, Nq) + diag + mods.right));
+      if (rows_end > qw0) w_end = min(w_end, max(0, rows_end + diag + mods.right));
+    }
+    if (mods.left >= 0) {
+      jb = max(0, q0 + diag - mods.left) / BN;
+      w_begin = qw0 + diag - mods.left;
+    }
+  }
+  const int nt = kv_end > jb * BN ? (kv_end - jb * BN + BN - 1) / BN : 0;
 
   // ---- Direct global->LDS tile loads.  This wave issues the K (V) tile's
   // instructions j = wave, wave + 4, ...; lane -> 16-byte slot 64 j + lane ->
@@ -210,9 +241,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16_t{};
   float m = -INFINITY;  // running max of t = s * c_log2 (log2 units)
   float lsum = 0.f;     // this lane half's share of the running sum
-  const float ce = prescale ? 1.0f : c_log2;
+  // With score variants the transformed scores are held in log2 units.
+  const float ce = (MODS || prescale) ? 1.0f : c_log2;
+  float slope = 0.f;
+  if constexpr (MODS) slope = mods.slopes ? mods.slopes[w.hq] : 0.f;
 
-  if (nt > 0) issue_tile(0, smem);
+  if (nt > 0) issue_tile(jb * BN, smem);
   __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tile 0 have landed
   __syncthreads();
 
@@ -290,13 +324,14 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int kLean = 0, kFull = 1, kMasked = 2;
   auto tile = [&](int t, auto mode) {
     constexpr int kMode = decltype(mode)::value;
-    const int j0 = t * BN;
+    const int j0 = (jb + t) * BN;
     // Tile t+1 streams into the other stage while this one is computed (that
     // stage was last read in iteration t-1, before the barrier that ended it).
     if (t + 1 < nt) issue_tile(j0 + BN, smem + ((t + 1) & 1) * C::kStage);
     const uint16_t* st = smem + (t & 1) * C::kStage;
 
-    if (j0 < w_end) {  // wave-uniform: skip tiles above this wave's diagonal
+    // wave-uniform: skip tiles above this wave's diagonal (or outside its window)
+    if (j0 < w_end && (!MODS || j0 + BN > w_begin)) {
       f32x16_t s[NKB];
       // The matrix phases (S^T here, O^T below) run at raised wave priority,
       // so that on a SIMD shared with a wave in its softmax phase the MFMA
@@ -317,7 +352,26 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         // Mask keys past the end and (causal) above the diagonal.
         need_mask = kMode == kMasked &&
                     ((j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + diag));
-        if (need_mask) {
+        if constexpr (MODS) {
+          // Softcap, ALiBi and the window on every element; log2 units.
+          if (mods.left >= 0 && j0 < qw0 + 31 + diag - mods.left) need_mask = true;
+          if (mods.right >= 0 && j0 + BN - 1 > qw0 + diag + mods.right) need_mask = true;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+              const int dist = my_q + diag - j;
+              float tv = s[kb][r] * mods.sigma;
+              if (mods.cap > 0.f) tv = mods.cap * tanh_fast(tv * __builtin_amdgcn_rcpf(mods.cap));
+              tv -= slope * (float)(dist < 0 ? -dist : dist);
+              const bool vis = j < Nk && (!CAUSAL || dist >= 0) &&
+                               (mods.left < 0 || dist <= mods.left) &&
+                               (mods.right < 0 || -dist <= mods.right);
+              s[kb][r] = vis ? tv * kLog2e_f : -INFINITY;
+            }
+          }
+        } else if (need_mask) {
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -360,7 +414,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
       };
       __builtin_amdgcn_s_setprio(1);
-      if (CAUSAL && need_mask)
+      if ((CAUSAL || MODS) && need_mask)
         pv_product(std::true_type{});
       else
         pv_product(std::false_type{});
@@ -377,6 +431,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int nf = Nk / BN;
   if (CAUSAL) nf = min(nf, max(0, (q0 + diag + 1) / BN));
   nf = min(nf, nt);
+  if constexpr (MODS) nf = 0;  // score variants: every tile takes the masked body
   using LeanMode = std::integral_constant<int, kLean>;
   using FullMode = std::integral_constant<int, kFull>;
   using MaskedMode = std::integral_constant<int, kMasked>;

@@ -71,7 +71,8 @@ typedef enum {
   ATTN_ERR_ALIASING = -8,          /* out or lse overlaps an input, or each other        */
   ATTN_ERR_NO_DEVICE = -9,         /* no HIP device, or the current device is not gfx950 */
   ATTN_ERR_LAUNCH = -10,           /* the kernel launch failed                            */
-  ATTN_ERR_WORKSPACE = -11         /* attn_decode: workspace smaller than required       */
+  ATTN_ERR_WORKSPACE = -11,        /* attn_decode: workspace smaller than required       */
+  ATTN_ERR_BAD_ARGUMENT = -12      /* attn_fwd_ext: window bound < -1, bad softcap       */
 } attn_status;
 
 /*
@@ -89,6 +90,29 @@ typedef enum {
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int Hq, int Hkv, int Nq, int Nk, int d,
              float scale, int causal, int dtype, void* stream);
+
+/*
+ * attn_fwd with score variants: the sliding window, ALiBi and softcapping
+ * that the hysenlabs.com page lists among the interface parameters
+ * (window_size, alibi_slopes; section "Die Schnittstellen von
+ * flash_attn_func bis KV-Cache") and dates in its version history (2.3,
+ * 2.4, 2.6; section "Von 2.0 bis 2.7").  With diag = Nk - Nq and
+ * t = scale * <q_i, k_j>:
+ *   window       key j kept for row i iff i + diag - window_left <= j and
+ *                j <= i + diag + window_right (-1 = no bound on that side;
+ *                combined with the causal mask when causal != 0)
+ *   softcap      > 0: t = softcap * tanh(t / softcap); 0 = off
+ *   alibi_slopes NULL, or Hq fp32 device values: t -= slopes[h] * |i + diag - j|
+ * then softmax over the kept keys as in attn_fwd (rows with no kept key:
+ * out = 0, lse = -inf).  With every variant off this is attn_fwd.
+ * Additional errors: ATTN_ERR_BAD_ARGUMENT (window bound < -1, softcap
+ * negative or not finite), ATTN_ERR_MISALIGNED (slopes not 4-byte aligned),
+ * ATTN_ERR_ALIASING (out or lse overlapping the slopes).
+ */
+int attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* lse,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                 int window_left, int window_right, const float* alibi_slopes, float softcap,
+                 int dtype, void* stream);
 
 /*
  * Exact attention backward: gradients of L = sum(dout * out) with respect to

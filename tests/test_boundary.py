@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
     assert names == ["attn_bwd", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_size",
-                     "attn_fwd", "attn_status_string", "attn_version"]
+                     "attn_fwd", "attn_fwd_ext", "attn_status_string", "attn_version"]
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_messages():
     assert "gfx950" in attn_version()
-    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11]
+    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, -12]
     msgs = [attn_status_string(c) for c in codes]
     assert len(set(msgs)) == len(codes)
     assert msgs[0].startswith("ATTN_OK")
@@ -317,3 +317,45 @@ def test_decode_aliasing():
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a HIP device is visible here")
 def test_decode_no_device_reported_without_gpu():
     assert call_dec() == _lib.ATTN_ERR_NO_DEVICE
+
+
+# ---------------------------------------------------------------------------
+# attn_fwd_ext (score variants)
+# ---------------------------------------------------------------------------
+from exact_tiled_attention_35_amd.attention import attn_fwd_ext_ptr  # noqa: E402
+
+SLOPES = 0x700000000
+
+
+def call_ext(left=-1, right=-1, slopes=0, cap=0.0, **over):
+    a = dict(GOOD)
+    a.update(over)
+    return attn_fwd_ext_ptr(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                            a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], left, right, slopes,
+                            cap, a["dtype"])
+
+
+def test_ext_without_variants_validates_like_attn_fwd():
+    assert call_ext(q=0) == _lib.ATTN_ERR_NULL_POINTER
+    assert call_ext() == call()
+    assert call_ext(Hkv=3) == _lib.ATTN_ERR_GQA_RATIO
+    assert call_ext(B=0, q=0) == _lib.ATTN_OK
+
+
+@pytest.mark.parametrize("args", [dict(left=-2), dict(right=-5), dict(cap=-1.0),
+                                  dict(cap=float("nan")), dict(cap=float("inf"))])
+def test_ext_bad_argument(args):
+    assert call_ext(**args) == _lib.ATTN_ERR_BAD_ARGUMENT
+
+
+def test_ext_order_misaligned_and_aliasing():
+    assert call_ext(left=-2, scale=float("nan")) == _lib.ATTN_ERR_BAD_SCALE
+    assert call_ext(left=-2, q=Q + 2) == _lib.ATTN_ERR_BAD_ARGUMENT
+    assert call_ext(slopes=SLOPES + 2) == _lib.ATTN_ERR_MISALIGNED
+    assert call_ext(slopes=OUT + 64) == _lib.ATTN_ERR_ALIASING
+    assert call_ext(slopes=LSE) == _lib.ATTN_ERR_ALIASING
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a HIP device is visible here")
+def test_ext_no_device_reported_without_gpu():
+    assert call_ext(left=4, right=0, slopes=SLOPES, cap=30.0) == _lib.ATTN_ERR_NO_DEVICE
