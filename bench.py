@@ -65,6 +65,27 @@ def decode_bytes(w) -> int:
             + w.B * 1 * w.Hkv * w.d * el * 4)
 
 
+def visible_pairs(Nq: int, Nk: int, causal: bool, left: int, right: int) -> int:
+    """Number of (query, key) pairs a row-wise window / causal mask keeps
+    (bottom-right aligned: key j kept for row i iff lo_i <= j <= hi_i)."""
+    import numpy as np
+
+    i = np.arange(Nq, dtype=np.int64)
+    dg = i + (Nk - Nq)
+    hi = np.full(Nq, Nk - 1, dtype=np.int64)
+    if causal:
+        hi = np.minimum(hi, dg)
+    if right >= 0:
+        hi = np.minimum(hi, dg + right)
+    lo = np.maximum(0, dg - left) if left >= 0 else np.zeros(Nq, dtype=np.int64)
+    return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def variant_flops(w, left, right) -> float:
+    """4 d flops per kept (query, key) pair and head (both products)."""
+    return 4.0 * w.B * w.Hq * w.d * visible_pairs(w.Nq, w.Nk, w.causal, left, right)
+
+
 def bwd_flops(w) -> float:
     """Five products of the forward's size: S, dP, dV, dK, dQ."""
     return 2.5 * flops(w)
@@ -280,6 +301,10 @@ def main():
                     help="fwd: attn_fwd (the headline metric); bwd: attn_bwd, the backward pass; "
                          "decode: attn_decode on a KV-cache decode workload")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--window", nargs=2, type=int, default=(-1, -1), metavar=("LEFT", "RIGHT"),
+                    help="fwd only: sliding window (attn_fwd_ext); flops count the kept pairs")
+    ap.add_argument("--softcap", type=float, default=0.0, help="fwd only: softcap (attn_fwd_ext)")
+    ap.add_argument("--alibi", action="store_true", help="fwd only: ALiBi slopes (attn_fwd_ext)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain elementwise copy kernel that "
@@ -324,9 +349,16 @@ def main():
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    variants = tuple(args.window) != (-1, -1) or args.softcap != 0.0 or args.alibi
     if args.op == "fwd":
+        slopes = None
+        if args.alibi:
+            slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / w.Hq) for h in range(w.Hq)],
+                                  dtype=torch.float32, device=dev)
+
         def step():
-            attn_fwd(dq, dk, dv, w.scale, w.causal, out=out, lse=lse)
+            attn_fwd(dq, dk, dv, w.scale, w.causal, out=out, lse=lse, window=tuple(args.window),
+                     alibi_slopes=slopes, softcap=args.softcap)
     else:
         from attn_workloads import make_qkv
 
@@ -364,10 +396,12 @@ def main():
     ms_per_step = wall / K * 1e3
 
     F = flops(w) if args.op == "fwd" else bwd_flops(w)
+    if args.op == "fwd" and variants:
+        F = variant_flops(w, *args.window)
     value = F / (wall / K) / 1e12
     achieved = F / avg_kernel_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = measured_traffic(w.name) if args.op == "fwd" else None
+    traffic = measured_traffic(w.name) if args.op == "fwd" and not variants else None
     log(f"[bench] {K} steps: {ms_per_step:.4f} ms/step wall, kernel avg {avg_kernel_s*1e6:.1f} us "
         f"(min {min(kernel_ms)*1e3:.1f} us), {achieved:.1f} TFLOP/s = {100*achieved/peak:.1f}% of peak")
 
@@ -404,13 +438,21 @@ def main():
     if args.calibration_copy_mib:
         calibration_copy(args.calibration_copy_mib)
         result["calibration_copy_bytes"] = args.calibration_copy_mib * 2**20
+    if variants:
+        result["config"]["variants"] = {"window": list(args.window), "softcap": args.softcap,
+                                         "alibi": bool(args.alibi)}
+        result["metric"] = ("attention fwd TFLOP/s with score variants (4*d per kept "
+                            "(query, key) pair and head)")
+        result["context"] = "score variants (attn_fwd_ext); the headline metric is plain attn_fwd"
     if args.op == "bwd":
         result["roofline"]["unit_of_work"] = ("one attn_bwd call: the dQ kernel and the dK/dV "
                                               "kernel back to back")
         result["context"] = "backward pass; the headline metric is the forward (--op fwd)"
     if not args.no_cpu_baseline:
         del dq, dk, dv
-        if args.op == "fwd":
+        if args.op == "fwd" and variants:
+            result["cpu_baseline"] = None  # the oracle baseline is timed on the plain forward
+        elif args.op == "fwd":
             result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
         else:
             result["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do, args.cpu_budget)

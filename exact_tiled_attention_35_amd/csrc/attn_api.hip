@@ -33,8 +33,10 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, i
   if (total64 > 0x7fffffff) return ATTN_ERR_BAD_SHAPE;
   const int total = (int)total64;
   const float c_log2 = scale * 1.44269504088896340736f;
-  // Score variants transform the raw scores themselves (no prescaling).
-  const int prescale = (!MODS && !(scale > 0.f)) ? 1 : 0;
+  // Softcap and ALiBi transform the raw scores themselves (no prescaling);
+  // a window alone keeps the plain kernel's scaling.
+  const bool transform = MODS && (mods.slopes || mods.cap > 0.f);
+  const int prescale = (!transform && !(scale > 0.f)) ? 1 : 0;
   hipLaunchKernelGGL((eta::attn_fwd_kernel<D, BF16, CAUSAL, MODS>), dim3(total), dim3(C::kThreads),
                      0, stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq, Hkv, Nq,

@@ -241,8 +241,10 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16_t{};
   float m = -INFINITY;  // running max of t = s * c_log2 (log2 units)
   float lsum = 0.f;     // this lane half's share of the running sum
-  // With score variants the transformed scores are held in log2 units.
-  const float ce = (MODS || prescale) ? 1.0f : c_log2;
+  // A window alone leaves the scores as they are ("plain"); softcap or ALiBi
+  // transform them, and the transformed scores are held in log2 units.
+  const bool plain = !MODS || (!mods.slopes && !(mods.cap > 0.f));
+  const float ce = (!plain || prescale) ? 1.0f : c_log2;
   float slope = 0.f;
   if constexpr (MODS) slope = mods.slopes ? mods.slopes[w.hq] : 0.f;
 
@@ -362,13 +364,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             for (int r = 0; r < 16; ++r) {
               const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
               const int dist = my_q + diag - j;
-              float tv = s[kb][r] * mods.sigma;
-              if (mods.cap > 0.f) tv = mods.cap * tanh_fast(tv * __builtin_amdgcn_rcpf(mods.cap));
-              tv -= slope * (float)(dist < 0 ? -dist : dist);
+              float tv = s[kb][r];
+              if (!plain) {
+                tv *= mods.sigma;
+                if (mods.cap > 0.f) tv = mods.cap * tanh_fast(tv * __builtin_amdgcn_rcpf(mods.cap));
+                tv = (tv - slope * (float)(dist < 0 ? -dist : dist)) * kLog2e_f;
+              }
               const bool vis = j < Nk && (!CAUSAL || dist >= 0) &&
                                (mods.left < 0 || dist <= mods.left) &&
                                (mods.right < 0 || -dist <= mods.right);
-              s[kb][r] = vis ? tv * kLog2e_f : -INFINITY;
+              s[kb][r] = vis ? tv : -INFINITY;
             }
           }
         } else if (need_mask) {
@@ -428,16 +433,33 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // them (m still -inf) takes the full body, the rest the lean one; tiles
   // from nf on take the masked body.  Separate loops keep each body's
   // register allocation free of the others' state.
+  // Tiles [t_lo, nf) are visible to every row of the workgroup.  A window
+  // adds masked tiles at its left edge (before t_lo) and bounds nf on the
+  // right; softcap and ALiBi change every score, so with them every tile
+  // takes the masked body.
   int nf = Nk / BN;
   if (CAUSAL) nf = min(nf, max(0, (q0 + diag + 1) / BN));
-  nf = min(nf, nt);
-  if constexpr (MODS) nf = 0;  // score variants: every tile takes the masked body
+  int t_lo = 0;
+  if constexpr (MODS) {
+    if (mods.right >= 0) nf = min(nf, max(0, (q0 + diag + mods.right + 1) / BN));
+    if (mods.left >= 0) {
+      const int q_last = min(q0 + BM, Nq) - 1;
+      t_lo = max(0, (q_last + diag - mods.left + BN - 1) / BN - jb);
+    }
+    nf -= jb;
+    if (!plain) t_lo = nf = 0;
+  }
+  nf = min(max(nf, 0), nt);
+  t_lo = min(t_lo, nf);
   using LeanMode = std::integral_constant<int, kLean>;
   using FullMode = std::integral_constant<int, kFull>;
   using MaskedMode = std::integral_constant<int, kMasked>;
   int t = 0;
+  if constexpr (MODS) {
+    for (; t < t_lo; ++t) tile(t, MaskedMode{});
+  }
   if constexpr (C::kLeanTiles) {
-    if (nf > 0) tile(t++, FullMode{});
+    if (t < nf) tile(t++, FullMode{});
     for (; t < nf; ++t) tile(t, LeanMode{});
   } else {
     for (; t < nf; ++t) tile(t, FullMode{});

@@ -108,6 +108,19 @@ def test_variants_against_oracle(shape, var):
     print(f"[parity-variants] {shape} {var}: max-abs {e:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_window_with_nonpositive_scale(scale):
+    check((1, 2, 1, 300, 300, 128, "bf16", True), (70, -1), False, 0.0, 1103, scale=scale)
+    check((1, 2, 1, 300, 300, 128, "bf16", False), (70, 20), True, 0.0, 1104, scale=scale)
+
+
+def test_long_window_interior_tiles():
+    # a window much longer than a tile: most tiles are fully inside every
+    # row's window and take the unmasked bodies
+    check((1, 4, 2, 1100, 1100, 128, "bf16", True), (511, -1), False, 0.0, 1105)
+    check((1, 4, 2, 700, 1300, 64, "fp16", False), (300, 200), False, 0.0, 1106)
+
+
 def test_variants_with_large_scale_and_tight_softcap():
     check((1, 2, 2, 200, 200, 128, "bf16", True), (40, -1), True, 2.0, 1100, scale=0.5)
 
