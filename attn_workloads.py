@@ -95,3 +95,45 @@ def make_qkv(B, Nq, Nk, Hq, Hkv, d, dtype="bf16", sigma=1.0, seed=0):
 
 def make_workload(w: Workload):
     return make_qkv(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.dtype, w.sigma, w.seed)
+
+
+def varlen_lengths(total, lo, hi, seed):
+    """Sequence lengths drawn uniformly from [lo, hi] until they sum to
+    ``total`` (the last one trimmed), from a seeded CPU generator."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    lens = []
+    while sum(lens) < total:
+        lens.append(int(torch.randint(lo, hi + 1, (1,), generator=g)))
+    lens[-1] -= sum(lens) - total
+    return lens
+
+
+def make_varlen(lens_q, lens_k, Hq, Hkv, d, dtype="bf16", sigma=1.0, seed=0):
+    """Packed q [sum(lens_q), Hq, d], k and v [sum(lens_k), Hkv, d] (CPU) and
+    the int32 prefix sums cu_q, cu_k [B + 1]; values drawn as in make_qkv."""
+    dt = DTYPES[dtype]
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    tq, tk = int(sum(lens_q)), int(sum(lens_k))
+
+    def draw(shape):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        if sigma != 1.0:
+            x.mul_(sigma)
+        return x.to(dt)
+
+    q = draw((tq, Hq, d))
+    k = draw((tk, Hkv, d))
+    v = draw((tk, Hkv, d))
+    cu_q = torch.tensor([0] + list(torch.tensor(lens_q, dtype=torch.int64).cumsum(0)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(torch.tensor(lens_k, dtype=torch.int64).cumsum(0)), dtype=torch.int32)
+    return q, k, v, cu_q, cu_k
+
+
+# Packed variable-length self-attention: 16384 tokens in sequences of 256 to
+# 4096 tokens (the README benchmark's 16k tokens per batch and hidden 2048 as
+# 16 heads of 128), seed 8; causal and not.
+VARLEN_WORKLOADS = {
+    n: dict(name=n, total=16384, lo=256, hi=4096, H=16, d=128, dtype="bf16", seed=8, causal=c)
+    for n, c in (("varlen_causal_t16384_len256to4096_h16_d128_bf16", True),
+                 ("varlen_t16384_len256to4096_h16_d128_bf16", False))
+}

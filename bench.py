@@ -297,9 +297,10 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
-    ap.add_argument("--op", choices=("fwd", "bwd", "decode"), default="fwd",
+    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "varlen"), default="fwd",
                     help="fwd: attn_fwd (the headline metric); bwd: attn_bwd, the backward pass; "
-                         "decode: attn_decode on a KV-cache decode workload")
+                         "decode: attn_decode on a KV-cache decode workload; varlen: "
+                         "attn_fwd_varlen on packed variable-length sequences")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--window", nargs=2, type=int, default=(-1, -1), metavar=("LEFT", "RIGHT"),
                     help="fwd only: sliding window (attn_fwd_ext); flops count the kept pairs")
@@ -327,10 +328,15 @@ def main():
 
     import torch
 
-    from attn_workloads import DECODE_WORKLOADS, HEADLINE, WORKLOADS, make_workload
+    from attn_workloads import DECODE_WORKLOADS, HEADLINE, VARLEN_WORKLOADS, WORKLOADS, make_workload
     from exact_tiled_attention_35_amd import attn_bwd_ptr, attn_fwd, attn_version
     from exact_tiled_attention_35_amd.attention import _DTYPE_CODE
 
+    if args.op == "varlen":
+        if not torch.cuda.is_available():
+            log("no GPU visible")
+            sys.exit(1)
+        return bench_varlen(args, VARLEN_WORKLOADS[args.workload or next(iter(VARLEN_WORKLOADS))])
     if args.op == "decode":
         w = DECODE_WORKLOADS[args.workload or next(iter(DECODE_WORKLOADS))]
     else:
@@ -550,6 +556,129 @@ def bench_decode(args, w, dev):
         vcf = vc.clone()
         vcf[:, w.Nk - 1] = vn[:, 0]
         result["cpu_baseline"] = cpu_baseline_decode(w, q, kcf, vcf, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_varlen(wl, lens, q, k, v, scale, budget_s: float):
+    """Time the fp64 oracle sequence by sequence and head by head (all rows of
+    each) until ``budget_s`` is spent."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        blas_threads = os.cpu_count() or 1
+    starts = [0]
+    for n in lens:
+        starts.append(starts[-1] + n)
+    done, f = 0, 0.0
+    t0 = time.perf_counter()
+    for b, n in enumerate(lens):
+        s = starts[b]
+        for h in range(wl["H"]):
+            oracle.attention_rows(q[None, s:s + n], k[None, s:s + n], v[None, s:s + n], scale,
+                                  wl["causal"], 0, h, np.arange(n))
+            f += 4.0 * wl["d"] * visible_pairs(n, n, wl["causal"], -1, -1)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": f / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(lens) * wl['H']} (sequence, head) pairs in packing order, all "
+                  f"rows each, fp64 NumPy, {dt:.1f} s wall",
+    }
+
+
+def bench_varlen(args, wl):
+    """One step = one attn_fwd_varlen call over the packed batch; flops count
+    4*d per kept (query, key) pair and head, sequence by sequence."""
+    import torch
+
+    from attn_workloads import make_varlen, varlen_lengths
+    from exact_tiled_attention_35_amd import attn_fwd_varlen, attn_version
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {wl['name']}; library {attn_version()}")
+    lens = varlen_lengths(wl["total"], wl["lo"], wl["hi"], wl["seed"])
+    H, d, causal = wl["H"], wl["d"], wl["causal"]
+    q, k, v, cu_q, cu_k = make_varlen(lens, lens, H, H, d, wl["dtype"], 1.0, wl["seed"])
+    scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    gq, gk, gv, gcq, gck = (t.to(dev) for t in (q, k, v, cu_q, cu_k))
+    stream = torch.cuda.current_stream(dev)
+    max_q = max(lens)
+
+    def step():
+        attn_fwd_varlen(gq, gk, gv, gcq, gck, max_q, scale, causal)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_s = sum(kernel_ms) / K / 1e3
+    F = sum(4.0 * H * d * visible_pairs(n, n, causal, -1, -1) for n in lens)
+    value = F / (wall / K) / 1e12
+    achieved = F / avg_s / 1e12
+    peak = PEAK_TFLOPS[wl["dtype"]]
+    total = wl["total"]
+    nbytes = total * H * d * 2 * 4 + H * total * 4 + (len(lens) + 1) * 4 * 2
+    log(f"[bench] {K} steps: {wall / K * 1e3:.4f} ms/step wall, kernel avg {avg_s * 1e6:.1f} us "
+        f"(min {min(kernel_ms) * 1e3:.1f} us), {achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% "
+        f"of peak; lengths {lens}")
+    result = {
+        "metric": "attention fwd TFLOP/s over packed variable-length sequences (4*d per kept "
+                  "(query, key) pair and head)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl["dtype"],
+        "data": "synthetic (seeded N(0, 1) inputs rounded to the element type; seeded lengths)",
+        "config": {"workload": wl["name"], "total_tokens": total, "lengths": lens, "H": H,
+                   "d": d, "causal": causal, "seed": wl["seed"], "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "algorithmic_bytes": nbytes,
+            "kernel_avg_us": round(avg_s * 1e6, 2),
+        },
+        "cpu_baseline": None,
+        "context": "packed variable-length forward; the headline metric is the forward (--op fwd)",
+    }
+    if not args.no_cpu_baseline:
+        del gq, gk, gv
+        result["cpu_baseline"] = cpu_baseline_varlen(wl, lens, q, k, v, scale, args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 

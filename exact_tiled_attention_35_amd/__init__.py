@@ -17,6 +17,8 @@ from .attention import (  # noqa: F401
     attn_fwd,
     attn_fwd_ext_ptr,
     attn_fwd_ptr,
+    attn_fwd_varlen,
+    attn_fwd_varlen_ptr,
     attn_status_string,
     attn_version,
 )

@@ -163,6 +163,53 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out, lse
 
 
+def attn_fwd_varlen_ptr(q: int, k: int, v: int, out: int, lse: int, cu_q: int, cu_k: int, B: int,
+                        Hq: int, Hkv: int, total_q: int, total_k: int, max_seqlen_q: int, d: int,
+                        scale: float, causal: bool, dtype: int, stream: int = 0) -> int:
+    """The C entry point attn_fwd_varlen with raw integer pointers."""
+    return _lib.load().attn_fwd_varlen(q or None, k or None, v or None, out or None, lse or None,
+                                       cu_q or None, cu_k or None, int(B), int(Hq), int(Hkv),
+                                       int(total_q), int(total_k), int(max_seqlen_q), int(d),
+                                       float(scale), int(bool(causal)), int(dtype), stream or None)
+
+
+def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
+                    softmax_scale: float | None = None, causal: bool = False):
+    """Exact attention over packed variable-length sequences.
+
+    q: [total_q, Hq, d]; k, v: [total_k, Hkv, d]; cu_seqlens_*: int32 [B + 1]
+    on the device.  Returns (out [total_q, Hq, d], lse [Hq, total_q] fp32).
+    """
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D [total, H, d]")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or dk != d:
+        raise ValueError("k and v must be [total_k, Hkv, d] with q's d")
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, bf16 or fp16")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on q's HIP device")
+    B = cu_seqlens_q.numel() - 1
+    _check_like("cu_seqlens_q", cu_seqlens_q, (B + 1,), torch.int32, q.device)
+    _check_like("cu_seqlens_k", cu_seqlens_k, (B + 1,), torch.int32, q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q)
+    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        code = attn_fwd_varlen_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                                   B, Hq, Hkv, total_q, total_k, max_seqlen_q, d, softmax_scale,
+                                   causal, _DTYPE_CODE[q.dtype], stream)
+    if code != _lib.ATTN_OK:
+        raise AttnError(code)
+    return out, lse
+
+
 class _Attention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, softmax_scale, causal):

@@ -24,9 +24,10 @@ using eta_host::overlaps;
 
 constexpr const char* kVersion = "0.2.0 gfx950 exact-tiled-attention fwd+bwd";
 
-template <int D, bool BF16, bool CAUSAL, bool MODS>
+template <int D, bool BF16, bool CAUSAL, bool MODS, bool VARLEN = false>
 int launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
-           int Hkv, int Nq, int Nk, float scale, const eta::ScoreMods& mods, hipStream_t stream) {
+           int Hkv, int Nq, int Nk, float scale, const eta::ScoreMods& mods, hipStream_t stream,
+           const eta::VarlenArgs& va = eta::VarlenArgs{nullptr, nullptr, 0, 0, 0}) {
   using C = eta::TileCfg<D>;
   const int nqb = (Nq + C::BM - 1) / C::BM;
   const int64_t total64 = (int64_t)B * Hq * nqb;
@@ -37,10 +38,11 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, i
   // a window alone keeps the plain kernel's scaling.
   const bool transform = MODS && (mods.slopes || mods.cap > 0.f);
   const int prescale = (!transform && !(scale > 0.f)) ? 1 : 0;
-  hipLaunchKernelGGL((eta::attn_fwd_kernel<D, BF16, CAUSAL, MODS>), dim3(total), dim3(C::kThreads),
-                     0, stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq, Hkv, Nq,
-                     Nk, nqb, total, c_log2, prescale, mods);
+  hipLaunchKernelGGL((eta::attn_fwd_kernel<D, BF16, CAUSAL, MODS, VARLEN>), dim3(total),
+                     dim3(C::kThreads), 0, stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                     static_cast<uint16_t*>(out), lse, Hq, Hkv, Nq, Nk, nqb, total, c_log2, prescale,
+                     mods, va);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -124,7 +126,72 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   return dispatch_hdim<false>(d, bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, none, s);
 }
 
+template <int D>
+int dispatch_varlen(bool bf16, bool causal, const void* q, const void* k, const void* v, void* out,
+                    float* lse, int B, int Hq, int Hkv, int max_q, float scale,
+                    const eta::VarlenArgs& va, hipStream_t s) {
+  const eta::ScoreMods none{-1, -1, nullptr, 0.f, scale};
+  // Nq = max_q sizes the grid; the kernel reads each sequence's lengths.
+  if (bf16) {
+    return causal ? launch<D, true, true, false, true>(q, k, v, out, lse, B, Hq, Hkv, max_q, 1, scale, none, s, va)
+                  : launch<D, true, false, false, true>(q, k, v, out, lse, B, Hq, Hkv, max_q, 1, scale, none, s, va);
+  }
+  return causal ? launch<D, false, true, false, true>(q, k, v, out, lse, B, Hq, Hkv, max_q, 1, scale, none, s, va)
+                : launch<D, false, false, false, true>(q, k, v, out, lse, B, Hq, Hkv, max_q, 1, scale, none, s, va);
+}
+
 }  // namespace
+
+extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                               const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq,
+                               int Hkv, int total_q, int total_k, int max_seqlen_q, int d,
+                               float scale, int causal, int dtype, void* stream) {
+  // 1. shape
+  if (B < 0 || Hq < 1 || Hkv < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || d < 1)
+    return ATTN_ERR_BAD_SHAPE;
+  // 2. nothing to do
+  if (B == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_OK;
+  const double q_elems = (double)total_q * Hq * d, kv_elems = (double)total_k * Hkv * d;
+  if (q_elems > 0x1p60 || kv_elems > 0x1p60) return ATTN_ERR_BAD_SHAPE;
+  if ((double)128 * Hq * d * 2 >= 0x1p31 || (double)64 * Hkv * d * 2 >= 0x1p31)
+    return ATTN_ERR_BAD_SHAPE;
+  if ((double)B * Hq * ((max_seqlen_q + 127) / 128) > 0x7fffffff) return ATTN_ERR_BAD_SHAPE;
+  // 3. null pointers (k and v may be NULL only when there are no keys)
+  if (!q || !out || !lse || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL_POINTER;
+  if (total_k > 0 && (!k || !v)) return ATTN_ERR_NULL_POINTER;
+  // 4-7. GQA ratio, head dim, dtype, scale
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA_RATIO;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED_HDIM;
+  if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
+  if (!finite_bits(scale)) return ATTN_ERR_BAD_SCALE;
+  // 8. alignment
+  if (!aligned16(q) || !aligned16(out) || !aligned16(lse) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3))
+    return ATTN_ERR_MISALIGNED;
+  if (total_k > 0 && (!aligned16(k) || !aligned16(v))) return ATTN_ERR_MISALIGNED;
+  // 9. aliasing: outputs must not overlap the inputs or each other
+  const size_t qb = (size_t)q_elems * 2, kvb = (size_t)kv_elems * 2;
+  const size_t lb = (size_t)Hq * total_q * sizeof(float), cb = (size_t)(B + 1) * 4;
+  const void* in_p[5] = {q, k, v, cu_seqlens_q, cu_seqlens_k};
+  const size_t in_n[5] = {qb, kvb, kvb, cb, cb};
+  for (int i = 0; i < 5; ++i) {
+    if (!in_p[i] || !in_n[i]) continue;
+    if (overlaps(out, qb, in_p[i], in_n[i]) || overlaps(lse, lb, in_p[i], in_n[i])) return ATTN_ERR_ALIASING;
+  }
+  if (overlaps(out, qb, lse, lb)) return ATTN_ERR_ALIASING;
+  // 10. device
+  const int dev_status = check_device();
+  if (dev_status != ATTN_OK) return dev_status;
+  // 11. launch
+  const eta::VarlenArgs va{cu_seqlens_q, cu_seqlens_k, total_q, total_k, B * Hq};
+  const bool bf16 = dtype == ATTN_DTYPE_BF16, c = causal != 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (d) {
+    case 64: return dispatch_varlen<64>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, max_seqlen_q, scale, va, s);
+    case 128: return dispatch_varlen<128>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, max_seqlen_q, scale, va, s);
+    default: return dispatch_varlen<256>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, max_seqlen_q, scale, va, s);
+  }
+}
 
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                         int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,

@@ -120,12 +120,23 @@ __device__ __forceinline__ float tanh_fast(float x) {
   return 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * 2.88539008177792681472f) + 1.0f);
 }
 
-template <int D, bool BF16, bool CAUSAL, bool MODS = false>
+// Variable-length sequences packed along the row axis: sequence b owns
+// query rows [cu_q[b], cu_q[b+1]) of q/out and key rows [cu_k[b], cu_k[b+1])
+// of k/v; lse is [Hq, total_q].  Offsets are clamped to [0, total] so that
+// no access leaves the packed tensors.
+struct VarlenArgs {
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
+  int pairs;  // sequences x query heads
+};
+
+template <int D, bool BF16, bool CAUSAL, bool MODS = false, bool VARLEN = false>
 __global__ void __launch_bounds__(TileCfg<D>::kThreads, TileCfg<D>::kMinWavesPerEU)
 attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                 float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int nqb,
-                int total, float c_log2, int prescale, ScoreMods mods) {
+                int total, float c_log2, int prescale, ScoreMods mods, VarlenArgs va) {
   using C = TileCfg<D>;
   constexpr int BN = C::BN, BM = C::BM, KS = C::KS, VS = C::VS;
   constexpr int NKS = D / 16;  // k-steps of the S^T product
@@ -140,18 +151,33 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
 
-  const WorkItem w = map_workgroup<CAUSAL>(blockIdx.x, total, nqb, Hq);
+  const WorkItem w = VARLEN ? map_workgroup_packed(blockIdx.x, nqb, Hq, va.pairs)
+                           : map_workgroup<CAUSAL>(blockIdx.x, total, nqb, Hq);
   const int hkv = w.hq / (Hq / Hkv);
   const int q0 = w.qblk * BM;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + l32;
+
+  // First rows of this (b, head) in q/out and k/v, and of its lse row.
+  int64_t q_row0 = (int64_t)w.b * Nq, k_row0 = (int64_t)w.b * Nk;
+  int64_t lse_off = ((int64_t)w.b * Hq + w.hq) * Nq;
+  if constexpr (VARLEN) {
+    const int qs0 = min(max(va.cu_q[w.b], 0), va.total_q);
+    const int ks0 = min(max(va.cu_k[w.b], 0), va.total_k);
+    Nq = min(max(va.cu_q[w.b + 1], qs0), va.total_q) - qs0;
+    Nk = min(max(va.cu_k[w.b + 1], ks0), va.total_k) - ks0;
+    q_row0 = qs0;
+    k_row0 = ks0;
+    lse_off = (int64_t)w.hq * va.total_q + qs0;
+    if (q0 >= Nq) return;  // the whole workgroup, before any barrier
+  }
   const int diag = Nk - Nq;  // causal: key j visible to row i iff j <= i + diag
 
   const int64_t q_rs = (int64_t)Hq * D, kv_rs = (int64_t)Hkv * D;
   // Row qw0 of (b, hq) in q / out; row 0 of (b, hkv) in k / v.
-  const int64_t qo_off = ((int64_t)w.b * Nq + qw0) * q_rs + (int64_t)w.hq * D;
-  const uint16_t* Kh = K + ((int64_t)w.b * Nk * Hkv + hkv) * D;
-  const uint16_t* Vh = V + ((int64_t)w.b * Nk * Hkv + hkv) * D;
+  const int64_t qo_off = (q_row0 + qw0) * q_rs + (int64_t)w.hq * D;
+  const uint16_t* Kh = K + (k_row0 * Hkv + hkv) * D;
+  const uint16_t* Vh = V + (k_row0 * Hkv + hkv) * D;
 
   // ---- Q (B operand of S^T = K Q^T): fragments resident in VGPRs for the
   // whole loop, or (d = 256) the workgroup's Q tile in LDS.  Rows past Nq
@@ -164,7 +190,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = buf_load16(qr, voff + 32 * ks);
   } else {
-    const int64_t q0_off = ((int64_t)w.b * Nq + q0) * q_rs + (int64_t)w.hq * D;
+    const int64_t q0_off = (q_row0 + q0) * q_rs + (int64_t)w.hq * D;
     const rsrc_t qr = make_rsrc(Q + q0_off, span_bytes(q0, BM, Nq, q_rs, D));
 #pragma unroll
     for (int i = 0; i < C::kQInstPerWave; ++i) {
@@ -483,7 +509,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   }
   const int nrows = max(0, min(32, Nq - qw0));
-  const rsrc_t lr = make_rsrc(LSE + ((int64_t)w.b * Hq + w.hq) * Nq + qw0, nrows * 4);
+  const rsrc_t lr = make_rsrc(LSE + lse_off + qw0, nrows * 4);
   buf_store4(lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY, lr, 4 * l32);
 }
 

@@ -140,4 +140,20 @@ __device__ __forceinline__ WorkItem map_workgroup(int wg, int total, int nqb, in
   return w;
 }
 
+// blockIdx -> (sequence, head, query block) for packed variable-length
+// batches, where the grid is sized by the longest sequence.  Query blocks go
+// in descending order, each block index across all (sequence, head) pairs
+// before the next: only long sequences own high block indices, so the
+// heaviest work items start first (a non-causal block of a longer sequence
+// also sees more keys), and every XCD draws the same mix of sequences.  Pair
+// p stays on XCD p mod 8 when the pair count is a multiple of 8.
+__device__ __forceinline__ WorkItem map_workgroup_packed(int wg, int nqb, int Hq, int pairs) {
+  WorkItem w;
+  w.qblk = nqb - 1 - wg / pairs;
+  const int bh = wg % pairs;
+  w.hq = bh % Hq;
+  w.b = bh / Hq;
+  return w;
+}
+
 }  // namespace eta

@@ -115,6 +115,26 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* 
                  int dtype, void* stream);
 
 /*
+ * attn_fwd over variable-length sequences packed along the row axis (the
+ * unpadded layout the hysenlabs.com page's version history refers to,
+ * section "Von 2.0 bis 2.7"): sequence b owns query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]); each sequence is attended on its
+ * own exactly as attn_fwd does for one batch entry (causal: bottom-right
+ * aligned per sequence; a sequence without keys gets out = 0, lse = -inf).
+ *   q, out  [total_q, Hq, d]   k, v [total_k, Hkv, d]   lse [Hq, total_q] fp32
+ *   cu_seqlens_q, cu_seqlens_k  [B + 1] int32, device, nondecreasing from 0
+ *           to total_q / total_k (values outside [0, total] are clamped)
+ *   max_seqlen_q  at least the longest query sequence (sizes the grid)
+ * k and v may be NULL when total_k == 0.  Validation as attn_fwd; B == 0,
+ * total_q == 0 or max_seqlen_q == 0 is a no-op.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                    int total_q, int total_k, int max_seqlen_q, int d, float scale, int causal,
+                    int dtype, void* stream);
+
+/*
  * Exact attention backward: gradients of L = sum(dout * out) with respect to
  * q, k and v, for out = attn_fwd(q, k, v, scale, causal).  The pages state
  * that the library's backward pass computes these gradients, that it is

@@ -16,6 +16,7 @@ written out, per (batch, query head).
 from .exact import (  # noqa: F401
     attention,
     attention_backward,
+    attention_varlen,
     attention_rows,
     kv_head_of,
     allowed_keys,

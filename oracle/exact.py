@@ -64,6 +64,7 @@ __all__ = [
     "attention",
     "attention_rows",
     "attention_backward",
+    "attention_varlen",
     "kv_head_of",
     "allowed_keys",
     "visible_range",
@@ -303,3 +304,30 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool = False):
             dk[b, :, g, :] += sigma * (dS.T @ qh)
             delta[b, h, :] = D
     return dq, dk, dv, delta
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool = False):
+    """Exact attention over packed variable-length sequences: sequence b is
+    query rows [cu_q[b], cu_q[b+1]) of q [total_q, Hq, d] attending to key
+    rows [cu_k[b], cu_k[b+1]) of k, v [total_k, Hkv, d], each on its own with
+    ``attention`` (the unpadded layout of the hysenlabs.com page's version
+    history, section "Von 2.0 bis 2.7").
+
+    Returns (O [total_q, Hq, d], lse [Hq, total_q]) in fp64.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    cq = [int(x) for x in np.asarray(cu_seqlens_q).reshape(-1)]
+    ck = [int(x) for x in np.asarray(cu_seqlens_k).reshape(-1)]
+    total_q, Hq, d = q.shape
+    O = np.zeros((total_q, Hq, d))
+    lse = np.full((Hq, total_q), -np.inf)
+    for b in range(len(cq) - 1):
+        qs, qe, ks, ke = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if qe <= qs:
+            continue
+        if ke <= ks:  # no keys: rows stay 0 / -inf
+            continue
+        Ob, Lb = attention(q[None, qs:qe], k[None, ks:ke], v[None, ks:ke], scale, causal)
+        O[qs:qe] = Ob[0]
+        lse[:, qs:qe] = Lb[0]
+    return O, lse

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
     assert names == ["attn_bwd", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_size",
-                     "attn_fwd", "attn_fwd_ext", "attn_status_string", "attn_version"]
+                     "attn_fwd", "attn_fwd_ext", "attn_fwd_varlen", "attn_status_string", "attn_version"]
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -359,3 +359,87 @@ def test_ext_order_misaligned_and_aliasing():
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a HIP device is visible here")
 def test_ext_no_device_reported_without_gpu():
     assert call_ext(left=4, right=0, slopes=SLOPES, cap=30.0) == _lib.ATTN_ERR_NO_DEVICE
+
+
+# ---------------------------------------------------------------------------
+# attn_fwd_varlen (packed variable-length sequences)
+# ---------------------------------------------------------------------------
+from exact_tiled_attention_35_amd.attention import attn_fwd_varlen_ptr  # noqa: E402
+
+CUQ, CUK = 0x800000000, 0x900000000
+GOOD_VL = dict(q=Q, k=K, v=V, out=OUT, lse=LSE, cu_q=CUQ, cu_k=CUK, B=3, Hq=8, Hkv=2, total_q=300,
+               total_k=500, max_q=200, d=128, scale=0.088, causal=True, dtype=_lib.ATTN_DTYPE_BF16)
+
+
+def call_vl(**over):
+    a = dict(GOOD_VL)
+    a.update(over)
+    return attn_fwd_varlen_ptr(a["q"], a["k"], a["v"], a["out"], a["lse"], a["cu_q"], a["cu_k"],
+                               a["B"], a["Hq"], a["Hkv"], a["total_q"], a["total_k"], a["max_q"],
+                               a["d"], a["scale"], a["causal"], a["dtype"])
+
+
+@pytest.mark.parametrize("field,value", [("B", -1), ("Hq", 0), ("Hkv", 0), ("total_q", -1),
+                                         ("total_k", -1), ("max_q", -1), ("d", 0)])
+def test_varlen_bad_shape(field, value):
+    assert call_vl(**{field: value}) == _lib.ATTN_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("field", ["B", "total_q", "max_q"])
+def test_varlen_empty_is_a_noop_with_null_pointers(field):
+    assert call_vl(**{field: 0}, q=0, k=0, v=0, out=0, lse=0, cu_q=0, cu_k=0) == _lib.ATTN_OK
+
+
+def test_varlen_too_large_is_bad_shape():
+    assert call_vl(total_q=2**31 - 1, Hq=2**20, Hkv=2**20, d=64) == _lib.ATTN_ERR_BAD_SHAPE
+    assert call_vl(Hq=2**24, Hkv=2**24) == _lib.ATTN_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("field", ["q", "out", "lse", "cu_q", "cu_k", "k", "v"])
+def test_varlen_null_pointer(field):
+    assert call_vl(**{field: 0}) == _lib.ATTN_ERR_NULL_POINTER
+
+
+def test_varlen_keys_may_be_null_without_keys():
+    # With no key rows, k and v are never read: validation passes to the
+    # device check.
+    st = call_vl(total_k=0, k=0, v=0)
+    assert st in (_lib.ATTN_ERR_NO_DEVICE, _lib.ATTN_OK)
+
+
+def test_varlen_checks_in_order():
+    assert call_vl(Hkv=3) == _lib.ATTN_ERR_GQA_RATIO
+    assert call_vl(d=96) == _lib.ATTN_ERR_UNSUPPORTED_HDIM
+    assert call_vl(dtype=7) == _lib.ATTN_ERR_UNSUPPORTED_DTYPE
+    assert call_vl(scale=float("inf")) == _lib.ATTN_ERR_BAD_SCALE
+    assert call_vl(Hkv=3, d=96) == _lib.ATTN_ERR_GQA_RATIO
+    assert call_vl(q=Q + 8) == _lib.ATTN_ERR_MISALIGNED
+    assert call_vl(cu_q=CUQ + 2) == _lib.ATTN_ERR_MISALIGNED
+    assert call_vl(cu_k=CUK + 1) == _lib.ATTN_ERR_MISALIGNED
+    assert call_vl(lse=LSE + 4) == _lib.ATTN_ERR_MISALIGNED
+
+
+def test_varlen_aliasing():
+    assert call_vl(out=Q + 256) == _lib.ATTN_ERR_ALIASING
+    assert call_vl(lse=CUQ - 64) == _lib.ATTN_ERR_ALIASING
+    assert call_vl(cu_k=OUT + 16) == _lib.ATTN_ERR_ALIASING
+    assert call_vl(lse=OUT + 1024) == _lib.ATTN_ERR_ALIASING
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a HIP device is visible here")
+def test_varlen_no_device_reported_without_gpu():
+    assert call_vl() == _lib.ATTN_ERR_NO_DEVICE
+
+
+def test_python_varlen_binding_rejects_bad_tensors():
+    from exact_tiled_attention_35_amd import attn_fwd_varlen
+    q = torch.zeros(10, 4, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 10], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        attn_fwd_varlen(q[0], q, q, cu, cu, 10)
+    with pytest.raises(ValueError):
+        attn_fwd_varlen(q, q[:, :, :32], q[:, :, :32], cu, cu, 10)
+    with pytest.raises(ValueError):
+        attn_fwd_varlen(q, q.half(), q.half(), cu, cu, 10)
+    with pytest.raises(ValueError):  # CPU tensors
+        attn_fwd_varlen(q, q, q, cu, cu, 10)

@@ -1,0 +1,89 @@
+"""Pins of the oracle's packed variable-length attention (CPU only).
+
+Each sequence of the packed batch is checked against the pure-Python brute
+force run on that sequence alone, and an equal-length packing against the
+batched oracle; planted mistakes in the packing (key offsets taken from the
+query prefix sums, sequences shifted by one row) must fail the pin."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from attn_workloads import make_varlen
+from _bruteforce import brute_attention
+
+# (lens_q, lens_k, Hq, Hkv, d, causal): empty query sequences, a sequence
+# without keys, single rows, Nq != Nk per sequence (bottom-right causal).
+CASES = [
+    ([3, 0, 5, 1], [3, 2, 5, 4], 2, 1, 4, False),
+    ([3, 0, 5, 1], [3, 2, 5, 4], 2, 1, 4, True),
+    ([4, 2, 6], [2, 0, 7], 4, 2, 3, True),
+    ([1, 1, 1], [5, 1, 3], 2, 2, 5, False),
+]
+
+
+def as_lists(x):
+    return x.double().tolist()
+
+
+def brute_varlen(q, k, v, cu_q, cu_k, scale, causal):
+    total_q, Hq, d = q.shape
+    O = np.zeros((total_q, Hq, d))
+    L = np.full((Hq, total_q), -np.inf)
+    for b in range(len(cu_q) - 1):
+        qs, qe, ks, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if qe == qs or ke == ks:
+            continue
+        Ob, Lb = brute_attention([as_lists(q[qs:qe])], [as_lists(k[ks:ke])], [as_lists(v[ks:ke])],
+                                 scale, causal)
+        O[qs:qe] = np.array(Ob[0])
+        L[:, qs:qe] = np.array(Lb[0])
+    return O, L
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_varlen_matches_bruteforce_per_sequence(case):
+    lens_q, lens_k, Hq, Hkv, d, causal = case
+    q, k, v, cu_q, cu_k = make_varlen(lens_q, lens_k, Hq, Hkv, d, "bf16", 1.0, seed=11)
+    scale = float(np.float32(1 / math.sqrt(d)))  # the fp32 value the library receives
+    O, L = oracle.attention_varlen(q, k, v, cu_q, cu_k, scale, causal)
+    Ob, Lb = brute_varlen(q, k, v, cu_q, cu_k, scale, causal)
+    np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+    fin = np.isfinite(Lb)
+    assert (np.isfinite(L) == fin).all()
+    np.testing.assert_allclose(L[fin], Lb[fin], rtol=0, atol=1e-12)
+
+
+def test_sequence_without_keys_gives_zero_rows():
+    q, k, v, cu_q, cu_k = make_varlen([2, 3], [4, 0], 2, 2, 4, seed=3)
+    O, L = oracle.attention_varlen(q, k, v, cu_q, cu_k, 0.5, False)
+    assert (O[2:] == 0).all() and np.isneginf(L[:, 2:]).all()
+    assert np.isfinite(L[:, :2]).all()
+
+
+def test_equal_lengths_match_the_batched_oracle():
+    B, N, Hq, Hkv, d = 3, 5, 4, 2, 8
+    q, k, v, cu_q, cu_k = make_varlen([N] * B, [N] * B, Hq, Hkv, d, seed=5)
+    for causal in (False, True):
+        O, L = oracle.attention_varlen(q, k, v, cu_q, cu_k, 0.3, causal)
+        Ob, Lb = oracle.attention(q.reshape(B, N, Hq, d), k.reshape(B, N, Hkv, d),
+                                  v.reshape(B, N, Hkv, d), 0.3, causal)
+        np.testing.assert_allclose(O, Ob.reshape(B * N, Hq, d), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(L, Lb.transpose(1, 0, 2).reshape(Hq, B * N), rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("mistake", ["keys_at_query_offsets", "shifted_by_one"])
+def test_planted_packing_mistakes_fail_the_pin(mistake):
+    lens_q, lens_k, Hq, Hkv, d, causal = CASES[2]
+    q, k, v, cu_q, cu_k = make_varlen(lens_q, lens_k, Hq, Hkv, d, "bf16", 1.0, seed=11)
+    scale = float(np.float32(1 / math.sqrt(d)))  # the fp32 value the library receives
+    Ob, _ = brute_varlen(q, k, v, cu_q, cu_k, scale, causal)
+    if mistake == "keys_at_query_offsets":
+        bad_q, bad_k = cu_q, cu_q.clamp(max=int(cu_k[-1]))
+    else:
+        bad_q, bad_k = cu_q, (cu_k + 1).clamp(max=int(cu_k[-1]))
+        bad_k[0] = 0
+    O, _ = oracle.attention_varlen(q, k, v, bad_q, bad_k, scale, causal)
+    assert np.abs(O - Ob).max() > 1e-3
