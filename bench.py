@@ -306,6 +306,8 @@ def main():
                     help="fwd only: sliding window (attn_fwd_ext); flops count the kept pairs")
     ap.add_argument("--softcap", type=float, default=0.0, help="fwd only: softcap (attn_fwd_ext)")
     ap.add_argument("--alibi", action="store_true", help="fwd only: ALiBi slopes (attn_fwd_ext)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="decode only: number of key splits (0: the library's heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain elementwise copy kernel that "
@@ -483,7 +485,7 @@ def bench_decode(args, w, dev):
     sl = torch.full((w.B,), w.Nk - 1, dtype=torch.int32, device=dev)
     out = torch.empty_like(gq)
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
-    splits = attn_decode_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+    splits = args.splits or attn_decode_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
     ws_bytes = attn_decode_workspace_size(w.B, w.Hq, w.Nq, w.d, splits)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     args_c = [t.data_ptr() for t in (gq, gkc, gvc, sl, gkn, gvn, out, lse, ws)]

@@ -316,31 +316,57 @@ attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 }
 
 // One wave per query row: lse = log sum_s exp(lse_s), O = sum_s w_s O_s with
-// w_s = exp(lse_s - lse); rows no split saw get O = 0 and lse = -inf.
+// w_s = exp(lse_s - lse); rows no split saw get O = 0 and lse = -inf.  Lane
+// l holds the logsumexp of splits l and 64 + l, so the maximum and the
+// weights take two loads and a few lane exchanges.  The partial outputs are
+// read 16 bytes per lane: a wave covers 64 / (D / 4) splits per load, the
+// loads of all splits are independent, and the lane groups that summed
+// different splits are added at the end.
 template <int D, bool BF16>
 __global__ void __launch_bounds__(256)
 attn_decode_merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpart,
                          uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Nq,
                          int splits) {
-  constexpr int PER = D / 64;  // elements per lane
+  constexpr int CPR = D / 4;        // 16-byte chunks per row
+  constexpr int SPL = 64 / CPR;     // splits per load instruction
   const int64_t nrow = (int64_t)B * Hq * Nq;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= nrow) return;
-  float mx = -INFINITY;
-  for (int s = 0; s < splits; ++s) mx = __builtin_fmaxf(mx, Lpart[(int64_t)s * nrow + row]);
-  float acc[PER];
+  if (row >= nrow) return;  // the whole wave
+  // splits <= 128: lane l covers splits l and 64 + l
+  const float ls0 = lane < splits ? Lpart[(int64_t)lane * nrow + row] : -INFINITY;
+  const float ls1 = 64 + lane < splits ? Lpart[(int64_t)(64 + lane) * nrow + row] : -INFINITY;
+  float mx = __builtin_fmaxf(ls0, ls1);
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int x = 32; x >= 1; x >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, x));
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
+  const int sub = lane / CPR, c = lane % CPR;
   if (mx != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const float ls = Lpart[(int64_t)s * nrow + row];
-      const float wgt = ls == -INFINITY ? 0.f : exp2_fast((ls - mx) * 1.44269504088896340736f);
-      den += wgt;
-      const float* op = Opart + ((int64_t)s * nrow + row) * D + lane * PER;
+    const float w0 = ls0 == -INFINITY ? 0.f : exp2_fast((ls0 - mx) * 1.44269504088896340736f);
+    const float w1 = ls1 == -INFINITY ? 0.f : exp2_fast((ls1 - mx) * 1.44269504088896340736f);
+    den = w0 + w1;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = __builtin_fmaf(wgt, op[e], acc[e]);
+    for (int x = 32; x >= 1; x >>= 1) den += __shfl_xor(den, x);
+    const f32x4_t* op = reinterpret_cast<const f32x4_t*>(Opart + row * D) + c;
+    const int64_t split_stride = nrow * CPR;  // in 16-byte chunks
+#pragma unroll 16
+    for (int s0 = 0; s0 < splits; s0 += SPL) {
+      const int sp = s0 + sub;  // this lane's split
+      const float wa = __shfl(w0, sp & 63), wb = __shfl(w1, sp & 63);
+      const float wgt = sp < 64 ? wa : wb;
+      if (sp < splits) {
+        const f32x4_t v = op[sp * split_stride];
+        acc[0] = __builtin_fmaf(wgt, v[0], acc[0]);
+        acc[1] = __builtin_fmaf(wgt, v[1], acc[1]);
+        acc[2] = __builtin_fmaf(wgt, v[2], acc[2]);
+        acc[3] = __builtin_fmaf(wgt, v[3], acc[3]);
+      }
+    }
+#pragma unroll
+    for (int x = CPR; x < 64; x <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], x);
     }
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
@@ -349,17 +375,11 @@ attn_decode_merge_kernel(const float* __restrict__ Opart, const float* __restric
   const int64_t bh = row / Nq;
   const int h = (int)(bh % Hq);
   const int64_t b = bh / Hq;
-  uint16_t* out = O + ((b * Nq + i) * Hq + h) * D + lane * PER;
+  if (sub == 0) {
+    f32x4_t o4;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    float o = acc[e] * inv;
-    uint16_t bits;
-    if constexpr (BF16) {
-      bits = __builtin_bit_cast(uint16_t, (__bf16)o);
-    } else {
-      bits = __builtin_bit_cast(uint16_t, (_Float16)o);
-    }
-    out[e] = bits;
+    for (int e = 0; e < 4; ++e) o4[e] = acc[e] * inv;
+    *reinterpret_cast<u32x2_t*>(O + ((b * Nq + i) * Hq + h) * D + 4 * c) = pack4<BF16>(o4);
   }
   if (lane == 0) LSE[row] = den > 0.f ? mx + __builtin_amdgcn_logf(den) * kLn2 : -INFINITY;
 }
