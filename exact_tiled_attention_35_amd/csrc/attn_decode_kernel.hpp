@@ -318,10 +318,11 @@ attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 // One wave per query row: lse = log sum_s exp(lse_s), O = sum_s w_s O_s with
 // w_s = exp(lse_s - lse); rows no split saw get O = 0 and lse = -inf.  Lane
 // l holds the logsumexp of splits l and 64 + l, so the maximum and the
-// weights take two loads and a few lane exchanges.  The partial outputs are
-// read 16 bytes per lane: a wave covers 64 / (D / 4) splits per load, the
-// loads of all splits are independent, and the lane groups that summed
-// different splits are added at the end.
+// sum of the weights take two loads and a few lane exchanges.  The partial
+// outputs are read 16 bytes per lane: a wave covers 64 / (D / 4) splits per
+// load, each lane recomputes its split's weight, the loads of all splits are
+// independent, and the lane groups that summed different splits are added at
+// the end.
 template <int D, bool BF16>
 __global__ void __launch_bounds__(256)
 attn_decode_merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpart,
@@ -350,17 +351,24 @@ attn_decode_merge_kernel(const float* __restrict__ Opart, const float* __restric
     for (int x = 32; x >= 1; x >>= 1) den += __shfl_xor(den, x);
     const f32x4_t* op = reinterpret_cast<const f32x4_t*>(Opart + row * D) + c;
     const int64_t split_stride = nrow * CPR;  // in 16-byte chunks
-#pragma unroll 16
-    for (int s0 = 0; s0 < splits; s0 += SPL) {
-      const int sp = s0 + sub;  // this lane's split
-      const float wa = __shfl(w0, sp & 63), wb = __shfl(w1, sp & 63);
-      const float wgt = sp < 64 ? wa : wb;
-      if (sp < splits) {
-        const f32x4_t v = op[sp * split_stride];
-        acc[0] = __builtin_fmaf(wgt, v[0], acc[0]);
-        acc[1] = __builtin_fmaf(wgt, v[1], acc[1]);
-        acc[2] = __builtin_fmaf(wgt, v[2], acc[2]);
-        acc[3] = __builtin_fmaf(wgt, v[3], acc[3]);
+    // CH splits per lane at a time: all their loads first, then the sums.
+    constexpr int CH = 16;
+    for (int s0 = 0; s0 < splits; s0 += SPL * CH) {
+      float lsv[CH];
+      f32x4_t vv[CH];
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        // this lane's split; past the last one, reread it with weight 0
+        const int sp = min(s0 + SPL * u + sub, splits - 1);
+        lsv[u] = Lpart[(int64_t)sp * nrow + row];
+        vv[u] = op[sp * split_stride];
+      }
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const bool live = s0 + SPL * u + sub < splits && lsv[u] != -INFINITY;
+        const float wgt = live ? exp2_fast((lsv[u] - mx) * 1.44269504088896340736f) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wgt, vv[u][e], acc[e]);
       }
     }
 #pragma unroll
