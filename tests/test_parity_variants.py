@@ -148,3 +148,44 @@ def test_inactive_variants_are_attn_fwd_and_no_op_variants_agree():
     # a window wider than the sequence takes the variant kernel and changes nothing
     o2, l2 = attn_fwd(q, k, v, None, True, window=(1000, 1000))
     assert (o2.double() - ref.double()).abs().max() <= 8e-3 and (l2 - rl).abs().max() <= 1e-5
+
+
+# The variant configurations the bench times, at full size: sampled rows of
+# several heads against the oracle (rows near the window edges included).
+FULL = [  # (workload, window, alibi, softcap)
+    ("causal_gqa_b1_hq64_hkv8_n16384_d128_bf16", (4095, 0), False, 0.0),
+    ("causal_mha_b2_h32_n8192_d128_bf16", (1023, 0), False, 0.0),
+    ("mha_b4_h16_n4096_d128_bf16", (-1, -1), False, 30.0),
+    ("mha_b4_h16_n4096_d128_bf16", (-1, -1), True, 0.0),
+]
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=lambda c: f"{c[0]}-w{c[1][0]}_{c[1][1]}-a{int(c[2])}-c{c[3]:g}")
+def test_variant_workloads_full_size(cfg):
+    from attn_workloads import WORKLOADS, make_workload
+    from exact_tiled_attention_35_amd import attn_fwd
+
+    name, window, alibi, cap = cfg
+    w = WORKLOADS[name]
+    print(f"[parity-variants] full size {cfg}", flush=True)
+    q, k, v = make_workload(w)
+    sl = slopes_for(w.Hq) if alibi else None
+    out, lse = attn_fwd(q.cuda(), k.cuda(), v.cuda(), w.scale, w.causal, window=window,
+                        alibi_slopes=sl.cuda() if sl is not None else None, softcap=cap)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(w.seed)
+    heads = sorted({(0, 0), (w.B - 1, w.Hq - 1), (0, w.Hq // 2)})
+    L = window[0]
+    for b, h in heads:
+        fixed = {0, 1, 63, 64, 127, 128, w.Nq // 2, w.Nq - 1}
+        if L >= 0:
+            fixed |= {L - 1, L, L + 1, L + 64, min(w.Nq - 1, 2 * L + 5)}
+        rows = sorted(r for r in fixed | {int(x) for x in rng.integers(0, w.Nq, 16)} if 0 <= r < w.Nq)
+        O, Lr = oracle.attention_rows(q, k, v, w.scale, w.causal, b, h, rows, window=window,
+                                      alibi_slopes=sl.numpy() if sl is not None else None,
+                                      softcap=cap)
+        err = np.abs(out[b, rows, h].double().numpy() - O)
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (b, h, err.max(), err.mean())
+        assert np.abs(lse[b, h, rows].double().numpy() - Lr).max() <= LSE_ABS, (b, h)
