@@ -18,8 +18,8 @@
 //    r % Nq)), so each KV head's cache is streamed once per split for the
 //    whole group.  The keys of (b, KV head) are cut into `splits` ranges of
 //    whole tiles, one per workgroup, so that short query blocks still fill
-//    the GPU; K/V tiles stream through a 4-stage LDS ring (three tiles in
-//    flight) because the loop is bound by HBM, not by the matrix cores.  The
+//    the GPU; K/V tiles stream through two LDS stages (the loop is bound by
+//    HBM, not by the matrix cores).  The
 //    products, the online softmax and the masking are the forward kernel's
 //    (S^T = K Q^T and O^T = V^T P^T on 32x32x16 MFMAs, one query row per
 //    lane, exp2 with the running maximum).  With one split the result goes
@@ -40,7 +40,7 @@ template <int D>
 struct DecCfg {
   static constexpr int kWaves = 4, kThreads = 256, BM = 128;
   static constexpr int BN = 32;       // keys per tile
-  static constexpr int kStages = 4;   // LDS ring: three tiles in flight
+  static constexpr int kStages = 2;   // the next tile streams in while this one is computed
   static constexpr int kChunks = D / 8;
   static constexpr int KCP = kChunks + 1, VCP = kChunks + 4;
   static constexpr int KS = 8 * KCP, VS = 8 * VCP;
@@ -89,7 +89,7 @@ attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    float* __restrict__ Lpart, int B, int Hq, int Hkv, int Nq, int Ncap, int Nnew,
                    int nrb, int splits, float c_log2, int prescale) {
   using C = DecCfg<D>;
-  constexpr int BN = C::BN, BM = C::BM, KS = C::KS, VS = C::VS, NS = C::kStages;
+  constexpr int BN = C::BN, BM = C::BM, KS = C::KS, VS = C::VS;
   constexpr int NKS = D / 16, NKB = BN / 32, NDB = D / 32, NKK = BN / 16;
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::kLdsElems];
@@ -179,33 +179,20 @@ attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   float m = -INFINITY, lsum = 0.f;
   const float ce = prescale ? 1.0f : c_log2;
 
-  // Every wave issues at least kMinLoads load instructions per tile, so
-  // "at most kMinLoads * (NS - 2) loads outstanding" implies that tile t,
-  // issued before the NS - 2 newer ones, has landed (loads complete in
-  // order).  s_waitcnt operand: vmcnt in bits 3:0 and 15:14, expcnt and
-  // lgkmcnt left at their maxima.
-  constexpr int kMinLoads = C::kKInst / 4 + C::kVInst / 4;
-  constexpr int kVm = kMinLoads * (NS - 2);
-  static_assert(kVm < 64, "vmcnt range");
-  constexpr int kWaitNewerTiles = (kVm & 0xf) | (0x7 << 4) | (0xf << 8) | ((kVm >> 4) << 14);
-
-  // Prologue: NS - 1 tiles in flight.
-#pragma unroll
-  for (int t = 0; t < NS - 1; ++t)
-    if (t < nt) issue_tile(t, smem + t * C::kStage);
+  // Two LDS stages.  The V reads of a tile wait for every load this wave
+  // has in flight (the compiler cannot tell the stages apart), so deeper
+  // rings keep no more loads in flight; a four-stage ring with waits on
+  // the older tiles only was measured slower on this HBM stream.
+  if (nt > 0) issue_tile(0, smem);
 
   for (int t = 0; t < nt; ++t) {
-    // Tile t has landed once at most NS - 2 newer tiles are outstanding;
-    // every wave waits for its own loads, then the barrier publishes them
-    // and ends all reads of the slot the next load reuses.
-    if (t + NS - 2 < nt) {
-      __builtin_amdgcn_s_waitcnt(kWaitNewerTiles);
-    } else {
-      __builtin_amdgcn_s_waitcnt(0);
-    }
+    // Tile t has landed: every wave waits for its own loads, then the
+    // barrier publishes them and ends all reads of the stage the next tile
+    // reuses (read in iteration t - 1).
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + NS - 1 < nt) issue_tile(t + NS - 1, smem + ((t + NS - 1) % NS) * C::kStage);
-    const uint16_t* st = smem + (t % NS) * C::kStage;
+    if (t + 1 < nt) issue_tile(t + 1, smem + ((t + 1) & 1) * C::kStage);
+    const uint16_t* st = smem + (t & 1) * C::kStage;
     const int j0 = (t0 + t) * BN;
 
     if (wave_live) {
