@@ -37,13 +37,23 @@ METRIC = "attention fwd TFLOP/s (bf16, d=128) and % of MI355X bf16 MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # MI355X dense MFMA, published
 METRIC_BWD = ("attention bwd TFLOP/s (10*B*Hq*Nq*Nk*d per call, halved for causal) and % of "
               "MI355X bf16 MFMA peak")
-# Sources of the forward kernel and its launch code (the committed HBM
-# traffic figures are valid only for these).
-KERNEL_SOURCES = [
-    os.path.join(ROOT, "exact_tiled_attention_35_amd", "csrc", n)
-    for n in ("gfx950_ops.hpp", "attn_fwd_kernel.hpp", "attn_api.hip", "attn_host.hpp")
-]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
+# Sources of each operation's kernels and launch code (the committed HBM
+# traffic figures are valid only for these), the file that holds those
+# figures, and the kernels one call launches.
+_CSRC = os.path.join(ROOT, "exact_tiled_attention_35_amd", "csrc")
+OP_SOURCES = {
+    "fwd": ("gfx950_ops.hpp", "attn_fwd_kernel.hpp", "attn_api.hip", "attn_host.hpp"),
+    "bwd": ("gfx950_ops.hpp", "attn_bwd_kernel.hpp", "attn_bwd_api.hip", "attn_host.hpp"),
+    "decode": ("gfx950_ops.hpp", "attn_decode_kernel.hpp", "attn_decode_api.hip", "attn_host.hpp"),
+}
+KERNEL_SOURCES = [os.path.join(_CSRC, n) for n in OP_SOURCES["fwd"]]
+TRAFFIC_FILES = {op: os.path.join(ROOT, "profiles", f"attn_{op}_traffic.json") for op in OP_SOURCES}
+TRAFFIC_FILE = TRAFFIC_FILES["fwd"]
+OP_KERNELS = {
+    "fwd": ("attn_fwd_kernel",),
+    "bwd": ("attn_bwd_dq_kernel", "attn_bwd_dkdv_kernel"),
+    "decode": ("kv_append_kernel", "attn_decode_kernel", "attn_decode_merge_kernel"),
+}
 
 
 def log(*a):
@@ -105,24 +115,24 @@ def algorithmic_bytes(w) -> int:
             + w.B * w.Hq * w.Nq * 4)                  # lse written
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(op: str = "fwd") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
+    for n in OP_SOURCES[op]:
+        with open(os.path.join(_CSRC, n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_name: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+def measured_traffic(workload_name: str, op: str = "fwd"):
+    """HBM bytes per call from the committed rocprofv3 counter runs, or None
     if they were taken on another version of the kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[op]) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     rec = t.get("workloads", {}).get(workload_name)
-    if not rec or t.get("kernel_source_hash") != kernel_source_hash():
+    if not rec or t.get("kernel_source_hash") != kernel_source_hash(op):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -255,38 +265,49 @@ def _pmc_rows(path: str, counter: str):
     return rows
 
 
-def write_traffic_summary(fetch_csv: str, write_csv: str, copy_mib, workload=None):
-    """Per-launch HBM bytes of the attention kernel from FETCH_SIZE / WRITE_SIZE
-    (KiB per dispatch), each scaled by the factor that maps the same counter
-    onto a plain copy of known size."""
-    from attn_workloads import HEADLINE, WORKLOADS
+def write_traffic_summary(fetch_csv: str, write_csv: str, copy_mib, workload=None, op="fwd"):
+    """Per-call HBM bytes of an operation from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch; a call's kernels are summed), each scaled by the factor that
+    maps the same counter onto a plain copy of known size."""
+    from attn_workloads import DECODE_WORKLOADS, HEADLINE, WORKLOADS
 
     copy_bytes = int(copy_mib) * 2**20
-    name = workload or HEADLINE
-    w = WORKLOADS[name]
-    out = {"kernel_source_hash": kernel_source_hash(), "workloads": {}}
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    if op == "decode":
+        name = workload or next(iter(DECODE_WORKLOADS))
+        w = DECODE_WORKLOADS[name]
+        algo = decode_bytes(w)
+    else:
+        name = workload or HEADLINE
+        w = WORKLOADS[name]
+        algo = algorithmic_bytes(w) if op == "fwd" else bwd_algorithmic_bytes(w)
+    path = TRAFFIC_FILES[op]
+    out = {"kernel_source_hash": kernel_source_hash(op), "workloads": {}}
+    if os.path.exists(path):
+        with open(path) as f:
             old = json.load(f)
         if old.get("kernel_source_hash") == out["kernel_source_hash"]:
             out = old
-    rec = {}
+    rec = {"kernels": list(OP_KERNELS[op])} if op != "fwd" else {}
     for csv_path, counter, key in ((fetch_csv, "FETCH_SIZE", "read"), (write_csv, "WRITE_SIZE", "written")):
         rows = _pmc_rows(csv_path, counter)
-        attn = [v for (k, v) in rows if "attn_fwd_kernel" in k]
         copy = [v for (k, v) in rows if "neg_kernel" in k]
-        if not attn or not copy:
-            raise SystemExit(f"{csv_path}: need both attention and copy dispatches for {counter}")
-        copy_kib = max(copy)
-        factor = copy_bytes / (copy_kib * 1024.0)
-        kib = sum(attn) / len(attn)
+        per_kernel = []
+        for kern in OP_KERNELS[op]:
+            vals = [v for (k, v) in rows if kern + "<" in k]
+            if not vals:
+                raise SystemExit(f"{csv_path}: no {kern} dispatches for {counter}")
+            per_kernel.append(sum(vals) / len(vals))
+        if not copy:
+            raise SystemExit(f"{csv_path}: no copy dispatch for {counter}")
+        factor = copy_bytes / (max(copy) * 1024.0)
+        kib = sum(per_kernel)
         rec[f"{counter}_KiB_per_launch"] = kib
         rec[f"{counter}_copy_scale"] = factor
         rec[f"bytes_{key}_per_launch"] = kib * 1024.0 * factor
     rec["hbm_bytes_per_launch"] = rec["bytes_read_per_launch"] + rec["bytes_written_per_launch"]
-    rec["algorithmic_bytes"] = algorithmic_bytes(w)
+    rec["algorithmic_bytes"] = algo
     out["workloads"][name] = rec
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(path, "w") as f:
         json.dump(out, f, indent=2)
     print(json.dumps(rec, indent=2))
 
@@ -320,7 +341,8 @@ def main():
     args = ap.parse_args()
 
     if args.traffic_from:
-        write_traffic_summary(*args.traffic_from, workload=args.workload)
+        write_traffic_summary(*args.traffic_from, workload=args.workload,
+                              op=args.op if args.op in OP_SOURCES else "fwd")
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -409,7 +431,7 @@ def main():
     value = F / (wall / K) / 1e12
     achieved = F / avg_kernel_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = measured_traffic(w.name) if args.op == "fwd" and not variants else None
+    traffic = None if variants else measured_traffic(w.name, args.op)
     log(f"[bench] {K} steps: {ms_per_step:.4f} ms/step wall, kernel avg {avg_kernel_s*1e6:.1f} us "
         f"(min {min(kernel_ms)*1e3:.1f} us), {achieved:.1f} TFLOP/s = {100*achieved/peak:.1f}% of peak")
 
@@ -543,7 +565,7 @@ def bench_decode(args, w, dev):
             "peak": peak,
             "unit": "GB/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name, "decode"),
             "algorithmic_bytes": nbytes,
             "kernel_avg_us": round(avg_s * 1e6, 2),
             "unit_of_work": "one attn_decode call: append, split attention and merge kernels",
@@ -551,6 +573,9 @@ def bench_decode(args, w, dev):
         "cpu_baseline": None,
         "context": "KV-cache decode; the headline metric is the forward (--op fwd)",
     }
+    if args.calibration_copy_mib:
+        calibration_copy(args.calibration_copy_mib)
+        result["calibration_copy_bytes"] = args.calibration_copy_mib * 2**20
     if not args.no_cpu_baseline:
         del gq, gkc, gvc
         kcf = kc.clone()
