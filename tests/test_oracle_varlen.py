@@ -87,3 +87,32 @@ def test_planted_packing_mistakes_fail_the_pin(mistake):
         bad_k[0] = 0
     O, _ = oracle.attention_varlen(q, k, v, bad_q, bad_k, scale, causal)
     assert np.abs(O - Ob).max() > 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_is_document_masked_attention(causal):
+    # Documents packed into one sequence, each token attending only to the
+    # tokens of its own document (document masking): the same as the packed
+    # variable-length attention with the document boundaries as prefix sums.
+    # Reference: one dense softmax over the whole packed sequence with a
+    # block-diagonal mask, written out here in fp64.
+    lens = [5, 1, 7, 3]
+    q, k, v, cu, _ = make_varlen(lens, lens, 2, 1, 8, "bf16", 1.0, seed=21)
+    scale = float(np.float32(0.35))
+    O, L = oracle.attention_varlen(q, k, v, cu, cu, scale, causal)
+    doc = np.repeat(np.arange(len(lens)), lens)
+    T = len(doc)
+    pos = np.concatenate([np.arange(n) for n in lens])
+    allowed = doc[:, None] == doc[None, :]
+    if causal:
+        allowed &= pos[None, :] <= pos[:, None]
+    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    for h in range(2):
+        sc = qd[:, h, :] @ kd[:, 0, :].T * scale
+        sc = np.where(allowed, sc, -np.inf)
+        mx = sc.max(axis=1, keepdims=True)
+        w = np.exp(sc - mx)
+        ref = (w / w.sum(axis=1, keepdims=True)) @ vd[:, 0, :]
+        np.testing.assert_allclose(O[:, h, :], ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L[h], (mx[:, 0] + np.log(w.sum(axis=1))), rtol=0, atol=1e-12)
+    assert T == int(cu[-1])
