@@ -227,6 +227,20 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
           dp[kb] = mfma_32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(vrow + a_off), df[ks], dp[kb]);
         }
       }
+      if constexpr (D >= 256) {
+        // d = 256 runs one wave per SIMD, so no other wave covers the LDS
+        // latency: the K and V operand reads run three k-steps ahead of the
+        // MFMAs, the K^T reads of the dQ product four MFMAs ahead.  (The
+        // dK/dV kernel already holds 512 registers; there the same pattern
+        // spills.)
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int i = 0; i < NKS - 3; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+      }
       __builtin_amdgcn_s_setprio(0);
       // dS^T = P^T (dP^T - D), P^T = 2^(s c - lse2); keys past the end and
       // (causal) above the diagonal get P = 0.
@@ -258,6 +272,15 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
           const u32x2_t x1 = lds_read_tr4(ktr + t_rd + (16 * kk + 8) * TS + 32 * db);
           acc[db] = mfma_32x32x16<BF16>(u32x4_t{x0[0], x0[1], x1[0], x1[1]}, b, acc[db]);
         }
+      }
+      if constexpr (D >= 256) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < NKK * NDB - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
       __builtin_amdgcn_s_setprio(0);
     }

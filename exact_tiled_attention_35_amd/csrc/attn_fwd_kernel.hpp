@@ -295,6 +295,18 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         s[kb] = mfma_32x32x16<BF16>(a, b, s[kb]);
       }
     }
+    if constexpr (C::kQInLds) {
+      // d = 256 runs one wave per SIMD, so no other wave covers the LDS
+      // latency: the Q and K operand reads are kept three k-steps ahead of
+      // the MFMAs (deeper was measured slower)
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < NKS - 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    }
     if (prescale) {  // scale <= 0: take the max of s*c directly
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) s[kb] *= c_log2;
@@ -442,6 +454,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             oacc[db] = mfma_32x32x16<BF16>(a, phi, oacc[db]);
             if constexpr (decltype(with_lo)::value) oacc[db] = mfma_32x32x16<BF16>(a, plo, oacc[db]);
           }
+        }
+        if constexpr (C::kQInLds && !decltype(with_lo)::value) {
+          // and the V^T operand reads four MFMAs ahead
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+          for (int i = 0; i < NKK * NDB - 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
       };
       __builtin_amdgcn_s_setprio(1);
