@@ -96,9 +96,8 @@ struct TileCfg {
   static constexpr int kQElems = kQInLds ? kQInst * 64 * 8 : 0;
   static constexpr int kLdsElems = 2 * kStage + kQElems;
   static constexpr int kMinWavesPerEU = (D >= 256) ? 1 : 2;
-  // Unmasked tiles skip the tile maximum (see the kernel); at d = 256 the
-  // extra live state of that body costs more than the maximum it saves.
-  static constexpr bool kLeanTiles = (D <= 128);
+  // Unmasked tiles after the first skip the tile maximum (see the kernel).
+  static constexpr bool kLeanTiles = true;
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile sizes must be multiples of 32");
   static_assert((KS / 2) % 8 == 4 && (VS / 2) % 32 == 16, "bank-conflict-free strides");
 };
