@@ -272,6 +272,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const float ce = (!plain || prescale) ? 1.0f : c_log2;
   float slope = 0.f;
   if constexpr (MODS) slope = mods.slopes ? mods.slopes[w.hq] : 0.f;
+  const bool alibi_only = MODS && mods.slopes && !(mods.cap > 0.f) && mods.left < 0 && mods.right < 0;
+  const float slope_l2 = slope * kLog2e_f, sigma_l2 = mods.sigma * kLog2e_f;
 
   if (nt > 0) issue_tile(jb * BN, smem);
   __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tile 0 have landed
@@ -395,22 +397,43 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           // Softcap, ALiBi and the window on every element; log2 units.
           if (mods.left >= 0 && j0 < qw0 + 31 + diag - mods.left) need_mask = true;
           if (mods.right >= 0 && j0 + BN - 1 > qw0 + diag + mods.right) need_mask = true;
+          // ALiBi alone (no softcap, no window) on a tile whose keys all lie
+          // on one side of every row's diagonal key: the distance keeps its
+          // sign, so the bias is linear in the key offset and every key is
+          // visible -- two FMAs per score instead of the general transform.
+          const bool below = j0 + BN - 1 <= qw0 + diag;
+          const bool above = !CAUSAL && j0 >= qw0 + 31 + diag;
+          if (alibi_only && (below || above) && j0 + BN <= Nk) {
+            // t = s*sigma*log2e - slope*log2e*|my_q + diag - j|, with
+            // j = j0 + kb*32 + 8*(r/4) + 4*hh + r%4
+            const float ss = below ? slope_l2 : -slope_l2;
+            const float lane_base = -ss * (float)(my_q + diag - j0 - 4 * hh);
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
+            for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              const int dist = my_q + diag - j;
-              float tv = s[kb][r];
-              if (!plain) {
-                tv *= mods.sigma;
-                if (mods.cap > 0.f) tv = mods.cap * tanh_fast(tv * __builtin_amdgcn_rcpf(mods.cap));
-                tv = (tv - slope * (float)(dist < 0 ? -dist : dist)) * kLog2e_f;
+              for (int r = 0; r < 16; ++r) {
+                const float off = (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
+                s[kb][r] = __builtin_fmaf(s[kb][r], sigma_l2, __builtin_fmaf(ss, off, lane_base));
               }
-              const bool vis = j < Nk && (!CAUSAL || dist >= 0) &&
-                               (mods.left < 0 || dist <= mods.left) &&
-                               (mods.right < 0 || -dist <= mods.right);
-              s[kb][r] = vis ? tv : -INFINITY;
+            }
+          } else {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const int dist = my_q + diag - j;
+                float tv = s[kb][r];
+                if (!plain) {
+                  tv *= mods.sigma;
+                  if (mods.cap > 0.f) tv = mods.cap * tanh_fast(tv * __builtin_amdgcn_rcpf(mods.cap));
+                  tv = (tv - slope * (float)(dist < 0 ? -dist : dist)) * kLog2e_f;
+                }
+                const bool vis = j < Nk && (!CAUSAL || dist >= 0) &&
+                                 (mods.left < 0 || dist <= mods.left) &&
+                                 (mods.right < 0 || -dist <= mods.right);
+                s[kb][r] = vis ? tv : -INFINITY;
+              }
             }
           }
         } else if (need_mask) {
