@@ -274,6 +274,10 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if constexpr (MODS) slope = mods.slopes ? mods.slopes[w.hq] : 0.f;
   const bool alibi_only = MODS && mods.slopes && !(mods.cap > 0.f) && mods.left < 0 && mods.right < 0;
   const float slope_l2 = slope * kLog2e_f, sigma_l2 = mods.sigma * kLog2e_f;
+  const bool cap_only = MODS && !mods.slopes && mods.cap > 0.f && mods.left < 0 && mods.right < 0;
+  // softcap: exp2 argument 2 x log2e with x = s sigma / cap; output scale cap log2e
+  const float cap_in = cap_only ? mods.sigma * __builtin_amdgcn_rcpf(mods.cap) * 2.88539008177792681472f : 0.f;
+  const float cap_l2 = mods.cap * kLog2e_f;
 
   if (nt > 0) issue_tile(jb * BN, smem);
   __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tile 0 have landed
@@ -397,13 +401,24 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           // Softcap, ALiBi and the window on every element; log2 units.
           if (mods.left >= 0 && j0 < qw0 + 31 + diag - mods.left) need_mask = true;
           if (mods.right >= 0 && j0 + BN - 1 > qw0 + diag + mods.right) need_mask = true;
-          // ALiBi alone (no softcap, no window) on a tile whose keys all lie
-          // on one side of every row's diagonal key: the distance keeps its
-          // sign, so the bias is linear in the key offset and every key is
-          // visible -- two FMAs per score instead of the general transform.
+          // Fast paths for tiles every key of which every row sees (no
+          // masking): softcap alone, and ALiBi alone on a tile whose keys all
+          // lie on one side of every row's diagonal key (the distance keeps
+          // its sign, so the bias is linear in the key offset: two FMAs per
+          // score).  Other tiles take the general per-element transform.
           const bool below = j0 + BN - 1 <= qw0 + diag;
           const bool above = !CAUSAL && j0 >= qw0 + 31 + diag;
-          if (alibi_only && (below || above) && j0 + BN <= Nk) {
+          if (cap_only && (!CAUSAL || below) && j0 + BN <= Nk) {
+            // t = cap * tanh(s * sigma / cap) * log2e, tanh(x) = 1 - 2 / (e^(2x) + 1)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const float e = exp2_fast(s[kb][r] * cap_in);
+                s[kb][r] = __builtin_fmaf(-2.0f * cap_l2, __builtin_amdgcn_rcpf(e + 1.0f), cap_l2);
+              }
+            }
+          } else if (alibi_only && (below || above) && j0 + BN <= Nk) {
             // t = s*sigma*log2e - slope*log2e*|my_q + diag - j|, with
             // j = j0 + kb*32 + 8*(r/4) + 4*hh + r%4
             const float ss = below ? slope_l2 : -slope_l2;
