@@ -503,8 +503,18 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
       };
+      // P as hi + lo keeps rows that see few keys, where one P entry carries
+      // most of the weight, at the output's rounding.  A tile masked only by
+      // the left edge of a window of at least 128 keys needs no lo half:
+      // every row it holds sees at least that many keys.
+      bool with_lo = (CAUSAL || MODS) && need_mask;
+      if constexpr (MODS) {
+        const bool right_edge = (CAUSAL && j0 + BN - 1 > qw0 + diag) ||
+                                (mods.right >= 0 && j0 + BN - 1 > qw0 + diag + mods.right);
+        if (plain && mods.left >= 127 && !right_edge && j0 + BN <= Nk) with_lo = false;
+      }
       __builtin_amdgcn_s_setprio(1);
-      if ((CAUSAL || MODS) && need_mask)
+      if (with_lo)
         pv_product(std::true_type{});
       else
         pv_product(std::false_type{});
