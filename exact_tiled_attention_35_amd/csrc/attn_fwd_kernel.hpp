@@ -17,7 +17,8 @@
 //  * One workgroup = 4 wave64s = one block of 128 query rows of one (b, head);
 //    each wave owns 32 query rows.
 //  * Both products run transposed on v_mfma_f32_32x32x16_{bf16,f16}:
-//        S^T = K . Q^T   (A = K tile from LDS, B = Q^T kept in VGPRs)
+//        S^T = K . Q^T   (A = K tile from LDS, B = Q^T kept in VGPRs, or at
+//                         d = 256 read from an LDS copy of the Q tile)
 //        O^T = V^T . P^T (A = V^T tile from LDS, B = P^T straight from the
 //                         S^T accumulators)
 //    With the 32x32 accumulator layout (lane l, register r holds row
@@ -32,9 +33,10 @@
 //    flight while tile t is computed, one barrier per tile.
 //  * Online softmax in the log2 domain: t = s * scale * log2(e), p = 2^(t - m).
 //    The running maximum m is only raised when a tile's maximum exceeds it
-//    by more than RESCALE_THRESHOLD (p then stays <= 2^threshold).  Because
+//    by more than kRescaleThreshold (p then stays <= 2^threshold).  Because
 //    the same m is used for the sum l and for O, the result is still exact;
-//    the rescale of O is skipped on almost every tile.
+//    the rescale of O is skipped on almost every tile.  Tiles every row sees
+//    completely skip the tile maximum altogether ("lean" tiles, below).
 //  * Causal: tiles entirely above the diagonal are never loaded; tiles that
 //    cross it (and ragged tails) are masked per element.  On those tiles P is
 //    fed to the PV product as hi + lo halves (two MFMAs), which keeps the
@@ -42,6 +44,9 @@
 //    the accuracy of the output rounding.
 //  * The row sum l is accumulated from the unrounded fp32 p.
 //  * Epilogue: O /= l, rounded to nearest-even; lse = (m + log2 l) * ln 2.
+//  * Template switches: MODS adds the score variants (sliding window, ALiBi,
+//    softcap), VARLEN takes the rows of packed variable-length sequences
+//    from prefix sums; with both off the kernel is the plain one.
 #pragma once
 
 #include <hip/hip_runtime.h>
