@@ -116,10 +116,17 @@ def algorithmic_bytes(w) -> int:
 
 
 def kernel_source_hash(op: str = "fwd") -> str:
+    """Hash of an operation's kernel sources with comments and whitespace
+    removed, so that edits to comments alone keep the measured figures."""
+    import re
+
     h = hashlib.sha256()
     for n in OP_SOURCES[op]:
-        with open(os.path.join(_CSRC, n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(_CSRC, n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
