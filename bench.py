@@ -336,6 +336,11 @@ def main():
     ap.add_argument("--alibi", action="store_true", help="fwd only: ALiBi slopes (attn_fwd_ext)")
     ap.add_argument("--splits", type=int, default=0,
                     help="decode only: number of key splits (0: the library's heuristic)")
+    ap.add_argument("--cold-mib", type=int, default=0, metavar="MIB",
+                    help="fwd/bwd diagnostic: after the timed steps, time the same number of "
+                         "steps again with MIB MiB of scratch read before each one (evicts L2 "
+                         "and the Infinity Cache; outside the timed region) and report them "
+                         "as \"cold\"; the headline figures stay the warm ones")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain elementwise copy kernel that "
@@ -472,6 +477,8 @@ def main():
         "context": "FlexAttention with the FA4 backend reports 1.2x-3.2x speedups on NVIDIA "
                    "Hopper/Blackwell (liora.io news item); other hardware, not a target",
     }
+    if args.cold_mib > 0:
+        result["cold"] = cold_timing(step, stream, K, args.cold_mib, F, peak)
     if args.calibration_copy_mib:
         calibration_copy(args.calibration_copy_mib)
         result["calibration_copy_bytes"] = args.calibration_copy_mib * 2**20
@@ -494,6 +501,34 @@ def main():
         else:
             result["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do, args.cpu_budget)
     print(json.dumps(result), flush=True)
+
+
+def cold_timing(step, stream, K, mib, F, peak):
+    """Diagnostic: K steps, each after MIB MiB of scratch has been read on the
+    same stream (a reduction, outside the events), so that no input is left in
+    L2 or the Infinity Cache when the step starts.  The scratch is written once
+    beforehand and then only read, so no dirty lines are left to be written
+    back during a step.  Returns the event-timed kernel average and its
+    fraction of the peak."""
+    import torch
+
+    scratch = torch.ones(mib * 2**20 // 4, dtype=torch.float32, device=stream.device)
+    sums = [scratch.sum() for _ in range(2)]  # flush the initial writes
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for i in range(K):
+        sums.append(scratch.sum())
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    avg_s = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / K / 1e3
+    achieved = F / avg_s / 1e12
+    log(f"[bench] cold ({mib} MiB read before each step): kernel avg {avg_s * 1e6:.1f} us, "
+        f"{achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% of peak")
+    return {"scratch_mib": mib, "kernel_avg_us": round(avg_s * 1e6, 2),
+            "achieved": round(achieved, 3), "frac": round(achieved / peak, 4)}
 
 
 def bench_decode(args, w, dev):
