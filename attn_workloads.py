@@ -137,3 +137,23 @@ VARLEN_WORKLOADS = {
     for n, c in (("varlen_causal_t16384_len256to4096_h16_d128_bf16", True),
                  ("varlen_t16384_len256to4096_h16_d128_bf16", False))
 }
+
+
+def make_block_mask(B, Hm, nqb, nkb, density, seed):
+    """uint8 flags [B, Hm, nqb, nkb] for the block-sparse forward: each
+    (query block, key block) pair is kept with probability ``density``,
+    independently, from a seeded CPU generator."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    return (torch.rand((B, Hm, nqb, nkb), generator=g, dtype=torch.float32) < density).to(torch.uint8)
+
+
+# Block-sparse forward: the headline shape and the causal B2 H32 N8192 shape,
+# each query head with its own random mask over the 128 x 128 blocks
+# (density 0.5, seed 9).
+BLOCK = 128
+BLOCKSPARSE_WORKLOADS = {
+    "blocksparse_d50_mha_b4_h16_n4096_d128_bf16":
+        dict(base="mha_b4_h16_n4096_d128_bf16", density=0.5, mask_seed=9),
+    "blocksparse_d50_causal_mha_b2_h32_n8192_d128_bf16":
+        dict(base="causal_mha_b2_h32_n8192_d128_bf16", density=0.5, mask_seed=9),
+}

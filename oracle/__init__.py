@@ -17,6 +17,7 @@ from .exact import (  # noqa: F401
     attention,
     attention_backward,
     attention_varlen,
+    attention_block_sparse,
     attention_rows,
     kv_head_of,
     allowed_keys,

@@ -45,6 +45,17 @@ Readings where the pages are silent (each is listed in the design notes):
   softcapping replaces the scaled score t by cap * tanh(t / cap); ALiBi then
   adds -slope_h * |i + diag - j|.  The softmax runs over the result.
 
+Block sparsity (``attention_block_sparse``; the liora.io item on
+FlexAttention's new backend names block sparsity among its features, in the
+section on its limitations, and gives 128 x 128 as the Hopper kernel's
+block size): a mask of flags over (query block, key block) pairs decides
+which blocks of the score matrix take part.  Reading: row i lies in query
+block floor(i / 128), key j in key block floor(j / 128); key j is visible to
+row i iff the flag of that pair is nonzero and j is causally visible (when
+causal); everything else is the definition above.  The mask is
+[B, Hm, ceil(Nq / 128), ceil(Nk / 128)] with Hm = 1 (shared by all query
+heads) or Hm = Hq.
+
 The backward pass (``attention_backward``): the pages say the library
 computes gradients (hysenlabs.com page, section "GPU-Abdeckung: Ampere,
 Hopper und AMD-Backends" on the backward pass for head dimension 256;
@@ -65,6 +76,7 @@ __all__ = [
     "attention_rows",
     "attention_backward",
     "attention_varlen",
+    "attention_block_sparse",
     "kv_head_of",
     "allowed_keys",
     "visible_range",
@@ -137,10 +149,12 @@ def _check_shapes(q: np.ndarray, k: np.ndarray, v: np.ndarray):
 
 
 def _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, want_p,
-                      window=(-1, -1), slope=0.0, softcap=0.0):
+                      window=(-1, -1), slope=0.0, softcap=0.0, key_mask=None):
     """Exact attention for the query rows ``rows`` of one (b, h) pair.
 
     qh: [Nq, d]; kg, vg: [Nk, d] (already the KV head this query head reads).
+    key_mask: optional [R, Nk] booleans; a key takes part only where it is
+    True (in addition to the causal and window bounds).
     Returns (O [R, d], lse [R], S [R, Nk], P [R, Nk] or None).
     """
     rows = np.asarray(rows, dtype=np.int64)
@@ -155,6 +169,8 @@ def _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, want_p,
                    dtype=np.int64).reshape(len(rows), 2)
     kidx = np.arange(Nk)[None, :]
     visible = (kidx >= rng[:, :1]) & (kidx < rng[:, 1:])
+    if key_mask is not None:
+        visible = visible & np.asarray(key_mask, dtype=bool)
     S = np.where(visible, S, -np.inf)
     # Row-wise softmax over keys.  Subtracting the row maximum is the usual
     # stable evaluation; it does not change the value.
@@ -330,4 +346,45 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
         Ob, Lb = attention(q[None, qs:qe], k[None, ks:ke], v[None, ks:ke], scale, causal)
         O[qs:qe] = Ob[0]
         lse[:, qs:qe] = Lb[0]
+    return O, lse
+
+
+def attention_block_sparse(q, k, v, block_mask, scale: float, causal: bool = False,
+                           block: int = 128):
+    """Exact attention restricted by a block mask, in fp64.
+
+    block_mask: [B, Hm, ceil(Nq / block), ceil(Nk / block)] (numpy or CPU
+    torch), Hm = 1 or Hq; query row i and key j interact iff
+    block_mask[b, hm, i // block, j // block] != 0 (hm = 0 when Hm = 1, else
+    the query head) and, when ``causal``, j <= i + (Nk - Nq).  The flags are
+    expanded to one boolean per (row, key) and the softmax runs over the
+    scores of the keys they keep, exactly as in ``attention``; a row that
+    keeps no key gets O = 0 and lse = -inf.  ``block`` is 128 for the
+    library; smaller values serve tiny test shapes.
+
+    Returns (O [B, Nq, Hq, d], lse [B, Hq, Nq]) in fp64.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, Nq, Nk, Hq, Hkv, d = _check_shapes(q, k, v)
+    if hasattr(block_mask, "detach"):
+        block_mask = block_mask.detach().cpu().numpy()
+    bm = np.asarray(block_mask) != 0
+    nqb, nkb = -(-Nq // block), -(-Nk // block)
+    if bm.ndim != 4 or bm.shape[0] != B or bm.shape[1] not in (1, Hq) or \
+            bm.shape[2] != nqb or bm.shape[3] != nkb:
+        raise ValueError(f"block_mask{bm.shape} must be [B, 1 or Hq, {nqb}, {nkb}]")
+    sigma = float(np.float32(scale))
+    O = np.zeros((B, Nq, Hq, d))
+    lse = np.full((B, Hq, Nq), -np.inf)
+    rows = np.arange(Nq)
+    qblk, kblk = rows // block, np.arange(Nk) // block
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            flags = bm[b, 0 if bm.shape[1] == 1 else h]
+            key_mask = flags[qblk[:, None], kblk[None, :]]  # [Nq, Nk]
+            Or, lr, _, _ = _rows_of_one_head(q[b, :, h, :], k[b, :, g, :], v[b, :, g, :], sigma,
+                                             rows, Nq, Nk, causal, False, key_mask=key_mask)
+            O[b, :, h, :] = Or
+            lse[b, h, :] = lr
     return O, lse

@@ -10,13 +10,14 @@ directly as it can be: weight_j = exp(s_j) / sum_k exp(s_k).
 import math
 
 
-def brute_attention(q, k, v, scale, causal, left=-1, right=-1, slopes=None, cap=0.0):
+def brute_attention(q, k, v, scale, causal, left=-1, right=-1, slopes=None, cap=0.0, keep=None):
     """q: nested lists [B][Nq][Hq][d]; k, v: [B][Nk][Hkv][d]; python floats.
 
     Optional score variants: a window of ``left`` keys before and ``right``
     keys after the diagonal key i + Nk - Nq (negative = unbounded); per-head
     ALiBi ``slopes`` (bias -slope * distance to that diagonal key); a softcap
-    ``cap`` (cap * tanh(score / cap), before the bias).
+    ``cap`` (cap * tanh(score / cap), before the bias); ``keep(b, h, i, j)``,
+    a predicate that a key must also satisfy (an explicit element mask).
 
     Returns (O as nested lists [B][Nq][Hq][d], lse as [B][Hq][Nq])."""
     B, Nq, Hq, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
@@ -30,7 +31,8 @@ def brute_attention(q, k, v, scale, causal, left=-1, right=-1, slopes=None, cap=
                 dk = i + Nk - Nq  # the key on this row's diagonal
                 keys = [j for j in range(Nk)
                         if (not causal or j <= dk) and (left < 0 or dk - j <= left)
-                        and (right < 0 or j - dk <= right)]
+                        and (right < 0 or j - dk <= right)
+                        and (keep is None or keep(b, h, i, j))]
                 if not keys:
                     lse[b][h][i] = -math.inf
                     continue
