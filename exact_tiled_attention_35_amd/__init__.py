@@ -14,7 +14,10 @@ from .attention import (  # noqa: F401
     attn_decode_num_splits,
     attn_decode_ptr,
     attn_decode_workspace_size,
+    BLOCK_MASK_SIZE,
     attn_fwd,
+    attn_fwd_blocksparse,
+    attn_fwd_blocksparse_ptr,
     attn_fwd_ext_ptr,
     attn_fwd_ptr,
     attn_fwd_varlen,

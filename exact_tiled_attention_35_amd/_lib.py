@@ -49,6 +49,8 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd_ext.restype = ci
     lib.attn_fwd_varlen.argtypes = [vp] * 7 + [ci] * 7 + [cf, ci, ci, vp]
     lib.attn_fwd_varlen.restype = ci
+    lib.attn_fwd_blocksparse.argtypes = [vp] * 6 + [ci] * 7 + [cf, ci, ci, vp]
+    lib.attn_fwd_blocksparse.restype = ci
     lib.attn_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, ci, ci, cf, ci, ci, vp]
     lib.attn_bwd.restype = ci
     lib.attn_decode.argtypes = [vp] * 9 + [ctypes.c_size_t] + [ci] * 7 + [cf, ci, ci, ci, vp]

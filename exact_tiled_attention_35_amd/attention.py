@@ -210,6 +210,57 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, lse
 
 
+BLOCK_MASK_SIZE = 128  # rows and keys per block of the block mask (ATTN_BLOCK_MASK_SIZE)
+
+
+def attn_fwd_blocksparse_ptr(q: int, k: int, v: int, out: int, lse: int, block_mask: int,
+                             mask_heads: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
+                             scale: float, causal: bool, dtype: int, stream: int = 0) -> int:
+    """The C entry point attn_fwd_blocksparse with raw integer pointers."""
+    return _lib.load().attn_fwd_blocksparse(q or None, k or None, v or None, out or None,
+                                            lse or None, block_mask or None, int(mask_heads),
+                                            int(B), int(Hq), int(Hkv), int(Nq), int(Nk), int(d),
+                                            float(scale), int(bool(causal)), int(dtype),
+                                            stream or None)
+
+
+def attn_fwd_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         block_mask: torch.Tensor, softmax_scale: float | None = None,
+                         causal: bool = False, out: torch.Tensor | None = None,
+                         lse: torch.Tensor | None = None):
+    """Exact attention restricted by a block mask.
+
+    q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d] as for ``attn_fwd``; block_mask:
+    uint8 or bool [B, 1 or Hq, ceil(Nq / 128), ceil(Nk / 128)] on q's device,
+    nonzero where a (query block, key block) pair of 128 x 128 takes part.
+    Returns (out [B, Nq, Hq, d], lse [B, Hq, Nq] fp32).
+    """
+    B, Nq, Hq, Hkv, Nk, d = _check_qkv(q, k, v)
+    nqb, nkb = -(-Nq // BLOCK_MASK_SIZE), -(-Nk // BLOCK_MASK_SIZE)
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.view(torch.uint8)
+    if block_mask.dim() != 4 or block_mask.shape[1] not in (1, Hq):
+        raise ValueError(f"block_mask must be [B, 1 or Hq, {nqb}, {nkb}]")
+    _check_like("block_mask", block_mask, (B, block_mask.shape[1], nqb, nkb), torch.uint8, q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check_like("out", out, q.shape, q.dtype, q.device)
+    _check_like("lse", lse, (B, Hq, Nq), torch.float32, q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        code = attn_fwd_blocksparse_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        lse.data_ptr(), block_mask.data_ptr(), block_mask.shape[1],
+                                        B, Hq, Hkv, Nq, Nk, d, softmax_scale, causal,
+                                        _DTYPE_CODE[q.dtype], stream)
+    if code != _lib.ATTN_OK:
+        raise AttnError(code)
+    return out, lse
+
+
 class _Attention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, softmax_scale, causal):

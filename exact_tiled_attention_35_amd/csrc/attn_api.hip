@@ -24,10 +24,11 @@ using eta_host::overlaps;
 
 constexpr const char* kVersion = "0.2.0 gfx950 exact-tiled-attention fwd+bwd";
 
-template <int D, bool BF16, bool CAUSAL, bool MODS, bool VARLEN = false>
+template <int D, bool BF16, bool CAUSAL, bool MODS, bool VARLEN = false, bool SPARSE = false>
 int launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
            int Hkv, int Nq, int Nk, float scale, const eta::ScoreMods& mods, hipStream_t stream,
-           const eta::VarlenArgs& va = eta::VarlenArgs{nullptr, nullptr, 0, 0, 0}) {
+           const eta::VarlenArgs& va = eta::VarlenArgs{nullptr, nullptr, 0, 0, 0},
+           const eta::BlockMaskArgs& bm = eta::BlockMaskArgs{nullptr, 0, 0}) {
   using C = eta::TileCfg<D>;
   const int nqb = (Nq + C::BM - 1) / C::BM;
   const int64_t total64 = (int64_t)B * Hq * nqb;
@@ -38,11 +39,11 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, i
   // a window alone keeps the plain kernel's scaling.
   const bool transform = MODS && (mods.slopes || mods.cap > 0.f);
   const int prescale = (!transform && !(scale > 0.f)) ? 1 : 0;
-  hipLaunchKernelGGL((eta::attn_fwd_kernel<D, BF16, CAUSAL, MODS, VARLEN>), dim3(total),
+  hipLaunchKernelGGL((eta::attn_fwd_kernel<D, BF16, CAUSAL, MODS, VARLEN, SPARSE>), dim3(total),
                      dim3(C::kThreads), 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                      static_cast<uint16_t*>(out), lse, Hq, Hkv, Nq, Nk, nqb, total, c_log2, prescale,
-                     mods, va);
+                     mods, va, bm);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -140,7 +141,70 @@ int dispatch_varlen(bool bf16, bool causal, const void* q, const void* k, const 
                 : launch<D, false, false, false, true>(q, k, v, out, lse, B, Hq, Hkv, max_q, 1, scale, none, s, va);
 }
 
+template <int D>
+int dispatch_sparse(bool bf16, bool causal, const void* q, const void* k, const void* v, void* out,
+                    float* lse, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
+                    const eta::BlockMaskArgs& bm, hipStream_t s) {
+  const eta::ScoreMods none{-1, -1, nullptr, 0.f, scale};
+  const eta::VarlenArgs nv{nullptr, nullptr, 0, 0, 0};
+  if (bf16) {
+    return causal ? launch<D, true, true, false, false, true>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, none, s, nv, bm)
+                  : launch<D, true, false, false, false, true>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, none, s, nv, bm);
+  }
+  return causal ? launch<D, false, true, false, false, true>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, none, s, nv, bm)
+                : launch<D, false, false, false, false, true>(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, none, s, nv, bm);
+}
+
 }  // namespace
+
+extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* out,
+                                    float* lse, const unsigned char* block_mask, int mask_heads,
+                                    int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                                    int causal, int dtype, void* stream) {
+  // 1. shape
+  if (B < 0 || Nq < 0 || Hq < 1 || Hkv < 1 || Nk < 1 || d < 1) return ATTN_ERR_BAD_SHAPE;
+  // 2. empty problem: nothing to do
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  const double q_elems = (double)B * Nq * Hq * d, kv_elems = (double)B * Nk * Hkv * d;
+  if (q_elems > 0x1p60 || kv_elems > 0x1p60) return ATTN_ERR_BAD_SHAPE;
+  if ((double)128 * Hq * d * 2 >= 0x1p31 || (double)64 * Hkv * d * 2 >= 0x1p31)
+    return ATTN_ERR_BAD_SHAPE;
+  if ((double)B * Hq * ((Nq + 127) / 128) > 0x7fffffff) return ATTN_ERR_BAD_SHAPE;
+  const int nqb = (Nq + eta::kMaskBlock - 1) / eta::kMaskBlock;
+  const int nkb = (Nk + eta::kMaskBlock - 1) / eta::kMaskBlock;
+  // 3. null pointers
+  if (!q || !k || !v || !out || !lse || !block_mask) return ATTN_ERR_NULL_POINTER;
+  // 4-7. GQA ratio, head dimension, element type, scale, mask heads
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA_RATIO;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED_HDIM;
+  if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
+  if (!finite_bits(scale)) return ATTN_ERR_BAD_SCALE;
+  if (mask_heads != 1 && mask_heads != Hq) return ATTN_ERR_BAD_ARGUMENT;
+  // 8. alignment (the mask is read byte by byte)
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+    return ATTN_ERR_MISALIGNED;
+  // 9. aliasing: outputs must not overlap the inputs (mask included) or each other
+  const size_t qb = (size_t)q_elems * 2, kvb = (size_t)kv_elems * 2;
+  const size_t lb = (size_t)B * Hq * Nq * sizeof(float);
+  const size_t mb = (size_t)B * mask_heads * nqb * nkb;
+  const void* in_p[4] = {q, k, v, block_mask};
+  const size_t in_n[4] = {qb, kvb, kvb, mb};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(out, qb, in_p[i], in_n[i]) || overlaps(lse, lb, in_p[i], in_n[i])) return ATTN_ERR_ALIASING;
+  if (overlaps(out, qb, lse, lb)) return ATTN_ERR_ALIASING;
+  // 10. device
+  const int dev_status = check_device();
+  if (dev_status != ATTN_OK) return dev_status;
+  // 11. launch
+  const eta::BlockMaskArgs bm{block_mask, mask_heads, nkb};
+  const bool bf16 = dtype == ATTN_DTYPE_BF16, c = causal != 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (d) {
+    case 64: return dispatch_sparse<64>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, bm, s);
+    case 128: return dispatch_sparse<128>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, bm, s);
+    default: return dispatch_sparse<256>(bf16, c, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, scale, bm, s);
+  }
+}
 
 extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                                const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq,
@@ -223,7 +287,8 @@ extern "C" const char* attn_status_string(int status) {
     case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: kernel launch failed";
     case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace smaller than attn_decode_workspace_size";
     case ATTN_ERR_BAD_ARGUMENT:
-      return "ATTN_ERR_BAD_ARGUMENT: window bounds must be >= -1 and softcap finite and >= 0";
+      return "ATTN_ERR_BAD_ARGUMENT: window bounds must be >= -1, softcap finite and >= 0, "
+             "mask_heads 1 or Hq";
     default: return "unknown attn status";
   }
 }

@@ -46,7 +46,8 @@
 //  * Epilogue: O /= l, rounded to nearest-even; lse = (m + log2 l) * ln 2.
 //  * Template switches: MODS adds the score variants (sliding window, ALiBi,
 //    softcap), VARLEN takes the rows of packed variable-length sequences
-//    from prefix sums; with both off the kernel is the plain one.
+//    from prefix sums, SPARSE visits only the key blocks a block mask flags;
+//    with all off the kernel is the plain one.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -135,13 +136,27 @@ struct VarlenArgs {
   int pairs;  // sequences x query heads
 };
 
-template <int D, bool BF16, bool CAUSAL, bool MODS = false, bool VARLEN = false>
+// Block sparsity: flags over (query block, key block) pairs of 128 x 128
+// decide which blocks of the score matrix take part; key j is visible to row
+// i only if the flag of (i / 128, j / 128) is nonzero (and causally, when
+// causal).  mask is [B, heads, ceil(Nq / 128), nkb] bytes with heads = 1
+// (shared by all query heads) or Hq; nkb = ceil(Nk / 128).
+constexpr int kMaskBlock = 128;
+struct BlockMaskArgs {
+  const uint8_t* mask;
+  int heads, nkb;
+};
+
+template <int D, bool BF16, bool CAUSAL, bool MODS = false, bool VARLEN = false, bool SPARSE = false>
 __global__ void __launch_bounds__(TileCfg<D>::kThreads, TileCfg<D>::kMinWavesPerEU)
 attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                 float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int nqb,
-                int total, float c_log2, int prescale, ScoreMods mods, VarlenArgs va) {
+                int total, float c_log2, int prescale, ScoreMods mods, VarlenArgs va,
+                BlockMaskArgs bm) {
   using C = TileCfg<D>;
+  static_assert(!(SPARSE && (MODS || VARLEN)), "block sparsity is an instance of its own");
+  static_assert(kMaskBlock % C::BN == 0 && kMaskBlock == C::BM, "a mask block is whole tiles");
   constexpr int BN = C::BN, BM = C::BM, KS = C::KS, VS = C::VS;
   constexpr int NKS = D / 16;  // k-steps of the S^T product
   constexpr int NKB = BN / 32; // 32-key blocks per tile
@@ -226,7 +241,58 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       w_begin = qw0 + diag - mods.left;
     }
   }
-  const int nt = kv_end > jb * BN ? (kv_end - jb * BN + BN - 1) / BN : 0;
+  int nt = kv_end > jb * BN ? (kv_end - jb * BN + BN - 1) / BN : 0;
+
+  // ---- Block sparsity: the tiles of flagged key blocks below kv_end, in key
+  // order.  Each wave reads the flags of 64 key blocks per step (one byte per
+  // lane, a ballot makes them wave-uniform), counts the tiles it will visit
+  // (nt) and those every row sees whole (sp_nf, the lean/full bodies), and
+  // then walks the flagged blocks; unflagged tiles are never loaded.
+  constexpr int TPB = kMaskBlock / BN;  // tiles per mask block
+  int sp_nf = 0, sp_chunk = 0, sp_blk = 0, sp_sub = TPB, sp_cur = 0, sp_nchunks = 0;
+  uint64_t sp_bits = 0;
+  const int nkb_eff = (kv_end + kMaskBlock - 1) / kMaskBlock;
+  const int64_t sp_row = ((int64_t)w.b * bm.heads + (bm.heads == 1 ? 0 : w.hq)) * nqb + w.qblk;
+  // this row of flags; flags past kv_end read as 0 (unused without SPARSE)
+  const rsrc_t sp_mr = make_rsrc(SPARSE ? bm.mask + sp_row * bm.nkb : nullptr, SPARSE ? nkb_eff : 0);
+  if constexpr (SPARSE) {
+    sp_nchunks = (nkb_eff + 63) / 64;
+    int nf_plain = Nk / BN;
+    if (CAUSAL) nf_plain = min(nf_plain, max(0, (q0 + diag + 1) / BN));
+    const int full_blocks = nf_plain / TPB, full_rem = nf_plain % TPB;
+    const int last = nkb_eff - 1;  // may hold fewer than TPB tiles
+    const int last_tiles = (kv_end - kMaskBlock * last + BN - 1) / BN;
+    int blocks = 0, nf_blocks = 0;
+    nt = 0;
+    for (int c = 0; c < sp_nchunks; ++c) {
+      const uint64_t bits = __builtin_amdgcn_ballot_w64(
+          __builtin_amdgcn_raw_buffer_load_b8(sp_mr, 64 * c + lane, 0, 0) != 0);
+      if (c == 0) sp_bits = bits;
+      blocks += __builtin_popcountll(bits);
+      const int below = full_blocks - 64 * c;  // blocks of this chunk under full_blocks
+      nf_blocks += __builtin_popcountll(below >= 64 ? bits : below <= 0 ? 0ull
+                                        : bits & ((1ull << below) - 1));
+      if (full_rem && below >= 0 && below < 64 && ((bits >> below) & 1)) sp_nf += full_rem;
+      if (last / 64 == c && ((bits >> (last % 64)) & 1)) nt -= TPB - last_tiles;
+    }
+    nt += TPB * blocks;
+    sp_nf += TPB * nf_blocks;
+  }
+  // Start of the next visited tile (block sparsity only); called once per
+  // tile, only while one is left, so a flagged block lies ahead.
+  auto sparse_next = [&]() -> int {
+    if (++sp_sub >= TPB) {
+      while (sp_bits == 0 && sp_chunk + 1 < sp_nchunks) {
+        ++sp_chunk;
+        sp_bits = __builtin_amdgcn_ballot_w64(
+            __builtin_amdgcn_raw_buffer_load_b8(sp_mr, 64 * sp_chunk + lane, 0, 0) != 0);
+      }
+      sp_blk = 64 * sp_chunk + (sp_bits ? __builtin_ctzll(sp_bits) : 0);
+      sp_bits &= sp_bits - 1;
+      sp_sub = 0;
+    }
+    return sp_blk * kMaskBlock + sp_sub * BN;
+  };
 
   // ---- Direct global->LDS tile loads.  This wave issues the K (V) tile's
   // instructions j = wave, wave + 4, ...; lane -> 16-byte slot 64 j + lane ->
@@ -284,7 +350,10 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const float cap_in = cap_only ? mods.sigma * __builtin_amdgcn_rcpf(mods.cap) * 2.88539008177792681472f : 0.f;
   const float cap_l2 = mods.cap * kLog2e_f;
 
-  if (nt > 0) issue_tile(jb * BN, smem);
+  if constexpr (SPARSE) {
+    if (nt > 0) sp_cur = sparse_next();
+  }
+  if (nt > 0) issue_tile(SPARSE ? sp_cur : jb * BN, smem);
   __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tile 0 have landed
   __syncthreads();
 
@@ -374,10 +443,14 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int kLean = 0, kFull = 1, kMasked = 2;
   auto tile = [&](int t, auto mode) {
     constexpr int kMode = decltype(mode)::value;
-    const int j0 = (jb + t) * BN;
+    const int j0 = SPARSE ? sp_cur : (jb + t) * BN;
     // Tile t+1 streams into the other stage while this one is computed (that
     // stage was last read in iteration t-1, before the barrier that ended it).
-    if (t + 1 < nt) issue_tile(j0 + BN, smem + ((t + 1) & 1) * C::kStage);
+    if (t + 1 < nt) {
+      int jn = j0 + BN;
+      if constexpr (SPARSE) jn = sp_cur = sparse_next();
+      issue_tile(jn, smem + ((t + 1) & 1) * C::kStage);
+    }
     const uint16_t* st = smem + (t & 1) * C::kStage;
 
     // wave-uniform: skip tiles above this wave's diagonal (or outside its window)
@@ -509,10 +582,11 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
       };
       // P as hi + lo keeps rows that see few keys, where one P entry carries
-      // most of the weight, at the output's rounding.  A tile masked only by
+      // most of the weight, at the output's rounding (with a block mask a row
+      // may keep only the keys of a ragged last block).  A tile masked only by
       // the left edge of a window of at least 128 keys needs no lo half:
       // every row it holds sees at least that many keys.
-      bool with_lo = (CAUSAL || MODS) && need_mask;
+      bool with_lo = (CAUSAL || MODS || SPARSE) && need_mask;
       if constexpr (MODS) {
         const bool right_edge = (CAUSAL && j0 + BN - 1 > qw0 + diag) ||
                                 (mods.right >= 0 && j0 + BN - 1 > qw0 + diag + mods.right);
@@ -549,6 +623,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     nf -= jb;
     if (!plain) t_lo = nf = 0;
   }
+  if constexpr (SPARSE) nf = sp_nf;
   nf = min(max(nf, 0), nt);
   t_lo = min(t_lo, nf);
   using LeanMode = std::integral_constant<int, kLean>;

@@ -72,7 +72,7 @@ typedef enum {
   ATTN_ERR_NO_DEVICE = -9,         /* no HIP device, or the current device is not gfx950 */
   ATTN_ERR_LAUNCH = -10,           /* the kernel launch failed                            */
   ATTN_ERR_WORKSPACE = -11,        /* attn_decode: workspace smaller than required       */
-  ATTN_ERR_BAD_ARGUMENT = -12      /* attn_fwd_ext: window bound < -1, bad softcap       */
+  ATTN_ERR_BAD_ARGUMENT = -12      /* window bound < -1, bad softcap; mask_heads not 1/Hq */
 } attn_status;
 
 /*
@@ -133,6 +133,30 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
                     const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
                     int total_q, int total_k, int max_seqlen_q, int d, float scale, int causal,
                     int dtype, void* stream);
+
+/*
+ * attn_fwd restricted by a block mask (block sparsity, which the liora.io
+ * item on FlexAttention's new backend lists among its features in its
+ * section on limitations; the same item gives 128 x 128 as the Hopper
+ * kernel's block size).  Query row i and key j interact only if
+ *     block_mask[b, hm, i / 128, j / 128] != 0
+ * with hm = 0 when mask_heads == 1 (one mask for all query heads) and hm = h
+ * when mask_heads == Hq, and, when causal != 0, j <= i + (Nk - Nq) as in
+ * attn_fwd.  Everything else is attn_fwd's definition; a row that keeps no
+ * key gets out = 0 and lse = -inf.  Key blocks whose flag is 0 are never
+ * read.
+ *   block_mask  [B, mask_heads, ceil(Nq / 128), ceil(Nk / 128)] bytes,
+ *               device, read; any nonzero byte keeps its block
+ * The other arguments, layouts and the validation order are attn_fwd's, with
+ * ATTN_ERR_NULL_POINTER also for a NULL block_mask, ATTN_ERR_BAD_ARGUMENT
+ * when mask_heads is neither 1 nor Hq (checked after the scale), and
+ * ATTN_ERR_ALIASING also when out or lse overlaps the mask.  The mask needs
+ * no alignment.
+ */
+#define ATTN_BLOCK_MASK_SIZE 128
+int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* out, float* lse,
+                         const unsigned char* block_mask, int mask_heads, int B, int Hq, int Hkv,
+                         int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream);
 
 /*
  * Exact attention backward: gradients of L = sum(dout * out) with respect to

@@ -18,6 +18,7 @@ from .exact import (  # noqa: F401
     attention_backward,
     attention_varlen,
     attention_block_sparse,
+    attention_block_sparse_rows,
     attention_rows,
     kv_head_of,
     allowed_keys,

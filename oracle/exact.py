@@ -77,6 +77,7 @@ __all__ = [
     "attention_backward",
     "attention_varlen",
     "attention_block_sparse",
+    "attention_block_sparse_rows",
     "kv_head_of",
     "allowed_keys",
     "visible_range",
@@ -346,6 +347,27 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
         Ob, Lb = attention(q[None, qs:qe], k[None, ks:ke], v[None, ks:ke], scale, causal)
         O[qs:qe] = Ob[0]
         lse[:, qs:qe] = Lb[0]
+    return O, lse
+
+
+def attention_block_sparse_rows(q, k, v, block_mask, scale: float, causal: bool, b: int, h: int,
+                                rows, block: int = 128):
+    """``attention_block_sparse`` for selected query rows of one (b, h) pair:
+    each row depends only on its own query row, its mask flags and the keys
+    and values of its KV head, so this is the same definition restricted to
+    those rows.  Returns (O [R, d], lse [R]) in fp64."""
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if hasattr(block_mask, "detach"):
+        block_mask = block_mask.detach().cpu().numpy()
+    bm = np.asarray(block_mask) != 0
+    rows = np.asarray(rows, dtype=np.int64)
+    flags = bm[b, 0 if bm.shape[1] == 1 else h]
+    key_mask = flags[(rows // block)[:, None], (np.arange(Nk) // block)[None, :]]
+    g = kv_head_of(h, Hq, Hkv)
+    O, lse, _, _ = _rows_of_one_head(_as_f64(q[b, :, h, :]), _as_f64(k[b, :, g, :]),
+                                     _as_f64(v[b, :, g, :]), float(np.float32(scale)), rows, Nq,
+                                     Nk, causal, False, key_mask=key_mask)
     return O, lse
 
 

@@ -41,7 +41,8 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
     assert names == ["attn_bwd", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_size",
-                     "attn_fwd", "attn_fwd_ext", "attn_fwd_varlen", "attn_status_string", "attn_version"]
+                     "attn_fwd", "attn_fwd_blocksparse", "attn_fwd_ext", "attn_fwd_varlen",
+                     "attn_status_string", "attn_version"]
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -443,3 +444,59 @@ def test_python_varlen_binding_rejects_bad_tensors():
         attn_fwd_varlen(q, q.half(), q.half(), cu, cu, 10)
     with pytest.raises(ValueError):  # CPU tensors
         attn_fwd_varlen(q, q, q, cu, cu, 10)
+
+
+# ---------------------------------------------------------------------------
+# attn_fwd_blocksparse (block mask over 128 x 128 blocks)
+# ---------------------------------------------------------------------------
+from exact_tiled_attention_35_amd.attention import attn_fwd_blocksparse_ptr  # noqa: E402
+
+MASK = 0xA00000001  # bytes need no alignment
+
+
+def call_bs(mask=MASK, mask_heads=1, **over):
+    a = dict(GOOD)
+    a.update(over)
+    return attn_fwd_blocksparse_ptr(a["q"], a["k"], a["v"], a["out"], a["lse"], mask, mask_heads,
+                                    a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                                    a["causal"], a["dtype"])
+
+
+@pytest.mark.parametrize("field,value", [("B", -1), ("Nq", -1), ("Hq", 0), ("Hkv", 0), ("Nk", 0), ("d", 0)])
+def test_blocksparse_bad_shape(field, value):
+    assert call_bs(**{field: value}) == _lib.ATTN_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("field", ["B", "Nq"])
+def test_blocksparse_empty_is_a_noop_with_null_pointers(field):
+    assert call_bs(**{field: 0}, q=0, k=0, v=0, out=0, lse=0, mask=0) == _lib.ATTN_OK
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "out", "lse", "mask"])
+def test_blocksparse_null_pointer(field):
+    over = {"mask": 0} if field == "mask" else {field: 0}
+    assert call_bs(**over) == _lib.ATTN_ERR_NULL_POINTER
+
+
+@pytest.mark.parametrize("heads", [0, 2, 7, -1, 9])
+def test_blocksparse_mask_heads_must_be_one_or_hq(heads):
+    assert call_bs(mask_heads=heads) == _lib.ATTN_ERR_BAD_ARGUMENT
+
+
+def test_blocksparse_checks_in_order():
+    assert call_bs(Hkv=3, mask_heads=2) == _lib.ATTN_ERR_GQA_RATIO
+    assert call_bs(d=96) == _lib.ATTN_ERR_UNSUPPORTED_HDIM
+    assert call_bs(dtype=7) == _lib.ATTN_ERR_UNSUPPORTED_DTYPE
+    assert call_bs(scale=float("nan"), mask_heads=2) == _lib.ATTN_ERR_BAD_SCALE
+    assert call_bs(mask_heads=2, q=Q + 8) == _lib.ATTN_ERR_BAD_ARGUMENT
+    assert call_bs(q=Q + 8) == _lib.ATTN_ERR_MISALIGNED
+    assert call_bs(mask=OUT + 100) == _lib.ATTN_ERR_ALIASING
+    assert call_bs(mask=LSE) == _lib.ATTN_ERR_ALIASING
+    # mask bytes: B * heads * ceil(Nq/128) * ceil(Nk/128) = 2 * 8 * 1 * 1 = 16
+    assert call_bs(mask=OUT - 16, mask_heads=8) != _lib.ATTN_ERR_ALIASING
+    assert call_bs(mask=OUT - 15, mask_heads=8) == _lib.ATTN_ERR_ALIASING
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a HIP device is visible here")
+def test_blocksparse_no_device_reported_without_gpu():
+    assert call_bs(mask_heads=8) == _lib.ATTN_ERR_NO_DEVICE

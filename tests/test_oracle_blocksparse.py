@@ -146,3 +146,14 @@ def test_rejects_a_mask_of_the_wrong_shape():
         oracle.attention_block_sparse(q, k, v, np.ones((1, 3, 3, 3)), 0.5, False, block=2)
     with pytest.raises(ValueError):
         oracle.attention_block_sparse(q, k, v, np.ones((1, 1, 2, 3)), 0.5, False, block=2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_selected_rows_equal_the_full_evaluation(causal):
+    case = (2, 11, 9, 4, 2, 3, 3, 4, causal)
+    q, k, v, mask = draw(case, 81)
+    O, L = oracle.attention_block_sparse(q, k, v, mask, 0.7, causal, block=3)
+    for b, h, rows in ((0, 0, [0, 1, 2]), (1, 3, [10, 4, 7]), (1, 1, range(11))):
+        Or, Lr = oracle.attention_block_sparse_rows(q, k, v, mask, 0.7, causal, b, h, rows, block=3)
+        np.testing.assert_array_equal(Or, O[b, list(rows), h, :])
+        np.testing.assert_array_equal(Lr, L[b, h, list(rows)])
