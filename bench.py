@@ -325,10 +325,11 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
-    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "varlen"), default="fwd",
+    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "varlen", "blocksparse"), default="fwd",
                     help="fwd: attn_fwd (the headline metric); bwd: attn_bwd, the backward pass; "
                          "decode: attn_decode on a KV-cache decode workload; varlen: "
-                         "attn_fwd_varlen on packed variable-length sequences")
+                         "attn_fwd_varlen on packed variable-length sequences; blocksparse: "
+                         "attn_fwd_blocksparse with a random block mask")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--window", nargs=2, type=int, default=(-1, -1), metavar=("LEFT", "RIGHT"),
                     help="fwd only: sliding window (attn_fwd_ext); flops count the kept pairs")
@@ -373,6 +374,13 @@ def main():
             log("no GPU visible")
             sys.exit(1)
         return bench_varlen(args, VARLEN_WORKLOADS[args.workload or next(iter(VARLEN_WORKLOADS))])
+    if args.op == "blocksparse":
+        from attn_workloads import BLOCKSPARSE_WORKLOADS
+
+        if not torch.cuda.is_available():
+            log("no GPU visible")
+            sys.exit(1)
+        return bench_blocksparse(args, args.workload or next(iter(BLOCKSPARSE_WORKLOADS)))
     if args.op == "decode":
         w = DECODE_WORKLOADS[args.workload or next(iter(DECODE_WORKLOADS))]
     else:
@@ -748,6 +756,150 @@ def bench_varlen(args, wl):
     if not args.no_cpu_baseline:
         del gq, gk, gv
         result["cpu_baseline"] = cpu_baseline_varlen(wl, lens, q, k, v, scale, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def blocksparse_pair_counts(Nq: int, Nk: int, causal: bool, block: int):
+    """[nqb, nkb] numbers of (query, key) pairs a fully kept block pair holds
+    (the causal bound applied inside it; bottom-right aligned)."""
+    import numpy as np
+
+    nqb, nkb = -(-Nq // block), -(-Nk // block)
+    i = np.arange(Nq)
+    hi = np.minimum(i + (Nk - Nq) + 1, Nk) if causal else np.full(Nq, Nk)  # keys [0, hi) per row
+    counts = np.zeros((nqb, nkb), dtype=np.int64)
+    for kb in range(nkb):
+        js, je = kb * block, min(Nk, kb * block + block)
+        per_row = np.clip(hi - js, 0, je - js)
+        counts[:, kb] = np.add.reduceat(per_row, np.arange(0, Nq, block))
+    return counts
+
+
+def cpu_baseline_blocksparse(w, q, k, v, mask, counts, budget_s: float):
+    """Time the fp64 oracle on whole query blocks of the workload, (batch,
+    head) pairs in order, until ``budget_s`` is spent."""
+    import numpy as np
+
+    import oracle
+    from attn_workloads import BLOCK
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        blas_threads = os.cpu_count() or 1
+    m = mask.numpy() != 0
+    done, f = 0, 0.0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.Hq):
+            oracle.attention_block_sparse_rows(q, k, v, mask, w.scale, w.causal, b, h,
+                                               np.arange(w.Nq), block=BLOCK)
+            f += 4.0 * w.d * float((m[b, h] * counts).sum())
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": f / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B * w.Hq} (batch, head) pairs, all rows each, fp64 NumPy, "
+                  f"{dt:.1f} s wall",
+    }
+
+
+def bench_blocksparse(args, name):
+    """One step = one attn_fwd_blocksparse call; flops count 4*d per kept
+    (query, key) pair and head (the mask's kept blocks, with the causal bound
+    inside them)."""
+    import torch
+
+    from attn_workloads import BLOCK, BLOCKSPARSE_WORKLOADS, WORKLOADS, make_block_mask, make_workload
+    from exact_tiled_attention_35_amd import attn_fwd_blocksparse, attn_version
+
+    spec = BLOCKSPARSE_WORKLOADS[name]
+    w = WORKLOADS[spec["base"]]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {name}; library {attn_version()}")
+    q, k, v = make_workload(w)
+    nqb, nkb = -(-w.Nq // BLOCK), -(-w.Nk // BLOCK)
+    mask = make_block_mask(w.B, w.Hq, nqb, nkb, spec["density"], spec["mask_seed"])
+    gq, gk, gv, gm = q.to(dev), k.to(dev), v.to(dev), mask.to(dev)
+    out = torch.empty_like(gq)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        attn_fwd_blocksparse(gq, gk, gv, gm, w.scale, w.causal, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    avg_s = sum(kernel_ms) / K / 1e3
+    counts = blocksparse_pair_counts(w.Nq, w.Nk, w.causal, BLOCK)
+    kept_blocks = mask.numpy() != 0
+    pairs = float((kept_blocks * counts[None, None]).sum())
+    F = 4.0 * w.d * pairs
+    value = F / (wall / K) / 1e12
+    achieved = F / avg_s / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    log(f"[bench] {K} steps: {wall / K * 1e3:.4f} ms/step wall, kernel avg {avg_s * 1e6:.1f} us "
+        f"(min {min(kernel_ms) * 1e3:.1f} us), {achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% "
+        f"of peak; kept block pairs {kept_blocks.mean():.3f}, kept (query, key) pairs "
+        f"{pairs / (w.B * w.Hq * w.Nq * w.Nk):.3f}")
+    result = {
+        "metric": "attention fwd TFLOP/s with a block mask (4*d per kept (query, key) pair and head)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0, sigma^2) inputs rounded to the element type; seeded "
+                "random block mask)",
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk,
+                   "d": w.d, "causal": w.causal, "seed": w.seed, "block": BLOCK,
+                   "mask_density": spec["density"], "mask_seed": spec["mask_seed"],
+                   "kept_block_fraction": round(float(kept_blocks.mean()), 4),
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "kernel_avg_us": round(avg_s * 1e6, 2),
+        },
+        "cpu_baseline": None,
+        "context": "block-sparse forward; the headline metric is the plain forward (--op fwd)",
+    }
+    if not args.no_cpu_baseline:
+        del gq, gk, gv
+        result["cpu_baseline"] = cpu_baseline_blocksparse(w, q, k, v, mask, counts, args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 
