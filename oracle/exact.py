@@ -275,7 +275,8 @@ def _softmax_rows_backward(P, dP):
     return P * (dP - D[:, None]), D
 
 
-def attention_backward(q, k, v, dout, scale: float, causal: bool = False):
+def attention_backward(q, k, v, dout, scale: float, causal: bool = False, *,
+                       block_mask=None, block: int = 128):
     """Exact gradients of L = sum(dout * attention(q, k, v)) in fp64.
 
     Per (b, h) with KV head g, probabilities P (rows over the visible keys,
@@ -293,7 +294,9 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool = False):
     no visible key contribute nothing.
 
     Args: q [B, Nq, Hq, d]; k, v [B, Nk, Hkv, d]; dout like q (numpy arrays
-    or CPU torch tensors); scale as passed to the library (an fp32 value).
+    or CPU torch tensors); scale as passed to the library (an fp32 value);
+    block_mask: None, or the flags of ``attention_block_sparse`` (the
+    gradients of that function: P is its probability matrix).
 
     Returns (dq [B, Nq, Hq, d], dk [B, Nk, Hkv, d], dv [B, Nk, Hkv, d],
     delta [B, Hq, Nq]) in fp64, where delta holds D.
@@ -308,12 +311,25 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool = False):
     dv = np.zeros_like(v)
     delta = np.zeros((B, Hq, Nq))
     rows = np.arange(Nq)
+    bm = None
+    if block_mask is not None:
+        if hasattr(block_mask, "detach"):
+            block_mask = block_mask.detach().cpu().numpy()
+        bm = np.asarray(block_mask) != 0
+        if bm.ndim != 4 or bm.shape[0] != B or bm.shape[1] not in (1, Hq) or \
+                bm.shape[2] != -(-Nq // block) or bm.shape[3] != -(-Nk // block):
+            raise ValueError(f"block_mask{bm.shape} does not match the shapes")
     for b in range(B):
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             qh, kg, vg = q[b, :, h, :], k[b, :, g, :], v[b, :, g, :]
             dO = dout[b, :, h, :]
-            _, _, _, P = _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, True)
+            key_mask = None
+            if bm is not None:
+                flags = bm[b, 0 if bm.shape[1] == 1 else h]
+                key_mask = flags[(rows // block)[:, None], (np.arange(Nk) // block)[None, :]]
+            _, _, _, P = _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, True,
+                                           key_mask=key_mask)
             dv[b, :, g, :] += P.T @ dO
             dP = dO @ vg.T
             dS, D = _softmax_rows_backward(P, dP)

@@ -157,3 +157,99 @@ def test_selected_rows_equal_the_full_evaluation(causal):
         Or, Lr = oracle.attention_block_sparse_rows(q, k, v, mask, 0.7, causal, b, h, rows, block=3)
         np.testing.assert_array_equal(Or, O[b, list(rows), h, :])
         np.testing.assert_array_equal(Lr, L[b, h, list(rows)])
+
+
+# ---------------------------------------------------------------------------
+# Gradients of the block-sparse attention (attention_backward with a mask)
+# ---------------------------------------------------------------------------
+BWD_CASES = [  # (B, Nq, Nk, Hq, Hkv, d, block, Hm, causal)
+    (1, 5, 7, 2, 1, 3, 2, 2, False),
+    (1, 6, 4, 2, 2, 2, 2, 1, True),   # Nq > Nk: rows above the first key
+    (2, 4, 6, 2, 1, 2, 3, 2, True),
+]
+
+
+def bs_loss(q, k, v, do, mask, scale, causal, block):
+    O, _ = oracle.attention_block_sparse(q, k, v, mask, scale, causal, block=block)
+    return float((O * do).sum())
+
+
+def bs_finite_difference(q, k, v, do, mask, scale, causal, block, eps=1e-6):
+    grads = []
+    for which in range(3):
+        args = [q.copy(), k.copy(), v.copy()]
+        x = args[which]
+        g = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + eps
+            lp = bs_loss(*args, do, mask, scale, causal, block)
+            x[idx] = x0 - eps
+            lm = bs_loss(*args, do, mask, scale, causal, block)
+            x[idx] = x0
+            g[idx] = (lp - lm) / (2 * eps)
+        grads.append(g)
+    return grads
+
+
+def bwd_case(case, seed):
+    B, Nq, Nk, Hq, Hkv, d, block, Hm, causal = case
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal(s) for s in ((B, Nq, Hq, d), (B, Nk, Hkv, d), (B, Nk, Hkv, d)))
+    do = rng.standard_normal((B, Nq, Hq, d))
+    mask = (rng.random((B, Hm, -(-Nq // block), -(-Nk // block))) < 0.6).astype(np.uint8)
+    mask[0, 0, 0, :] = 0  # a query block that keeps no key
+    return q, k, v, do, mask
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=str)
+def test_block_sparse_gradients_match_finite_differences(case):
+    q, k, v, do, mask = bwd_case(case, 91)
+    causal, block = case[-1], case[6]
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, 0.6, causal, block_mask=mask, block=block)
+    fq, fk, fv = bs_finite_difference(q, k, v, do, mask, float(np.float32(0.6)), causal, block)
+    for got, want in ((dq, fq), (dk, fk), (dv, fv)):
+        assert np.abs(got - want).max() <= 1e-7
+    assert (dq[0, :block, 0] == 0).all()  # rows that keep no key get no gradient
+
+
+def test_block_sparse_gradients_match_sdpa_autograd():
+    B, Nq, Nk, Hq, Hkv, d, block = 2, 9, 9, 4, 2, 5, 2
+    rng = np.random.default_rng(92)
+    q, k, v, do = (rng.standard_normal(s) for s in
+                   ((B, Nq, Hq, d), (B, Nk, Hkv, d), (B, Nk, Hkv, d), (B, Nq, Hq, d)))
+    mask = (rng.random((B, Hq, 5, 5)) < 0.5).astype(np.uint8)
+    mask[..., 0] = 1  # every row keeps a key (SDPA gives NaN for rows that keep none)
+    for causal in (False, True):
+        dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, 0.4, causal, block_mask=mask, block=block)
+        em = torch.tensor(mask).bool().repeat_interleave(block, 2)[:, :, :Nq].repeat_interleave(block, 3)[..., :Nk]
+        if causal:
+            em = em & torch.ones(Nq, Nk, dtype=torch.bool).tril(Nk - Nq)
+        t = [torch.tensor(x).transpose(1, 2).contiguous().requires_grad_(True) for x in (q, k, v)]
+        kt = t[1].repeat_interleave(Hq // Hkv, 1)
+        vt = t[2].repeat_interleave(Hq // Hkv, 1)
+        out = torch.nn.functional.scaled_dot_product_attention(t[0], kt, vt, attn_mask=em,
+                                                               scale=float(np.float32(0.4)))
+        out.backward(torch.tensor(do).transpose(1, 2))
+        for got, ref in zip((dq, dk, dv), t):
+            np.testing.assert_allclose(got, ref.grad.transpose(1, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_all_ones_mask_gives_the_dense_gradients():
+    rng = np.random.default_rng(93)
+    q, k, v, do = (rng.standard_normal(s) for s in ((1, 5, 2, 3), (1, 6, 1, 3), (1, 6, 1, 3), (1, 5, 2, 3)))
+    for causal in (False, True):
+        a = oracle.attention_backward(q, k, v, do, 0.5, causal, block_mask=np.ones((1, 1, 3, 3)), block=2)
+        b = oracle.attention_backward(q, k, v, do, 0.5, causal)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+
+
+def test_planted_mask_mistake_fails_the_gradient_pin():
+    case = BWD_CASES[0]
+    q, k, v, do, mask = bwd_case(case, 94)
+    mask[0, 1] = 1 - mask[0, 0]
+    wrong = np.roll(mask, 1, axis=3)
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, 0.6, False, block_mask=wrong, block=2)
+    fq, fk, fv = bs_finite_difference(q, k, v, do, mask, float(np.float32(0.6)), False, 2)
+    assert max(np.abs(dq - fq).max(), np.abs(dk - fk).max(), np.abs(dv - fv).max()) > 1e-3
