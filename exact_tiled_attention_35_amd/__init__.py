@@ -9,6 +9,8 @@ from .attention import (  # noqa: F401
     AttnError,
     attention,
     attn_bwd,
+    attn_bwd_blocksparse,
+    attn_bwd_blocksparse_ptr,
     attn_bwd_ptr,
     attn_decode,
     attn_decode_num_splits,

@@ -53,6 +53,8 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd_blocksparse.restype = ci
     lib.attn_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, ci, ci, cf, ci, ci, vp]
     lib.attn_bwd.restype = ci
+    lib.attn_bwd_blocksparse.argtypes = [vp] * 11 + [ci] * 7 + [cf, ci, ci, vp]
+    lib.attn_bwd_blocksparse.restype = ci
     lib.attn_decode.argtypes = [vp] * 9 + [ctypes.c_size_t] + [ci] * 7 + [cf, ci, ci, ci, vp]
     lib.attn_decode.restype = ci
     lib.attn_decode_num_splits.argtypes = [ci] * 6

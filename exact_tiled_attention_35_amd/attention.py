@@ -261,6 +261,50 @@ def attn_fwd_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, lse
 
 
+def attn_bwd_blocksparse_ptr(q: int, k: int, v: int, out: int, dout: int, lse: int, dq: int,
+                             dk: int, dv: int, delta: int, block_mask: int, mask_heads: int,
+                             B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, scale: float,
+                             causal: bool, dtype: int, stream: int = 0) -> int:
+    """The C entry point attn_bwd_blocksparse with raw integer pointers."""
+    return _lib.load().attn_bwd_blocksparse(
+        q or None, k or None, v or None, out or None, dout or None, lse or None, dq or None,
+        dk or None, dv or None, delta or None, block_mask or None, int(mask_heads), int(B),
+        int(Hq), int(Hkv), int(Nq), int(Nk), int(d), float(scale), int(bool(causal)), int(dtype),
+        stream or None)
+
+
+def attn_bwd_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                         dout: torch.Tensor, lse: torch.Tensor, block_mask: torch.Tensor,
+                         softmax_scale: float | None = None, causal: bool = False):
+    """Backward of ``attn_fwd_blocksparse``: ``out`` and ``lse`` as it returned
+    them for the same arguments and mask.  Returns (dq, dk, dv, delta)."""
+    B, Nq, Hq, Hkv, Nk, d = _check_qkv(q, k, v)
+    _check_like("out", out, q.shape, q.dtype, q.device)
+    _check_like("dout", dout, q.shape, q.dtype, q.device)
+    _check_like("lse", lse, (B, Hq, Nq), torch.float32, q.device)
+    nqb, nkb = -(-Nq // BLOCK_MASK_SIZE), -(-Nk // BLOCK_MASK_SIZE)
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.view(torch.uint8)
+    if block_mask.dim() != 4 or block_mask.shape[1] not in (1, Hq):
+        raise ValueError(f"block_mask must be [B, 1 or Hq, {nqb}, {nkb}]")
+    _check_like("block_mask", block_mask, (B, block_mask.shape[1], nqb, nkb), torch.uint8, q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        code = attn_bwd_blocksparse_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                                        dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                                        block_mask.data_ptr(), block_mask.shape[1], B, Hq, Hkv,
+                                        Nq, Nk, d, softmax_scale, causal, _DTYPE_CODE[q.dtype],
+                                        stream)
+    if code != _lib.ATTN_OK:
+        raise AttnError(code)
+    return dq, dk, dv, delta
+
+
 class _Attention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, softmax_scale, causal):

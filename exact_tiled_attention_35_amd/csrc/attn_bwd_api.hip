@@ -20,10 +20,11 @@ using eta_host::check_device;
 using eta_host::finite_bits;
 using eta_host::overlaps;
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool SPARSE>
 int launch_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
-               int Hkv, int Nq, int Nk, float scale, hipStream_t stream) {
+               int Hkv, int Nq, int Nk, float scale, const eta::BlockMaskArgs& bm,
+               hipStream_t stream) {
   using CQ = eta::DqCfg<D>;
   using CK = eta::DkvCfg<D>;
   const float c_log2 = scale * eta::kLog2e;
@@ -36,38 +37,55 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* out, con
   const auto* Vp = static_cast<const uint16_t*>(v);
   const auto* dO = static_cast<const uint16_t*>(dout);
   if (tq > 0) {
-    hipLaunchKernelGGL((eta::attn_bwd_dq_kernel<D, BF16, CAUSAL>), dim3((int)tq),
+    hipLaunchKernelGGL((eta::attn_bwd_dq_kernel<D, BF16, CAUSAL, SPARSE>), dim3((int)tq),
                        dim3(CQ::kThreads), 0, stream, Q, Kp, Vp, static_cast<const uint16_t*>(out),
                        dO, lse, static_cast<uint16_t*>(dq), delta, Hq, Hkv, Nq, Nk, nqb, (int)tq,
-                       scale, c_log2);
+                       scale, c_log2, bm);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
   }
-  hipLaunchKernelGGL((eta::attn_bwd_dkdv_kernel<D, BF16, CAUSAL>), dim3((int)tk),
+  hipLaunchKernelGGL((eta::attn_bwd_dkdv_kernel<D, BF16, CAUSAL, SPARSE>), dim3((int)tk),
                      dim3(CK::kThreads), 0, stream, Q, Kp, Vp, dO, lse, delta,
                      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), Hq, Hkv, Nq, Nk, nkb,
-                     (int)tk, scale, c_log2);
+                     (int)tk, scale, c_log2, bm);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-template <int D>
+template <int D, bool SPARSE>
 int dispatch_bwd(bool bf16, bool causal, const void* q, const void* k, const void* v,
                  const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
                  float* delta, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
-                 hipStream_t s) {
-#define ETA_BWD_ARGS q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, s
+                 const eta::BlockMaskArgs& bm, hipStream_t s) {
+#define ETA_BWD_ARGS q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s
   if (bf16) {
-    return causal ? launch_bwd<D, true, true>(ETA_BWD_ARGS) : launch_bwd<D, true, false>(ETA_BWD_ARGS);
+    return causal ? launch_bwd<D, true, true, SPARSE>(ETA_BWD_ARGS)
+                  : launch_bwd<D, true, false, SPARSE>(ETA_BWD_ARGS);
   }
-  return causal ? launch_bwd<D, false, true>(ETA_BWD_ARGS) : launch_bwd<D, false, false>(ETA_BWD_ARGS);
+  return causal ? launch_bwd<D, false, true, SPARSE>(ETA_BWD_ARGS)
+                : launch_bwd<D, false, false, SPARSE>(ETA_BWD_ARGS);
 #undef ETA_BWD_ARGS
 }
 
-}  // namespace
+template <bool SPARSE>
+int dispatch_hdim(int d, bool bf16, bool c, const void* q, const void* k, const void* v,
+                  const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                  float* delta, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
+                  const eta::BlockMaskArgs& bm, hipStream_t s) {
+  switch (d) {
+    case 64:
+      return dispatch_bwd<64, SPARSE>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s);
+    case 128:
+      return dispatch_bwd<128, SPARSE>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s);
+    default:
+      return dispatch_bwd<256, SPARSE>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s);
+  }
+}
 
-extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out,
-                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                        float* delta, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
-                        int causal, int dtype, void* stream) {
+// attn_bwd and attn_bwd_blocksparse: validation in the documented order,
+// then the plain kernels or (with a block mask) their block-sparse instances.
+int bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta,
+             const unsigned char* block_mask, int mask_heads, bool sparse, int B, int Hq, int Hkv,
+             int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream) {
   // 1. shape
   if (B < 0 || Nq < 0 || Hq < 1 || Hkv < 1 || Nk < 1 || d < 1) return ATTN_ERR_BAD_SHAPE;
   // 2. empty batch: nothing to do
@@ -85,11 +103,13 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   if (!k || !v || !dk || !dv) return ATTN_ERR_NULL_POINTER;
   const bool rows = Nq > 0;
   if (rows && (!q || !out || !dout || !lse || !dq || !delta)) return ATTN_ERR_NULL_POINTER;
+  if (sparse && rows && !block_mask) return ATTN_ERR_NULL_POINTER;
   // 4. GQA ratio, 5. head dimension, 6. element type, 7. scale
   if (Hq % Hkv != 0) return ATTN_ERR_GQA_RATIO;
   if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED_HDIM;
   if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
   if (!finite_bits(scale)) return ATTN_ERR_BAD_SCALE;
+  if (sparse && mask_heads != 1 && mask_heads != Hq) return ATTN_ERR_BAD_ARGUMENT;
   // 8. alignment
   if (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_MISALIGNED;
   if (rows && (!aligned16(q) || !aligned16(out) || !aligned16(dout) || !aligned16(lse) ||
@@ -98,13 +118,16 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   // 9. aliasing: no output overlaps an input or another output
   const size_t qb = rows ? (size_t)q_elems * 2 : 0, kvb = (size_t)kv_elems * 2;
   const size_t vb = rows ? (size_t)B * Hq * Nq * sizeof(float) : 0;
-  const void* in_p[6] = {q, k, v, out, dout, lse};
-  const size_t in_n[6] = {qb, kvb, kvb, qb, qb, vb};
+  const int nqbm = (Nq + eta::kMaskBlock - 1) / eta::kMaskBlock;
+  const int nkbm = (Nk + eta::kMaskBlock - 1) / eta::kMaskBlock;
+  const size_t mb = sparse && rows ? (size_t)B * mask_heads * nqbm * nkbm : 0;
+  const void* in_p[7] = {q, k, v, out, dout, lse, block_mask};
+  const size_t in_n[7] = {qb, kvb, kvb, qb, qb, vb, mb};
   const void* out_p[4] = {dq, dk, dv, delta};
   const size_t out_n[4] = {qb, kvb, kvb, vb};
   for (int i = 0; i < 4; ++i) {
     if (out_n[i] == 0) continue;
-    for (int j = 0; j < 6; ++j)
+    for (int j = 0; j < 7; ++j)
       if (in_n[j] && overlaps(out_p[i], out_n[i], in_p[j], in_n[j])) return ATTN_ERR_ALIASING;
     for (int j = i + 1; j < 4; ++j)
       if (out_n[j] && overlaps(out_p[i], out_n[i], out_p[j], out_n[j])) return ATTN_ERR_ALIASING;
@@ -116,12 +139,27 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   const bool bf16 = dtype == ATTN_DTYPE_BF16;
   const bool c = causal != 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (d) {
-    case 64:
-      return dispatch_bwd<64>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, s);
-    case 128:
-      return dispatch_bwd<128>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, s);
-    default:
-      return dispatch_bwd<256>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, s);
-  }
+  const eta::BlockMaskArgs bm{sparse && rows ? block_mask : nullptr, sparse ? mask_heads : 1, nkbm};
+  if (sparse)
+    return dispatch_hdim<true>(d, bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s);
+  return dispatch_hdim<false>(d, bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s);
+}
+
+}  // namespace
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        float* delta, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                        int causal, int dtype, void* stream) {
+  return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, delta, nullptr, 1, false, B, Hq, Hkv, Nq, Nk,
+                  d, scale, causal, dtype, stream);
+}
+
+extern "C" int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* out,
+                                    const void* dout, const float* lse, void* dq, void* dk,
+                                    void* dv, float* delta, const unsigned char* block_mask,
+                                    int mask_heads, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                    float scale, int causal, int dtype, void* stream) {
+  return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, delta, block_mask, mask_heads, true, B, Hq,
+                  Hkv, Nq, Nk, d, scale, causal, dtype, stream);
 }

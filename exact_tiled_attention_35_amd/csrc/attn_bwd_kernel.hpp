@@ -118,14 +118,15 @@ __device__ __forceinline__ void tile_issue(rsrc_t r, uint16_t* dst, int wave, co
 // ---------------------------------------------------------------------------
 // dQ (and D).
 // ---------------------------------------------------------------------------
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool SPARSE = false>
 __global__ void __launch_bounds__(DqCfg<D>::kThreads, DqCfg<D>::kMinWavesPerEU)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
                    const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
                    uint16_t* __restrict__ dQ, float* __restrict__ Dlt, int Hq, int Hkv, int Nq,
-                   int Nk, int nqb, int total, float scale, float c_log2) {
+                   int Nk, int nqb, int total, float scale, float c_log2, BlockMaskArgs bm) {
   using C = DqCfg<D>;
+  static_assert(kMaskBlock == C::BM && kMaskBlock % C::BN == 0, "a mask block is whole tiles");
   using L = typename C::L;
   constexpr int BN = C::BN, BM = C::BM, RS = L::RS, TS = L::TS;
   constexpr int NKS = D / 16, NKB = BN / 32, NDB = D / 32, NKK = BN / 16;
@@ -176,10 +177,44 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // Key range of the workgroup and of this wave.
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, min(q0 + BM, Nq) + diag);
-  const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   const int rows_end = min(qw0 + 32, Nq);
   int w_end = rows_end > qw0 ? Nk : 0;
   if (CAUSAL && rows_end > qw0) w_end = min(Nk, rows_end + diag);
+
+  // Block sparsity: the tiles of the flagged key blocks below kv_end, in key
+  // order, as in the forward (flags read 64 blocks per ballot; tiles of
+  // dropped blocks are never loaded).
+  constexpr int TPB = kMaskBlock / BN;
+  int sp_chunk = 0, sp_blk = 0, sp_sub = TPB, sp_nchunks = 0, sp_cur = 0;
+  uint64_t sp_bits = 0;
+  const int nkb_eff = kv_end > 0 ? (kv_end + kMaskBlock - 1) / kMaskBlock : 0;
+  const int64_t sp_row = ((int64_t)w.b * bm.heads + (bm.heads == 1 ? 0 : w.hq)) * nqb + w.qblk;
+  const rsrc_t sp_mr = make_rsrc(SPARSE ? bm.mask + sp_row * bm.nkb : nullptr, SPARSE ? nkb_eff : 0);
+  if constexpr (SPARSE) {
+    sp_nchunks = (nkb_eff + 63) / 64;
+    const int last = nkb_eff - 1;  // may hold fewer than TPB tiles
+    const int last_tiles = (kv_end - kMaskBlock * last + BN - 1) / BN;
+    int blocks = 0;
+    nt = 0;
+    for (int c = 0; c < sp_nchunks; ++c) {
+      const uint64_t bits = flag_word(sp_mr, c, 1, lane);
+      if (c == 0) sp_bits = bits;
+      blocks += __builtin_popcountll(bits);
+      if (last / 64 == c && ((bits >> (last % 64)) & 1)) nt -= TPB - last_tiles;
+    }
+    nt += TPB * blocks;
+  }
+  // Start of the next visited tile; called only while one is left.
+  auto sparse_next = [&]() -> int {
+    if (++sp_sub >= TPB) {
+      while (sp_bits == 0 && sp_chunk + 1 < sp_nchunks) sp_bits = flag_word(sp_mr, ++sp_chunk, 1, lane);
+      sp_blk = 64 * sp_chunk + (sp_bits ? __builtin_ctzll(sp_bits) : 0);
+      sp_bits &= sp_bits - 1;
+      sp_sub = 0;
+    }
+    return sp_blk * kMaskBlock + sp_sub * BN;
+  };
 
   int roff[kRowPW], toff[kTrPW];
   tile_offsets<BN, L::RCP, D>(wave, lane, kv_rs, roff);
@@ -201,13 +236,20 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
 
-  if (nt > 0) issue_tile(0, smem);
+  if constexpr (SPARSE) {
+    if (nt > 0) sp_cur = sparse_next();
+  }
+  if (nt > 0) issue_tile(SPARSE ? sp_cur : 0, smem);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < nt; ++t) {
-    const int j0 = t * BN;
-    if (t + 1 < nt) issue_tile(j0 + BN, smem + ((t + 1) & 1) * C::kStage);
+    const int j0 = SPARSE ? sp_cur : t * BN;
+    if (t + 1 < nt) {
+      int jn = j0 + BN;
+      if constexpr (SPARSE) jn = sp_cur = sparse_next();
+      issue_tile(jn, smem + ((t + 1) & 1) * C::kStage);
+    }
     const uint16_t* st = smem + (t & 1) * C::kStage;
     const uint16_t* krow = st;
     const uint16_t* ktr = st + C::kKRow;
@@ -320,14 +362,16 @@ __device__ __forceinline__ WorkItem map_key_block(int wg, int total, int nkb, in
   return w;
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool SPARSE = false>
 __global__ void __launch_bounds__(DkvCfg<D>::kThreads, DkvCfg<D>::kMinWavesPerEU)
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                      const float* __restrict__ LSE, const float* __restrict__ Dlt,
                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv,
-                     int Nq, int Nk, int nkb, int total, float scale, float c_log2) {
+                     int Nq, int Nk, int nkb, int total, float scale, float c_log2,
+                     BlockMaskArgs bm) {
   using C = DkvCfg<D>;
+  static_assert(kMaskBlock == C::BK && kMaskBlock % C::BQ == 0, "a mask block is whole tiles");
   using L = typename C::L;
   constexpr int BQ = C::BQ, BK = C::BK, RS = L::RS, TS = L::TS;
   constexpr int NKS = D / 16, NQB = BQ / 32, NDB = D / 32, NKK = BQ / 16;
@@ -365,7 +409,65 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   int qt_begin = 0;
   if (CAUSAL) qt_begin = min(nqt_all, max(0, k0 - diag) / BQ);
   const int nqt = nqt_all - qt_begin;
-  const int nsteps = (k0 < Nk) ? G * nqt : 0;
+  int nsteps = (k0 < Nk) ? G * nqt : 0;
+
+  // Block sparsity: for each query head of the group, the query tiles of the
+  // query blocks whose flag with this key block is set (a column of the
+  // mask: stride nkb bytes), within [qt_begin, nqt_all), head by head in
+  // block order -- the plain kernel's step order with dropped steps left out.
+  constexpr int TPQ = kMaskBlock / BQ;  // query tiles per mask block
+  const int nqbm = (Nq + kMaskBlock - 1) / kMaskBlock;
+  const int qb_lo = qt_begin / TPQ, qb_hi = (nqt_all - 1) / TPQ;
+  const int c_lo = qb_lo / 64, c_hi = max(qb_hi, 0) / 64;
+  auto column = [&](int gi) {
+    const int hm = bm.heads == 1 ? 0 : w.hq * G + gi;
+    const int64_t base = ((int64_t)w.b * bm.heads + hm) * nqbm * bm.nkb + w.qblk;
+    return make_rsrc(SPARSE ? bm.mask + base : nullptr, SPARSE && nqbm > 0 ? (nqbm - 1) * bm.nkb + 1 : 0);
+  };
+  // flags of query blocks [64 c, 64 c + 64) of head gi, limited to [qb_lo, qb_hi]
+  auto range_word = [&](const rsrc_t& col, int c) -> uint64_t {
+    uint64_t bits = flag_word(col, c, bm.nkb, lane);
+    if (c == c_lo) bits &= ~0ull << (qb_lo % 64);
+    if (c == c_hi && qb_hi % 64 != 63) bits &= (1ull << (qb_hi % 64 + 1)) - 1;
+    return bits;
+  };
+  int sp_gi = 0, sp_chunk = c_lo, sp_qt = 0, sp_qt_end = 0, sp_h = 0, sp_i0 = 0;
+  uint64_t sp_bits = 0;
+  rsrc_t sp_col = column(0);
+  if constexpr (SPARSE) {
+    nsteps = 0;
+    if (k0 < Nk && nqt > 0) {
+      for (int gi = 0; gi < G; ++gi) {
+        const rsrc_t col = column(gi);
+        for (int c = c_lo; c <= c_hi; ++c) {
+          const uint64_t bits = range_word(col, c);
+          if (gi == 0 && c == c_lo) sp_bits = bits;
+          nsteps += TPQ * __builtin_popcountll(bits);
+          if (qb_lo / 64 == c && ((bits >> (qb_lo % 64)) & 1)) nsteps -= qt_begin - TPQ * qb_lo;
+          if (qb_hi / 64 == c && ((bits >> (qb_hi % 64)) & 1)) nsteps -= TPQ * qb_hi + TPQ - nqt_all;
+        }
+      }
+    }
+  }
+  // The next visited step (head and query tile); called only while one is left.
+  auto sparse_next = [&]() {
+    if (++sp_qt >= sp_qt_end) {
+      for (int guard = 0; sp_bits == 0 && guard < G * (c_hi - c_lo + 1); ++guard) {
+        if (++sp_chunk > c_hi) {
+          sp_chunk = c_lo;
+          if (++sp_gi >= G) sp_gi = G - 1;
+          sp_col = column(sp_gi);
+        }
+        sp_bits = range_word(sp_col, sp_chunk);
+      }
+      const int qb = 64 * sp_chunk + (sp_bits ? __builtin_ctzll(sp_bits) : qb_lo % 64);
+      sp_bits &= sp_bits - 1;
+      sp_qt = max(TPQ * qb, qt_begin);
+      sp_qt_end = min(TPQ * qb + TPQ, nqt_all);
+    }
+    sp_h = w.hq * G + sp_gi;
+    sp_i0 = sp_qt * BQ;
+  };
   // First query row this wave's keys see (causal), for skipping whole tiles.
   const int w_first = CAUSAL ? kw0 - diag : -(1 << 30);
   const bool w_live = kw0 < Nk;
@@ -376,8 +478,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // Step s: query head hq = hkv*G + s / nqt, query tile qt_begin + s % nqt.
   auto step_rows = [&](int s) { return (qt_begin + s % nqt) * BQ; };
   auto issue_step = [&](int s, uint16_t* st) {
-    const int h = w.hq * G + s / nqt;
-    const int i0 = step_rows(s);
+    const int h = SPARSE ? sp_h : w.hq * G + s / nqt;
+    const int i0 = SPARSE ? sp_i0 : step_rows(s);
     const int64_t off = ((int64_t)w.b * Nq + i0) * q_rs + (int64_t)h * D;
     const int bytes = span_bytes(i0, BQ, Nq, q_rs, D);
     const rsrc_t qs = make_rsrc(Q + off, bytes);
@@ -402,12 +504,19 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16_t{};
 
+  if constexpr (SPARSE) {
+    if (nsteps > 0) sparse_next();
+  }
   if (nsteps > 0) issue_step(0, smem);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int s = 0; s < nsteps; ++s) {
-    if (s + 1 < nsteps) issue_step(s + 1, smem + ((s + 1) & 1) * C::kStage);
+    const int cur_i0 = SPARSE ? sp_i0 : step_rows(s);
+    if (s + 1 < nsteps) {
+      if constexpr (SPARSE) sparse_next();
+      issue_step(s + 1, smem + ((s + 1) & 1) * C::kStage);
+    }
     const uint16_t* st = smem + (s & 1) * C::kStage;
     const uint16_t* qrow = st;
     const uint16_t* drow = st + C::kRow;
@@ -415,7 +524,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const uint16_t* dtr = st + 2 * C::kRow + C::kTr;
     const float* lse_t = reinterpret_cast<const float*>(st + 2 * C::kRow + 2 * C::kTr);
     const float* dlt_t = lse_t + C::kVec / 2;
-    const int i0 = step_rows(s);
+    const int i0 = cur_i0;
 
     if (w_live && i0 + BQ - 1 >= w_first) {  // wave-uniform: some pair visible
       f32x16_t sc[NQB], dp[NQB];

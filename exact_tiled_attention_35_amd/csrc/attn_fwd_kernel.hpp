@@ -136,17 +136,6 @@ struct VarlenArgs {
   int pairs;  // sequences x query heads
 };
 
-// Block sparsity: flags over (query block, key block) pairs of 128 x 128
-// decide which blocks of the score matrix take part; key j is visible to row
-// i only if the flag of (i / 128, j / 128) is nonzero (and causally, when
-// causal).  mask is [B, heads, ceil(Nq / 128), nkb] bytes with heads = 1
-// (shared by all query heads) or Hq; nkb = ceil(Nk / 128).
-constexpr int kMaskBlock = 128;
-struct BlockMaskArgs {
-  const uint8_t* mask;
-  int heads, nkb;
-};
-
 template <int D, bool BF16, bool CAUSAL, bool MODS = false, bool VARLEN = false, bool SPARSE = false>
 __global__ void __launch_bounds__(TileCfg<D>::kThreads, TileCfg<D>::kMinWavesPerEU)
 attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -265,8 +254,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     int blocks = 0, nf_blocks = 0;
     nt = 0;
     for (int c = 0; c < sp_nchunks; ++c) {
-      const uint64_t bits = __builtin_amdgcn_ballot_w64(
-          __builtin_amdgcn_raw_buffer_load_b8(sp_mr, 64 * c + lane, 0, 0) != 0);
+      const uint64_t bits = flag_word(sp_mr, c, 1, lane);
       if (c == 0) sp_bits = bits;
       blocks += __builtin_popcountll(bits);
       const int below = full_blocks - 64 * c;  // blocks of this chunk under full_blocks
@@ -284,8 +272,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (++sp_sub >= TPB) {
       while (sp_bits == 0 && sp_chunk + 1 < sp_nchunks) {
         ++sp_chunk;
-        sp_bits = __builtin_amdgcn_ballot_w64(
-            __builtin_amdgcn_raw_buffer_load_b8(sp_mr, 64 * sp_chunk + lane, 0, 0) != 0);
+        sp_bits = flag_word(sp_mr, sp_chunk, 1, lane);
       }
       sp_blk = 64 * sp_chunk + (sp_bits ? __builtin_ctzll(sp_bits) : 0);
       sp_bits &= sp_bits - 1;

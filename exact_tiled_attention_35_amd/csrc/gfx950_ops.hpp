@@ -110,6 +110,26 @@ __device__ __forceinline__ u32x2_t lds_read_tr4(const uint16_t* p) {
       u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p));
 }
 
+// Block sparsity: flags over (query block, key block) pairs of 128 x 128
+// decide which blocks of the score matrix take part; key j is visible to row
+// i only if the flag of (i / 128, j / 128) is nonzero (and causally, when
+// causal).  mask is [B, heads, ceil(Nq / 128), nkb] bytes with heads = 1
+// (shared by all query heads) or Hq; nkb = ceil(Nk / 128).
+constexpr int kMaskBlock = 128;
+struct BlockMaskArgs {
+  const uint8_t* mask;
+  int heads, nkb;
+};
+
+// 64 flags of one line of the mask (a row of key blocks, stride 1 byte, or
+// a column of query blocks, stride nkb bytes) as one wave-uniform word: lane
+// i loads flag 64 c + i through a descriptor whose range ends after the
+// line's last flag (flags past it read as 0), and a ballot gathers them.
+__device__ __forceinline__ uint64_t flag_word(rsrc_t r, int c, int stride, int lane) {
+  return __builtin_amdgcn_ballot_w64(
+      __builtin_amdgcn_raw_buffer_load_b8(r, (64 * c + lane) * stride, 0, 0) != 0);
+}
+
 // Bytes from row r0 to the end of the last valid row of a [rows, D] window
 // of a tensor with row stride rs (elements), given N valid rows in total.
 __device__ __forceinline__ int span_bytes(int r0, int rows, int N, int64_t rs, int D) {

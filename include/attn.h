@@ -197,6 +197,26 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              float scale, int causal, int dtype, void* stream);
 
 /*
+ * attn_bwd for attn_fwd_blocksparse: gradients of L = sum(dout * out) for
+ * out = attn_fwd_blocksparse(q, k, v, block_mask, mask_heads, scale, causal)
+ * (P is that function's probability matrix: zero outside the kept blocks).
+ * The pages' FlexAttention item notes that its backward is not deterministic
+ * with block sparsity enabled; this one, like attn_bwd, uses no atomics and
+ * is bitwise reproducible.  Blocks whose flag is 0 are never read.
+ *   block_mask, mask_heads  as for attn_fwd_blocksparse (may be NULL when
+ *                           Nq == 0)
+ * The other arguments, layouts and the validation order are attn_bwd's, with
+ * ATTN_ERR_NULL_POINTER also for a NULL block_mask (Nq > 0),
+ * ATTN_ERR_BAD_ARGUMENT when mask_heads is neither 1 nor Hq (checked after
+ * the scale), and ATTN_ERR_ALIASING also when an output overlaps the mask.
+ */
+int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         float* delta, const unsigned char* block_mask, int mask_heads,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                         float scale, int causal, int dtype, void* stream);
+
+/*
  * KV-cache decode forward: new query rows against a key/value cache that is
  * updated in place, as the interface section of the hysenlabs.com page
  * describes the inference function ("Die Schnittstellen von flash_attn_func
