@@ -325,11 +325,13 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
-    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "varlen", "blocksparse"), default="fwd",
+    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "varlen", "blocksparse", "blocksparse_bwd"),
+                    default="fwd",
                     help="fwd: attn_fwd (the headline metric); bwd: attn_bwd, the backward pass; "
                          "decode: attn_decode on a KV-cache decode workload; varlen: "
                          "attn_fwd_varlen on packed variable-length sequences; blocksparse: "
-                         "attn_fwd_blocksparse with a random block mask")
+                         "attn_fwd_blocksparse with a random block mask; blocksparse_bwd: "
+                         "attn_bwd_blocksparse on the same workloads")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--window", nargs=2, type=int, default=(-1, -1), metavar=("LEFT", "RIGHT"),
                     help="fwd only: sliding window (attn_fwd_ext); flops count the kept pairs")
@@ -374,13 +376,14 @@ def main():
             log("no GPU visible")
             sys.exit(1)
         return bench_varlen(args, VARLEN_WORKLOADS[args.workload or next(iter(VARLEN_WORKLOADS))])
-    if args.op == "blocksparse":
+    if args.op in ("blocksparse", "blocksparse_bwd"):
         from attn_workloads import BLOCKSPARSE_WORKLOADS
 
         if not torch.cuda.is_available():
             log("no GPU visible")
             sys.exit(1)
-        return bench_blocksparse(args, args.workload or next(iter(BLOCKSPARSE_WORKLOADS)))
+        return bench_blocksparse(args, args.workload or next(iter(BLOCKSPARSE_WORKLOADS)),
+                                 backward=args.op == "blocksparse_bwd")
     if args.op == "decode":
         w = DECODE_WORKLOADS[args.workload or next(iter(DECODE_WORKLOADS))]
     else:
@@ -813,14 +816,16 @@ def cpu_baseline_blocksparse(w, q, k, v, mask, counts, budget_s: float):
     }
 
 
-def bench_blocksparse(args, name):
-    """One step = one attn_fwd_blocksparse call; flops count 4*d per kept
-    (query, key) pair and head (the mask's kept blocks, with the causal bound
-    inside them)."""
+def bench_blocksparse(args, name, backward=False):
+    """One step = one attn_fwd_blocksparse call (or, ``backward``, one
+    attn_bwd_blocksparse call from the forward's out and lse with a seeded
+    dout); flops count 4*d (backward: 10*d) per kept (query, key) pair and
+    head (the mask's kept blocks, with the causal bound inside them)."""
     import torch
 
-    from attn_workloads import BLOCK, BLOCKSPARSE_WORKLOADS, WORKLOADS, make_block_mask, make_workload
-    from exact_tiled_attention_35_amd import attn_fwd_blocksparse, attn_version
+    from attn_workloads import (BLOCK, BLOCKSPARSE_WORKLOADS, WORKLOADS, make_block_mask, make_qkv,
+                                make_workload)
+    from exact_tiled_attention_35_amd import attn_bwd_blocksparse, attn_fwd_blocksparse, attn_version
 
     spec = BLOCKSPARSE_WORKLOADS[name]
     w = WORKLOADS[spec["base"]]
@@ -837,6 +842,13 @@ def bench_blocksparse(args, name):
 
     def step():
         attn_fwd_blocksparse(gq, gk, gv, gm, w.scale, w.causal, out=out, lse=lse)
+
+    if backward:
+        step()
+        gdo = make_qkv(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.dtype, w.sigma, w.seed + 100)[0].to(dev)
+
+        def step():  # noqa: F811
+            attn_bwd_blocksparse(gq, gk, gv, out, gdo, lse, gm, w.scale, w.causal)
 
     for _ in range(args.warmup):
         step()
@@ -857,7 +869,7 @@ def bench_blocksparse(args, name):
     counts = blocksparse_pair_counts(w.Nq, w.Nk, w.causal, BLOCK)
     kept_blocks = mask.numpy() != 0
     pairs = float((kept_blocks * counts[None, None]).sum())
-    F = 4.0 * w.d * pairs
+    F = (10.0 if backward else 4.0) * w.d * pairs
     value = F / (wall / K) / 1e12
     achieved = F / avg_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -866,7 +878,9 @@ def bench_blocksparse(args, name):
         f"of peak; kept block pairs {kept_blocks.mean():.3f}, kept (query, key) pairs "
         f"{pairs / (w.B * w.Hq * w.Nq * w.Nk):.3f}")
     result = {
-        "metric": "attention fwd TFLOP/s with a block mask (4*d per kept (query, key) pair and head)",
+        "metric": ("attention bwd TFLOP/s with a block mask (10*d per kept (query, key) pair and head)"
+                   if backward else
+                   "attention fwd TFLOP/s with a block mask (4*d per kept (query, key) pair and head)"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -895,9 +909,10 @@ def bench_blocksparse(args, name):
             "kernel_avg_us": round(avg_s * 1e6, 2),
         },
         "cpu_baseline": None,
-        "context": "block-sparse forward; the headline metric is the plain forward (--op fwd)",
+        "context": ("block-sparse backward (the dQ and dK/dV kernels)" if backward else
+                    "block-sparse forward") + "; the headline metric is the plain forward (--op fwd)",
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not backward:
         del gq, gk, gv
         result["cpu_baseline"] = cpu_baseline_blocksparse(w, q, k, v, mask, counts, args.cpu_budget)
     print(json.dumps(result), flush=True)
