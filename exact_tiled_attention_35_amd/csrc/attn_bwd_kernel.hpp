@@ -425,22 +425,20 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     return make_rsrc(SPARSE ? bm.mask + base : nullptr, SPARSE && nqbm > 0 ? (nqbm - 1) * bm.nkb + 1 : 0);
   };
   // flags of query blocks [64 c, 64 c + 64) of head gi, limited to [qb_lo, qb_hi]
-  auto range_word = [&](const rsrc_t& col, int c) -> uint64_t {
-    uint64_t bits = flag_word(col, c, bm.nkb, lane);
+  auto range_word = [&](int gi, int c) -> uint64_t {
+    uint64_t bits = flag_word(column(gi), c, bm.nkb, lane);
     if (c == c_lo) bits &= ~0ull << (qb_lo % 64);
     if (c == c_hi && qb_hi % 64 != 63) bits &= (1ull << (qb_hi % 64 + 1)) - 1;
     return bits;
   };
   int sp_gi = 0, sp_chunk = c_lo, sp_qt = 0, sp_qt_end = 0, sp_h = 0, sp_i0 = 0;
   uint64_t sp_bits = 0;
-  rsrc_t sp_col = column(0);
   if constexpr (SPARSE) {
     nsteps = 0;
     if (k0 < Nk && nqt > 0) {
       for (int gi = 0; gi < G; ++gi) {
-        const rsrc_t col = column(gi);
         for (int c = c_lo; c <= c_hi; ++c) {
-          const uint64_t bits = range_word(col, c);
+          const uint64_t bits = range_word(gi, c);
           if (gi == 0 && c == c_lo) sp_bits = bits;
           nsteps += TPQ * __builtin_popcountll(bits);
           if (qb_lo / 64 == c && ((bits >> (qb_lo % 64)) & 1)) nsteps -= qt_begin - TPQ * qb_lo;
@@ -456,9 +454,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         if (++sp_chunk > c_hi) {
           sp_chunk = c_lo;
           if (++sp_gi >= G) sp_gi = G - 1;
-          sp_col = column(sp_gi);
         }
-        sp_bits = range_word(sp_col, sp_chunk);
+        sp_bits = range_word(sp_gi, sp_chunk);
       }
       const int qb = 64 * sp_chunk + (sp_bits ? __builtin_ctzll(sp_bits) : qb_lo % 64);
       sp_bits &= sp_bits - 1;
