@@ -17,6 +17,7 @@ from .exact import (  # noqa: F401
     attention,
     attention_backward,
     attention_varlen,
+    attention_backward_varlen,
     attention_block_sparse,
     attention_block_sparse_rows,
     attention_rows,

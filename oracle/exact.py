@@ -76,6 +76,7 @@ __all__ = [
     "attention_rows",
     "attention_backward",
     "attention_varlen",
+    "attention_backward_varlen",
     "attention_block_sparse",
     "attention_block_sparse_rows",
     "kv_head_of",
@@ -364,6 +365,33 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
         O[qs:qe] = Ob[0]
         lse[:, qs:qe] = Lb[0]
     return O, lse
+
+
+def attention_backward_varlen(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, scale: float,
+                              causal: bool = False):
+    """Gradients of L = sum(dout * attention_varlen(...)) in fp64: sequence by
+    sequence, ``attention_backward`` on that sequence's rows (the sequences
+    share no rows, so their gradients do not interact).  Key rows of a
+    sequence without query rows, and query rows of a sequence without keys,
+    get zero gradients.
+
+    Returns (dq [total_q, Hq, d], dk, dv [total_k, Hkv, d], delta [Hq, total_q]).
+    """
+    q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    cq = [int(x) for x in np.asarray(cu_seqlens_q).reshape(-1)]
+    ck = [int(x) for x in np.asarray(cu_seqlens_k).reshape(-1)]
+    total_q, Hq, d = q.shape
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    delta = np.zeros((Hq, total_q))
+    for b in range(len(cq) - 1):
+        qs, qe, ks, ke = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if qe <= qs or ke <= ks:
+            continue
+        g = attention_backward(q[None, qs:qe], k[None, ks:ke], v[None, ks:ke], dout[None, qs:qe],
+                               scale, causal)
+        dq[qs:qe], dk[ks:ke], dv[ks:ke] = g[0][0], g[1][0], g[2][0]
+        delta[:, qs:qe] = g[3][0]
+    return dq, dk, dv, delta
 
 
 def attention_block_sparse_rows(q, k, v, block_mask, scale: float, causal: bool, b: int, h: int,

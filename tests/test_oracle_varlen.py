@@ -116,3 +116,52 @@ def test_varlen_is_document_masked_attention(causal):
         np.testing.assert_allclose(O[:, h, :], ref, rtol=0, atol=1e-12)
         np.testing.assert_allclose(L[h], (mx[:, 0] + np.log(w.sum(axis=1))), rtol=0, atol=1e-12)
     assert T == int(cu[-1])
+
+
+# ---------------------------------------------------------------------------
+# Gradients over packed sequences (attention_backward_varlen)
+# ---------------------------------------------------------------------------
+def varlen_loss(q, k, v, do, cu_q, cu_k, scale, causal):
+    O, _ = oracle.attention_varlen(q, k, v, cu_q, cu_k, scale, causal)
+    return float((O * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_gradients_match_finite_differences(causal):
+    # sequences with and without query rows / keys, Nq != Nk per sequence
+    lens_q, lens_k = [2, 0, 3, 1], [3, 2, 2, 0]
+    rng = np.random.default_rng(101)
+    tq, tk, Hq, Hkv, d = sum(lens_q), sum(lens_k), 2, 1, 2
+    q, do = rng.standard_normal((tq, Hq, d)), rng.standard_normal((tq, Hq, d))
+    k, v = rng.standard_normal((tk, Hkv, d)), rng.standard_normal((tk, Hkv, d))
+    cu_q, cu_k = np.cumsum([0] + lens_q), np.cumsum([0] + lens_k)
+    dq, dk, dv, _ = oracle.attention_backward_varlen(q, k, v, do, cu_q, cu_k, 0.8, causal)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + eps
+            lp = varlen_loss(q, k, v, do, cu_q, cu_k, float(np.float32(0.8)), causal)
+            x[idx] = x0 - eps
+            lm = varlen_loss(q, k, v, do, cu_q, cu_k, float(np.float32(0.8)), causal)
+            x[idx] = x0
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert np.abs(g - fd).max() <= 1e-7
+    # the sequence without keys gets no query gradient; keys of the sequence
+    # without query rows get none either
+    assert (dq[5] == 0).all() and (dk[3:5] == 0).all() and (dv[3:5] == 0).all()
+
+
+def test_varlen_gradients_equal_the_batched_ones_for_equal_lengths():
+    B, N, Hq, Hkv, d = 3, 5, 4, 2, 3
+    q, k, v, cu_q, cu_k = make_varlen([N] * B, [N] * B, Hq, Hkv, d, seed=102)
+    do = make_varlen([N] * B, [N] * B, Hq, Hkv, d, seed=103)[0]
+    for causal in (False, True):
+        a = oracle.attention_backward_varlen(q, k, v, do, cu_q, cu_k, 0.3, causal)
+        b = oracle.attention_backward(q.reshape(B, N, Hq, d), k.reshape(B, N, Hkv, d),
+                                      v.reshape(B, N, Hkv, d), do.reshape(B, N, Hq, d), 0.3, causal)
+        np.testing.assert_allclose(a[0], b[0].reshape(B * N, Hq, d), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(a[1], b[1].reshape(B * N, Hkv, d), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(a[2], b[2].reshape(B * N, Hkv, d), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(a[3], b[3].transpose(1, 0, 2).reshape(Hq, B * N), rtol=0, atol=1e-14)
