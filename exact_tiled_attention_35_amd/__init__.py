@@ -12,6 +12,8 @@ from .attention import (  # noqa: F401
     attn_bwd_blocksparse,
     attn_bwd_blocksparse_ptr,
     attn_bwd_ptr,
+    attn_bwd_varlen,
+    attn_bwd_varlen_ptr,
     attn_decode,
     attn_decode_num_splits,
     attn_decode_ptr,

@@ -305,6 +305,59 @@ def attn_bwd_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out:
     return dq, dk, dv, delta
 
 
+def attn_bwd_varlen_ptr(q: int, k: int, v: int, out: int, dout: int, lse: int, dq: int, dk: int,
+                        dv: int, delta: int, cu_q: int, cu_k: int, B: int, Hq: int, Hkv: int,
+                        total_q: int, total_k: int, max_seqlen_q: int, max_seqlen_k: int, d: int,
+                        scale: float, causal: bool, dtype: int, stream: int = 0) -> int:
+    """The C entry point attn_bwd_varlen with raw integer pointers."""
+    return _lib.load().attn_bwd_varlen(
+        q or None, k or None, v or None, out or None, dout or None, lse or None, dq or None,
+        dk or None, dv or None, delta or None, cu_q or None, cu_k or None, int(B), int(Hq),
+        int(Hkv), int(total_q), int(total_k), int(max_seqlen_q), int(max_seqlen_k), int(d),
+        float(scale), int(bool(causal)), int(dtype), stream or None)
+
+
+def attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                    dout: torch.Tensor, lse: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                    cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                    softmax_scale: float | None = None, causal: bool = False):
+    """Backward of ``attn_fwd_varlen``: q, out, dout [total_q, Hq, d]; k, v
+    [total_k, Hkv, d]; lse [Hq, total_q] as the forward returned it.
+    Returns (dq, dk, dv, delta [Hq, total_q])."""
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D [total, H, d]")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk_ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or dk_ != d:
+        raise ValueError("k and v must be [total_k, Hkv, d] with q's d")
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, bf16 or fp16")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on q's HIP device")
+    _check_like("out", out, q.shape, q.dtype, q.device)
+    _check_like("dout", dout, q.shape, q.dtype, q.device)
+    _check_like("lse", lse, (Hq, total_q), torch.float32, q.device)
+    B = cu_seqlens_q.numel() - 1
+    _check_like("cu_seqlens_q", cu_seqlens_q, (B + 1,), torch.int32, q.device)
+    _check_like("cu_seqlens_k", cu_seqlens_k, (B + 1,), torch.int32, q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        code = attn_bwd_varlen_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), delta.data_ptr(), cu_seqlens_q.data_ptr(),
+                                   cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q, total_k,
+                                   max_seqlen_q, max_seqlen_k, d, softmax_scale, causal,
+                                   _DTYPE_CODE[q.dtype], stream)
+    if code != _lib.ATTN_OK:
+        raise AttnError(code)
+    return dq, dk, dv, delta
+
+
 class _Attention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, softmax_scale, causal):

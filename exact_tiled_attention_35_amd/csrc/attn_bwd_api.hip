@@ -40,14 +40,55 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* out, con
     hipLaunchKernelGGL((eta::attn_bwd_dq_kernel<D, BF16, CAUSAL, SPARSE>), dim3((int)tq),
                        dim3(CQ::kThreads), 0, stream, Q, Kp, Vp, static_cast<const uint16_t*>(out),
                        dO, lse, static_cast<uint16_t*>(dq), delta, Hq, Hkv, Nq, Nk, nqb, (int)tq,
-                       scale, c_log2, bm);
+                       scale, c_log2, bm, eta::VarlenArgs{nullptr, nullptr, 0, 0, 0});
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
   }
   hipLaunchKernelGGL((eta::attn_bwd_dkdv_kernel<D, BF16, CAUSAL, SPARSE>), dim3((int)tk),
                      dim3(CK::kThreads), 0, stream, Q, Kp, Vp, dO, lse, delta,
                      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), Hq, Hkv, Nq, Nk, nkb,
-                     (int)tk, scale, c_log2, bm);
+                     (int)tk, scale, c_log2, bm, eta::VarlenArgs{nullptr, nullptr, 0, 0, 0});
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+// Packed sequences: one dQ workgroup per (sequence, query head, 128 query
+// rows of the longest query sequence), one dK/dV workgroup per (sequence,
+// KV head, 128 keys of the longest key sequence); workgroups past their
+// sequence's end exit at once.
+template <int D, bool BF16, bool CAUSAL>
+int launch_bwd_varlen(const void* q, const void* k, const void* v, const void* out,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      float* delta, const int* cu_q, const int* cu_k, int B, int Hq, int Hkv,
+                      int total_q, int total_k, int max_q, int max_k, float scale,
+                      hipStream_t stream) {
+  using CQ = eta::DqCfg<D>;
+  using CK = eta::DkvCfg<D>;
+  const float c_log2 = scale * eta::kLog2e;
+  const int nqb = (max_q + CQ::BM - 1) / CQ::BM;
+  const int nkb = (max_k + CK::BK - 1) / CK::BK;
+  const int64_t tq = (int64_t)B * Hq * nqb, tk = (int64_t)B * Hkv * nkb;
+  if (tq > 0x7fffffff || tk > 0x7fffffff) return ATTN_ERR_BAD_SHAPE;
+  const auto* Q = static_cast<const uint16_t*>(q);
+  const auto* Kp = static_cast<const uint16_t*>(k);
+  const auto* Vp = static_cast<const uint16_t*>(v);
+  const auto* dO = static_cast<const uint16_t*>(dout);
+  const eta::BlockMaskArgs nb{nullptr, 1, 0};
+  if (tq > 0) {
+    const eta::VarlenArgs va{cu_q, cu_k, total_q, total_k, B * Hq};
+    hipLaunchKernelGGL((eta::attn_bwd_dq_kernel<D, BF16, CAUSAL, false, true>), dim3((int)tq),
+                       dim3(CQ::kThreads), 0, stream, Q, Kp, Vp, static_cast<const uint16_t*>(out),
+                       dO, lse, static_cast<uint16_t*>(dq), delta, Hq, Hkv, max_q, max_k, nqb,
+                       (int)tq, scale, c_log2, nb, va);
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+  }
+  if (tk > 0) {
+    const eta::VarlenArgs va{cu_q, cu_k, total_q, total_k, B * Hkv};
+    hipLaunchKernelGGL((eta::attn_bwd_dkdv_kernel<D, BF16, CAUSAL, false, true>), dim3((int)tk),
+                       dim3(CK::kThreads), 0, stream, Q, Kp, Vp, dO, lse, delta,
+                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), Hq, Hkv, max_q,
+                       max_k, nkb, (int)tk, scale, c_log2, nb, va);
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
 }
 
 template <int D, bool SPARSE>
@@ -162,4 +203,78 @@ extern "C" int attn_bwd_blocksparse(const void* q, const void* k, const void* v,
                                     float scale, int causal, int dtype, void* stream) {
   return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, delta, block_mask, mask_heads, true, B, Hq,
                   Hkv, Nq, Nk, d, scale, causal, dtype, stream);
+}
+
+extern "C" int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* out,
+                               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                               float* delta, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                               int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                               int max_seqlen_k, int d, float scale, int causal, int dtype,
+                               void* stream) {
+  // 1. shape
+  if (B < 0 || Hq < 1 || Hkv < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 ||
+      max_seqlen_k < 0 || d < 1)
+    return ATTN_ERR_BAD_SHAPE;
+  // 2. nothing to do
+  if (B == 0 || (total_q == 0 && total_k == 0)) return ATTN_OK;
+  const double q_elems = (double)total_q * Hq * d, kv_elems = (double)total_k * Hkv * d;
+  if (q_elems > 0x1p60 || kv_elems > 0x1p60) return ATTN_ERR_BAD_SHAPE;
+  if ((double)128 * Hq * d * 2 >= 0x1p31 || (double)128 * Hkv * d * 2 >= 0x1p31)
+    return ATTN_ERR_BAD_SHAPE;
+  if ((double)B * Hq * ((max_seqlen_q + 127) / 128) > 0x7fffffff ||
+      (double)B * Hkv * ((max_seqlen_k + 127) / 128) > 0x7fffffff)
+    return ATTN_ERR_BAD_SHAPE;
+  // 3. null pointers: the row buffers of whichever side has rows
+  const bool qrows = total_q > 0, krows = total_k > 0;
+  if (!cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL_POINTER;
+  if (qrows && (!q || !out || !dout || !lse || !dq || !delta)) return ATTN_ERR_NULL_POINTER;
+  if (krows && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL_POINTER;
+  // 4-7. GQA ratio, head dimension, element type, scale
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA_RATIO;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED_HDIM;
+  if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
+  if (!finite_bits(scale)) return ATTN_ERR_BAD_SCALE;
+  // 8. alignment
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3))
+    return ATTN_ERR_MISALIGNED;
+  if (qrows && (!aligned16(q) || !aligned16(out) || !aligned16(dout) || !aligned16(lse) ||
+                !aligned16(dq) || !aligned16(delta)))
+    return ATTN_ERR_MISALIGNED;
+  if (krows && (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv)))
+    return ATTN_ERR_MISALIGNED;
+  // 9. aliasing: no output overlaps an input or another output
+  const size_t qb = (size_t)q_elems * 2, kvb = (size_t)kv_elems * 2;
+  const size_t vb = (size_t)Hq * total_q * sizeof(float), cb = (size_t)(B + 1) * 4;
+  const void* in_p[8] = {q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k};
+  const size_t in_n[8] = {qb, kvb, kvb, qb, qb, vb, cb, cb};
+  const void* out_p[4] = {dq, dk, dv, delta};
+  const size_t out_n[4] = {qb, kvb, kvb, vb};
+  for (int i = 0; i < 4; ++i) {
+    if (out_n[i] == 0 || !out_p[i]) continue;
+    for (int j = 0; j < 8; ++j)
+      if (in_n[j] && in_p[j] && overlaps(out_p[i], out_n[i], in_p[j], in_n[j])) return ATTN_ERR_ALIASING;
+    for (int j = i + 1; j < 4; ++j)
+      if (out_n[j] && out_p[j] && overlaps(out_p[i], out_n[i], out_p[j], out_n[j]))
+        return ATTN_ERR_ALIASING;
+  }
+  // 10. device
+  const int dev_status = check_device();
+  if (dev_status != ATTN_OK) return dev_status;
+  // 11. launch (a side without rows launches nothing)
+  const bool bf16 = dtype == ATTN_DTYPE_BF16, c = causal != 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int mq = qrows ? max_seqlen_q : 0, mk = krows ? max_seqlen_k : 0;
+#define ETA_VL_ARGS q, k, v, out, dout, lse, dq, dk, dv, delta, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q, total_k, mq, mk, scale, s
+  switch (d) {
+    case 64:
+      return bf16 ? (c ? launch_bwd_varlen<64, true, true>(ETA_VL_ARGS) : launch_bwd_varlen<64, true, false>(ETA_VL_ARGS))
+                  : (c ? launch_bwd_varlen<64, false, true>(ETA_VL_ARGS) : launch_bwd_varlen<64, false, false>(ETA_VL_ARGS));
+    case 128:
+      return bf16 ? (c ? launch_bwd_varlen<128, true, true>(ETA_VL_ARGS) : launch_bwd_varlen<128, true, false>(ETA_VL_ARGS))
+                  : (c ? launch_bwd_varlen<128, false, true>(ETA_VL_ARGS) : launch_bwd_varlen<128, false, false>(ETA_VL_ARGS));
+    default:
+      return bf16 ? (c ? launch_bwd_varlen<256, true, true>(ETA_VL_ARGS) : launch_bwd_varlen<256, true, false>(ETA_VL_ARGS))
+                  : (c ? launch_bwd_varlen<256, false, true>(ETA_VL_ARGS) : launch_bwd_varlen<256, false, false>(ETA_VL_ARGS));
+  }
+#undef ETA_VL_ARGS
 }

@@ -118,13 +118,15 @@ __device__ __forceinline__ void tile_issue(rsrc_t r, uint16_t* dst, int wave, co
 // ---------------------------------------------------------------------------
 // dQ (and D).
 // ---------------------------------------------------------------------------
-template <int D, bool BF16, bool CAUSAL, bool SPARSE = false>
+template <int D, bool BF16, bool CAUSAL, bool SPARSE = false, bool VARLEN = false>
 __global__ void __launch_bounds__(DqCfg<D>::kThreads, DqCfg<D>::kMinWavesPerEU)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
                    const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
                    uint16_t* __restrict__ dQ, float* __restrict__ Dlt, int Hq, int Hkv, int Nq,
-                   int Nk, int nqb, int total, float scale, float c_log2, BlockMaskArgs bm) {
+                   int Nk, int nqb, int total, float scale, float c_log2, BlockMaskArgs bm,
+                   VarlenArgs va) {
+  static_assert(!(SPARSE && VARLEN), "block masks and packed sequences are separate instances");
   using C = DqCfg<D>;
   static_assert(kMaskBlock == C::BM && kMaskBlock % C::BN == 0, "a mask block is whole tiles");
   using L = typename C::L;
@@ -138,15 +140,30 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-  const WorkItem w = map_workgroup<CAUSAL>(blockIdx.x, total, nqb, Hq);
+  const WorkItem w = VARLEN ? map_workgroup_packed(blockIdx.x, nqb, Hq, va.pairs)
+                           : map_workgroup<CAUSAL>(blockIdx.x, total, nqb, Hq);
   const int hkv = w.hq / (Hq / Hkv);
   const int q0 = w.qblk * BM, qw0 = q0 + wave * 32, my_q = qw0 + l32;
+  // First rows of this (b, head) in q-shaped and k-shaped tensors, and of
+  // its lse / delta row; packed sequences take theirs from the prefix sums.
+  int64_t q_row0 = (int64_t)w.b * Nq, k_row0 = (int64_t)w.b * Nk;
+  int64_t vec_row0 = ((int64_t)w.b * Hq + w.hq) * Nq;
+  if constexpr (VARLEN) {
+    const int qs0 = min(max(va.cu_q[w.b], 0), va.total_q);
+    const int ks0 = min(max(va.cu_k[w.b], 0), va.total_k);
+    Nq = min(max(va.cu_q[w.b + 1], qs0), va.total_q) - qs0;
+    Nk = min(max(va.cu_k[w.b + 1], ks0), va.total_k) - ks0;
+    q_row0 = qs0;
+    k_row0 = ks0;
+    vec_row0 = (int64_t)w.hq * va.total_q + qs0;
+    if (q0 >= Nq) return;  // the whole workgroup, before any barrier
+  }
   const int diag = Nk - Nq;
 
   const int64_t q_rs = (int64_t)Hq * D, kv_rs = (int64_t)Hkv * D;
-  const int64_t qo_off = ((int64_t)w.b * Nq + qw0) * q_rs + (int64_t)w.hq * D;
-  const uint16_t* Kh = K + ((int64_t)w.b * Nk * Hkv + hkv) * D;
-  const uint16_t* Vh = V + ((int64_t)w.b * Nk * Hkv + hkv) * D;
+  const int64_t qo_off = (q_row0 + qw0) * q_rs + (int64_t)w.hq * D;
+  const uint16_t* Kh = K + (k_row0 * Hkv + hkv) * D;
+  const uint16_t* Vh = V + (k_row0 * Hkv + hkv) * D;
 
   // Q^T and dO^T fragments (B operands), O for D.  Rows >= Nq read as 0.
   const int rspan = span_bytes(qw0, 32, Nq, q_rs, D);
@@ -167,7 +184,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   }
   const float Di = dsum + __shfl_xor(dsum, 32);
   const int nrows = max(0, min(32, Nq - qw0));
-  const int64_t vec_off = ((int64_t)w.b * Hq + w.hq) * Nq + qw0;
+  const int64_t vec_off = vec_row0 + qw0;
   if (hh == 0) buf_store4(Di, make_rsrc(Dlt + vec_off, nrows * 4), 4 * l32);
   // lse in log2 units; an empty row (lse = -inf) has every key masked.
   const float lse_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -362,14 +379,15 @@ __device__ __forceinline__ WorkItem map_key_block(int wg, int total, int nkb, in
   return w;
 }
 
-template <int D, bool BF16, bool CAUSAL, bool SPARSE = false>
+template <int D, bool BF16, bool CAUSAL, bool SPARSE = false, bool VARLEN = false>
 __global__ void __launch_bounds__(DkvCfg<D>::kThreads, DkvCfg<D>::kMinWavesPerEU)
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                      const float* __restrict__ LSE, const float* __restrict__ Dlt,
                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv,
                      int Nq, int Nk, int nkb, int total, float scale, float c_log2,
-                     BlockMaskArgs bm) {
+                     BlockMaskArgs bm, VarlenArgs va) {
+  static_assert(!(SPARSE && VARLEN), "block masks and packed sequences are separate instances");
   using C = DkvCfg<D>;
   static_assert(kMaskBlock == C::BK && kMaskBlock % C::BQ == 0, "a mask block is whole tiles");
   using L = typename C::L;
@@ -383,13 +401,31 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-  const WorkItem w = map_key_block(blockIdx.x, total, nkb, Hkv);
+  // (w.hq is the KV head here, w.qblk the key block.)
+  const WorkItem w = VARLEN ? map_workgroup_packed(blockIdx.x, nkb, Hkv, va.pairs)
+                           : map_key_block(blockIdx.x, total, nkb, Hkv);
   const int G = Hq / Hkv;
   const int k0 = w.qblk * BK, kw0 = k0 + wave * 32, my_k = kw0 + l32;
+  // First rows of this batch entry (or packed sequence) in q-shaped and
+  // k-shaped tensors; lse / delta of query head h start at vec_row0(h).
+  int64_t q_row0 = (int64_t)w.b * Nq, k_row0 = (int64_t)w.b * Nk;
+  int64_t vec_stride = Nq, vec_first = (int64_t)w.b * Hq * Nq;
+  if constexpr (VARLEN) {
+    const int qs0 = min(max(va.cu_q[w.b], 0), va.total_q);
+    const int ks0 = min(max(va.cu_k[w.b], 0), va.total_k);
+    Nq = min(max(va.cu_q[w.b + 1], qs0), va.total_q) - qs0;
+    Nk = min(max(va.cu_k[w.b + 1], ks0), va.total_k) - ks0;
+    q_row0 = qs0;
+    k_row0 = ks0;
+    vec_stride = va.total_q;
+    vec_first = qs0;
+    if (k0 >= Nk) return;  // the whole workgroup, before any barrier
+  }
+  auto vec_row0 = [&](int h) { return vec_first + (int64_t)h * vec_stride; };
   const int diag = Nk - Nq;  // key j visible to query i iff j <= i + diag
 
   const int64_t q_rs = (int64_t)Hq * D, kv_rs = (int64_t)Hkv * D;
-  const int64_t kv_off = ((int64_t)w.b * Nk + kw0) * kv_rs + (int64_t)w.hq * D;
+  const int64_t kv_off = (k_row0 + kw0) * kv_rs + (int64_t)w.hq * D;
 
   // K^T and V^T fragments of this wave's 32 keys (B operands).
   const int kspan = span_bytes(kw0, 32, Nk, kv_rs, D);
@@ -477,7 +513,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   auto issue_step = [&](int s, uint16_t* st) {
     const int h = SPARSE ? sp_h : w.hq * G + s / nqt;
     const int i0 = SPARSE ? sp_i0 : step_rows(s);
-    const int64_t off = ((int64_t)w.b * Nq + i0) * q_rs + (int64_t)h * D;
+    const int64_t off = (q_row0 + i0) * q_rs + (int64_t)h * D;
     const int bytes = span_bytes(i0, BQ, Nq, q_rs, D);
     const rsrc_t qs = make_rsrc(Q + off, bytes);
     const rsrc_t ds = make_rsrc(dO + off, bytes);
@@ -486,7 +522,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     tile_issue<kTrInst>(qs, st + 2 * C::kRow, wave, toff);
     tile_issue<kTrInst>(ds, st + 2 * C::kRow + C::kTr, wave, toff);
     if (wave == 0) {
-      const int64_t voff = ((int64_t)w.b * Hq + h) * Nq + i0;
+      const int64_t voff = vec_row0(h) + i0;
       const int vb = max(0, min(BQ, Nq - i0)) * 4;
       buf_load_lds16(make_rsrc(LSE + voff, vb), st + 2 * C::kRow + 2 * C::kTr, 16 * lane);
       buf_load_lds16(make_rsrc(Dlt + voff, vb), st + 2 * C::kRow + 2 * C::kTr + C::kVec, 16 * lane);

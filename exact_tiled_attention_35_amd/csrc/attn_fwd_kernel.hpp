@@ -125,17 +125,6 @@ __device__ __forceinline__ float tanh_fast(float x) {
   return 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * 2.88539008177792681472f) + 1.0f);
 }
 
-// Variable-length sequences packed along the row axis: sequence b owns
-// query rows [cu_q[b], cu_q[b+1]) of q/out and key rows [cu_k[b], cu_k[b+1])
-// of k/v; lse is [Hq, total_q].  Offsets are clamped to [0, total] so that
-// no access leaves the packed tensors.
-struct VarlenArgs {
-  const int* cu_q;
-  const int* cu_k;
-  int total_q, total_k;
-  int pairs;  // sequences x query heads
-};
-
 template <int D, bool BF16, bool CAUSAL, bool MODS = false, bool VARLEN = false, bool SPARSE = false>
 __global__ void __launch_bounds__(TileCfg<D>::kThreads, TileCfg<D>::kMinWavesPerEU)
 attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,

@@ -110,6 +110,17 @@ __device__ __forceinline__ u32x2_t lds_read_tr4(const uint16_t* p) {
       u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p));
 }
 
+// Variable-length sequences packed along the row axis: sequence b owns
+// query rows [cu_q[b], cu_q[b+1]) of q/out and key rows [cu_k[b], cu_k[b+1])
+// of k/v; lse (and the backward's delta) is [Hq, total_q].  Offsets are
+// clamped to [0, total] so that no access leaves the packed tensors.
+struct VarlenArgs {
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
+  int pairs;  // sequences x heads of the grid's head axis
+};
+
 // Block sparsity: flags over (query block, key block) pairs of 128 x 128
 // decide which blocks of the score matrix take part; key j is visible to row
 // i only if the flag of (i / 128, j / 128) is nonzero (and causally, when

@@ -217,6 +217,29 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
                          float scale, int causal, int dtype, void* stream);
 
 /*
+ * attn_bwd for attn_fwd_varlen: gradients over sequences packed along the
+ * row axis (sequence b: query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]), key
+ * rows [cu_seqlens_k[b], cu_seqlens_k[b+1])), each sequence exactly as
+ * attn_bwd computes it for one batch entry; sequences share no gradients.
+ *   q, out, dout, dq  [total_q, Hq, d]      k, v, dk, dv  [total_k, Hkv, d]
+ *   lse, delta        [Hq, total_q] fp32 (lse as attn_fwd_varlen returned it)
+ *   cu_seqlens_q/k    [B + 1] int32, device (clamped to [0, total] as in
+ *                     attn_fwd_varlen)
+ *   max_seqlen_q/k    at least the longest query / key sequence (they size
+ *                     the two grids; rows past them are not written)
+ * Key rows of a sequence without query rows get dk = dv = 0; query rows of a
+ * sequence without keys get dq = 0.  No atomics: bitwise reproducible.
+ * Validation order as attn_bwd; B == 0 or total_q == total_k == 0 is a
+ * no-op; the buffers of a side without rows (total_q == 0 or total_k == 0)
+ * may be NULL.
+ */
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* out,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    float* delta, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                    int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                    int max_seqlen_k, int d, float scale, int causal, int dtype, void* stream);
+
+/*
  * KV-cache decode forward: new query rows against a key/value cache that is
  * updated in place, as the interface section of the hysenlabs.com page
  * describes the inference function ("Die Schnittstellen von flash_attn_func

@@ -40,7 +40,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
-    assert names == ["attn_bwd", "attn_bwd_blocksparse", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_size",
+    assert names == ["attn_bwd", "attn_bwd_blocksparse", "attn_bwd_varlen", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_size",
                      "attn_fwd", "attn_fwd_blocksparse", "attn_fwd_ext", "attn_fwd_varlen",
                      "attn_status_string", "attn_version"]
     for n in names:
@@ -546,3 +546,57 @@ def test_bwd_blocksparse_without_rows_needs_no_mask():
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a HIP device is visible here")
 def test_bwd_blocksparse_no_device_reported_without_gpu():
     assert call_bbs(mask_heads=8) == _lib.ATTN_ERR_NO_DEVICE
+
+
+# ---------------------------------------------------------------------------
+# attn_bwd_varlen
+# ---------------------------------------------------------------------------
+from exact_tiled_attention_35_amd.attention import attn_bwd_varlen_ptr  # noqa: E402
+
+GOOD_BVL = dict(q=Q, k=K, v=V, out=BB_OUT, dout=BB_DOUT, lse=LSE, dq=BB_DQ, dk=BB_DK, dv=BB_DV,
+                delta=BB_DELTA, cu_q=CUQ, cu_k=CUK, B=3, Hq=8, Hkv=2, total_q=300, total_k=500,
+                max_q=200, max_k=300, d=128, scale=0.088, causal=True, dtype=_lib.ATTN_DTYPE_BF16)
+BVL_ORDER = ["q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "delta", "cu_q", "cu_k", "B",
+             "Hq", "Hkv", "total_q", "total_k", "max_q", "max_k", "d", "scale", "causal", "dtype"]
+
+
+def call_bvl(**over):
+    a = dict(GOOD_BVL)
+    a.update(over)
+    return attn_bwd_varlen_ptr(*[a[n] for n in BVL_ORDER])
+
+
+@pytest.mark.parametrize("field,value", [("B", -1), ("Hq", 0), ("Hkv", 0), ("total_q", -1),
+                                         ("total_k", -1), ("max_q", -1), ("max_k", -1), ("d", 0)])
+def test_bwd_varlen_bad_shape(field, value):
+    assert call_bvl(**{field: value}) == _lib.ATTN_ERR_BAD_SHAPE
+
+
+def test_bwd_varlen_noops_and_null_pointers():
+    nulls = dict(q=0, k=0, v=0, out=0, dout=0, lse=0, dq=0, dk=0, dv=0, delta=0, cu_q=0, cu_k=0)
+    assert call_bvl(B=0, **nulls) == _lib.ATTN_OK
+    assert call_bvl(total_q=0, total_k=0, **nulls) == _lib.ATTN_OK
+    for f in ("q", "out", "dout", "lse", "dq", "delta", "k", "v", "dk", "dv", "cu_q", "cu_k"):
+        assert call_bvl(**{f: 0}) == _lib.ATTN_ERR_NULL_POINTER, f
+    # a side without rows needs no buffers
+    st = call_bvl(total_q=0, q=0, out=0, dout=0, lse=0, dq=0, delta=0)
+    assert st in (_lib.ATTN_ERR_NO_DEVICE, _lib.ATTN_OK)
+    st = call_bvl(total_k=0, k=0, v=0, dk=0, dv=0)
+    assert st in (_lib.ATTN_ERR_NO_DEVICE, _lib.ATTN_OK)
+
+
+def test_bwd_varlen_checks_in_order():
+    assert call_bvl(Hkv=3) == _lib.ATTN_ERR_GQA_RATIO
+    assert call_bvl(d=96) == _lib.ATTN_ERR_UNSUPPORTED_HDIM
+    assert call_bvl(dtype=7) == _lib.ATTN_ERR_UNSUPPORTED_DTYPE
+    assert call_bvl(scale=float("nan")) == _lib.ATTN_ERR_BAD_SCALE
+    assert call_bvl(cu_q=CUQ + 2) == _lib.ATTN_ERR_MISALIGNED
+    assert call_bvl(dk=BB_DK + 8) == _lib.ATTN_ERR_MISALIGNED
+    assert call_bvl(dq=Q) == _lib.ATTN_ERR_ALIASING
+    assert call_bvl(delta=CUK) == _lib.ATTN_ERR_ALIASING
+    assert call_bvl(dv=BB_DK + 64) == _lib.ATTN_ERR_ALIASING
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a HIP device is visible here")
+def test_bwd_varlen_no_device_reported_without_gpu():
+    assert call_bvl() == _lib.ATTN_ERR_NO_DEVICE
