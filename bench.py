@@ -325,11 +325,13 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
-    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "varlen", "blocksparse", "blocksparse_bwd"),
+    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "varlen", "varlen_bwd", "blocksparse",
+                                     "blocksparse_bwd"),
                     default="fwd",
                     help="fwd: attn_fwd (the headline metric); bwd: attn_bwd, the backward pass; "
                          "decode: attn_decode on a KV-cache decode workload; varlen: "
-                         "attn_fwd_varlen on packed variable-length sequences; blocksparse: "
+                         "attn_fwd_varlen on packed variable-length sequences; varlen_bwd: "
+                         "attn_bwd_varlen on them; blocksparse: "
                          "attn_fwd_blocksparse with a random block mask; blocksparse_bwd: "
                          "attn_bwd_blocksparse on the same workloads")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
@@ -371,11 +373,12 @@ def main():
     from exact_tiled_attention_35_amd import attn_bwd_ptr, attn_fwd, attn_version
     from exact_tiled_attention_35_amd.attention import _DTYPE_CODE
 
-    if args.op == "varlen":
+    if args.op in ("varlen", "varlen_bwd"):
         if not torch.cuda.is_available():
             log("no GPU visible")
             sys.exit(1)
-        return bench_varlen(args, VARLEN_WORKLOADS[args.workload or next(iter(VARLEN_WORKLOADS))])
+        return bench_varlen(args, VARLEN_WORKLOADS[args.workload or next(iter(VARLEN_WORKLOADS))],
+                            backward=args.op == "varlen_bwd")
     if args.op in ("blocksparse", "blocksparse_bwd"):
         from attn_workloads import BLOCKSPARSE_WORKLOADS
 
@@ -679,13 +682,15 @@ def cpu_baseline_varlen(wl, lens, q, k, v, scale, budget_s: float):
     }
 
 
-def bench_varlen(args, wl):
-    """One step = one attn_fwd_varlen call over the packed batch; flops count
-    4*d per kept (query, key) pair and head, sequence by sequence."""
+def bench_varlen(args, wl, backward=False):
+    """One step = one attn_fwd_varlen call over the packed batch (or,
+    ``backward``, one attn_bwd_varlen call from its out and lse with a seeded
+    dout); flops count 4*d (backward: 10*d) per kept (query, key) pair and
+    head, sequence by sequence."""
     import torch
 
     from attn_workloads import make_varlen, varlen_lengths
-    from exact_tiled_attention_35_amd import attn_fwd_varlen, attn_version
+    from exact_tiled_attention_35_amd import attn_bwd_varlen, attn_fwd_varlen, attn_version
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -699,7 +704,14 @@ def bench_varlen(args, wl):
     max_q = max(lens)
 
     def step():
-        attn_fwd_varlen(gq, gk, gv, gcq, gck, max_q, scale, causal)
+        return attn_fwd_varlen(gq, gk, gv, gcq, gck, max_q, scale, causal)
+
+    if backward:
+        out, lse = step()
+        gdo = make_varlen(lens, lens, H, H, d, wl["dtype"], 1.0, wl["seed"] + 100)[0].to(dev)
+
+        def step():  # noqa: F811
+            attn_bwd_varlen(gq, gk, gv, out, gdo, lse, gcq, gck, max_q, max_q, scale, causal)
 
     for _ in range(args.warmup):
         step()
@@ -717,18 +729,22 @@ def bench_varlen(args, wl):
     wall = time.perf_counter() - t0
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_s = sum(kernel_ms) / K / 1e3
-    F = sum(4.0 * H * d * visible_pairs(n, n, causal, -1, -1) for n in lens)
+    F = sum((10.0 if backward else 4.0) * H * d * visible_pairs(n, n, causal, -1, -1) for n in lens)
     value = F / (wall / K) / 1e12
     achieved = F / avg_s / 1e12
     peak = PEAK_TFLOPS[wl["dtype"]]
     total = wl["total"]
     nbytes = total * H * d * 2 * 4 + H * total * 4 + (len(lens) + 1) * 4 * 2
+    if backward:  # q, k, v, out, dout, lse read once; dq, dk, dv, delta written once
+        nbytes = total * H * d * 2 * 8 + H * total * 4 * 2 + (len(lens) + 1) * 4 * 2
     log(f"[bench] {K} steps: {wall / K * 1e3:.4f} ms/step wall, kernel avg {avg_s * 1e6:.1f} us "
         f"(min {min(kernel_ms) * 1e3:.1f} us), {achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% "
         f"of peak; lengths {lens}")
     result = {
-        "metric": "attention fwd TFLOP/s over packed variable-length sequences (4*d per kept "
-                  "(query, key) pair and head)",
+        "metric": ("attention bwd TFLOP/s over packed variable-length sequences (10*d per kept "
+                   "(query, key) pair and head)" if backward else
+                   "attention fwd TFLOP/s over packed variable-length sequences (4*d per kept "
+                   "(query, key) pair and head)"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -754,9 +770,10 @@ def bench_varlen(args, wl):
             "kernel_avg_us": round(avg_s * 1e6, 2),
         },
         "cpu_baseline": None,
-        "context": "packed variable-length forward; the headline metric is the forward (--op fwd)",
+        "context": ("packed variable-length backward" if backward else
+                    "packed variable-length forward") + "; the headline metric is the forward (--op fwd)",
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not backward:
         del gq, gk, gv
         result["cpu_baseline"] = cpu_baseline_varlen(wl, lens, q, k, v, scale, args.cpu_budget)
     print(json.dumps(result), flush=True)
