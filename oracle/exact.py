@@ -277,7 +277,8 @@ def _softmax_rows_backward(P, dP):
 
 
 def attention_backward(q, k, v, dout, scale: float, causal: bool = False, *,
-                       block_mask=None, block: int = 128):
+                       block_mask=None, block: int = 128, window=(-1, -1), alibi_slopes=None,
+                       softcap: float = 0.0):
     """Exact gradients of L = sum(dout * attention(q, k, v)) in fp64.
 
     Per (b, h) with KV head g, probabilities P (rows over the visible keys,
@@ -298,6 +299,11 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool = False, *,
     or CPU torch tensors); scale as passed to the library (an fp32 value);
     block_mask: None, or the flags of ``attention_block_sparse`` (the
     gradients of that function: P is its probability matrix).
+    window, alibi_slopes, softcap: the score variants of ``attention``.  The
+    window and ALiBi enter through P only (the bias does not depend on q or
+    k); with a softcap the final score is cap * tanh(s / cap) of the scaled
+    score s, so dS is multiplied by its derivative 1 - tanh(s / cap)^2 before
+    the products with K and Q.
 
     Returns (dq [B, Nq, Hq, d], dk [B, Nk, Hkv, d], dv [B, Nk, Hkv, d],
     delta [B, Hq, Nq]) in fp64, where delta holds D.
@@ -307,6 +313,9 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool = False, *,
     if dout.shape != q.shape:
         raise ValueError(f"dout{dout.shape} must match q{q.shape}")
     sigma = float(np.float32(scale))
+    cap = float(np.float32(softcap))
+    slopes = (np.zeros(Hq) if alibi_slopes is None
+              else np.asarray(alibi_slopes, dtype=np.float32).astype(np.float64).reshape(Hq))
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -330,10 +339,13 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool = False, *,
                 flags = bm[b, 0 if bm.shape[1] == 1 else h]
                 key_mask = flags[(rows // block)[:, None], (np.arange(Nk) // block)[None, :]]
             _, _, _, P = _rows_of_one_head(qh, kg, vg, sigma, rows, Nq, Nk, causal, True,
+                                           tuple(window), float(slopes[h]), cap,
                                            key_mask=key_mask)
             dv[b, :, g, :] += P.T @ dO
             dP = dO @ vg.T
             dS, D = _softmax_rows_backward(P, dP)
+            if cap > 0.0:
+                dS = dS * (1.0 - np.tanh(sigma * (qh @ kg.T) / cap) ** 2)
             dq[b, :, h, :] = sigma * (dS @ kg)
             dk[b, :, g, :] += sigma * (dS.T @ qh)
             delta[b, h, :] = D

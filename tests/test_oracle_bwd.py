@@ -175,3 +175,82 @@ def test_planted_mask_mistake_is_caught(monkeypatch):
     monkeypatch.undo()
     fq, fk, fv = finite_difference(q, k, v, do, float(np.float32(0.8)), True)
     assert np.abs(dv - fv).max() > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# Score variants (window, ALiBi, softcap) in the gradients
+# ---------------------------------------------------------------------------
+VAR_CASES = [  # (B, Hq, Hkv, Nq, Nk, d, causal, window, alibi, cap)
+    (1, 2, 1, 5, 7, 3, True, (2, 0), False, 0.0),
+    (1, 2, 2, 6, 4, 2, False, (1, 2), True, 0.0),
+    (1, 2, 1, 4, 6, 3, False, (-1, -1), False, 1.5),
+    (1, 2, 2, 5, 5, 2, True, (3, -1), True, 2.0),
+]
+
+
+def variant_loss(q, k, v, do, scale, causal, window, slopes, cap):
+    O, _ = oracle.attention(q, k, v, scale, causal, window=window, alibi_slopes=slopes, softcap=cap)
+    return float((O * do).sum())
+
+
+@pytest.mark.parametrize("case", VAR_CASES, ids=str)
+def test_variant_gradients_match_finite_differences(case):
+    B, Hq, Hkv, Nq, Nk, d, causal, window, alibi, cap = case
+    q, k, v, do = rand_case((B, Hq, Hkv, Nq, Nk, d, causal), 11)
+    slopes = np.array([0.5, 0.25][:Hq], dtype=np.float32) if alibi else None
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, 0.7, causal, window=window,
+                                              alibi_slopes=slopes, softcap=cap)
+    eps = 1e-6
+    sc = float(np.float32(0.7))
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + eps
+            lp = variant_loss(q, k, v, do, sc, causal, window, slopes, cap)
+            x[idx] = x0 - eps
+            lm = variant_loss(q, k, v, do, sc, causal, window, slopes, cap)
+            x[idx] = x0
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert np.abs(g - fd).max() <= 1e-7
+
+
+def test_window_and_alibi_gradients_match_sdpa_autograd():
+    B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 7, 9, 3
+    rng = np.random.default_rng(12)
+    q, k, v, do = (rng.standard_normal(s) for s in
+                   ((B, Nq, Hq, d), (B, Nk, Hkv, d), (B, Nk, Hkv, d), (B, Nq, Hq, d)))
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625], dtype=np.float32)
+    left, right = 3, 1
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, 0.6, False, window=(left, right),
+                                              alibi_slopes=slopes)
+    i = torch.arange(Nq)[:, None] + (Nk - Nq)
+    j = torch.arange(Nk)[None, :]
+    keep = (j >= i - left) & (j <= i + right)
+    bias = -torch.tensor(slopes, dtype=torch.float64)[:, None, None] * (i - j).abs()
+    bias = torch.where(keep, bias, torch.tensor(-math.inf, dtype=torch.float64))
+    t = [torch.tensor(x).transpose(1, 2).contiguous().requires_grad_(True) for x in (q, k, v)]
+    kt = t[1].repeat_interleave(Hq // Hkv, 1)
+    vt = t[2].repeat_interleave(Hq // Hkv, 1)
+    out = torch.nn.functional.scaled_dot_product_attention(t[0], kt, vt, attn_mask=bias[None],
+                                                           scale=float(np.float32(0.6)))
+    out.backward(torch.tensor(do).transpose(1, 2))
+    for got, ref in zip((dq, dk, dv), t):
+        np.testing.assert_allclose(got, ref.grad.transpose(1, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_softcap_gradient_without_its_derivative_fails_the_pin():
+    case = VAR_CASES[2]
+    B, Hq, Hkv, Nq, Nk, d, causal, window, alibi, cap = case
+    q, k, v, do = rand_case((B, Hq, Hkv, Nq, Nk, d, causal), 13)
+    good = oracle.attention_backward(q, k, v, do, 0.7, causal, softcap=cap)
+    # planted: the softcap's probabilities, but dS not multiplied by 1 - tanh^2
+    P = oracle.attention(q, k, v, 0.7, causal, softcap=cap, return_probs=True)[2]
+    sigma = float(np.float32(0.7))
+    dq_wrong = np.zeros_like(q)
+    for h in range(Hq):
+        g = h * Hkv // Hq
+        dP = do[0, :, h, :] @ v[0, :, g, :].T
+        D = (P[0, h] * dP).sum(1, keepdims=True)
+        dq_wrong[0, :, h, :] = sigma * ((P[0, h] * (dP - D)) @ k[0, :, g, :])
+    assert np.abs(dq_wrong - good[0]).max() > 1e-3
