@@ -11,6 +11,7 @@ from .attention import (  # noqa: F401
     attn_bwd,
     attn_bwd_blocksparse,
     attn_bwd_blocksparse_ptr,
+    attn_bwd_ext_ptr,
     attn_bwd_ptr,
     attn_bwd_varlen,
     attn_bwd_varlen_ptr,

@@ -57,6 +57,8 @@ def load() -> ctypes.CDLL:
     lib.attn_bwd_blocksparse.restype = ci
     lib.attn_bwd_varlen.argtypes = [vp] * 12 + [ci] * 8 + [cf, ci, ci, vp]
     lib.attn_bwd_varlen.restype = ci
+    lib.attn_bwd_ext.argtypes = [vp] * 10 + [ci] * 6 + [cf, ci, ci, ci, vp, cf, ci, vp]
+    lib.attn_bwd_ext.restype = ci
     lib.attn_decode.argtypes = [vp] * 9 + [ctypes.c_size_t] + [ci] * 7 + [cf, ci, ci, ci, vp]
     lib.attn_decode.restype = ci
     lib.attn_decode_num_splits.argtypes = [ci] * 6

@@ -75,13 +75,29 @@ def attn_bwd_ptr(q: int, k: int, v: int, out: int, dout: int, lse: int, dq: int,
                                 int(bool(causal)), int(dtype), stream or None)
 
 
+def attn_bwd_ext_ptr(q: int, k: int, v: int, out: int, dout: int, lse: int, dq: int, dk: int,
+                     dv: int, delta: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
+                     scale: float, causal: bool, window_left: int, window_right: int,
+                     alibi_slopes: int, softcap: float, dtype: int, stream: int = 0) -> int:
+    """The C entry point attn_bwd_ext with raw integer pointers."""
+    return _lib.load().attn_bwd_ext(q or None, k or None, v or None, out or None, dout or None,
+                                    lse or None, dq or None, dk or None, dv or None, delta or None,
+                                    int(B), int(Hq), int(Hkv), int(Nq), int(Nk), int(d),
+                                    float(scale), int(bool(causal)), int(window_left),
+                                    int(window_right), alibi_slopes or None, float(softcap),
+                                    int(dtype), stream or None)
+
+
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
              dout: torch.Tensor, lse: torch.Tensor, softmax_scale: float | None = None,
-             causal: bool = False):
+             causal: bool = False, window: tuple = (-1, -1),
+             alibi_slopes: torch.Tensor | None = None, softcap: float = 0.0):
     """Exact attention backward on the GPU.
 
     q, out, dout: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d]; lse: [B, Hq, Nq] fp32 --
-    ``out`` and ``lse`` as returned by ``attn_fwd`` for the same arguments.
+    ``out`` and ``lse`` as returned by ``attn_fwd`` for the same arguments
+    (score variants included: ``window``, ``alibi_slopes``, ``softcap`` select
+    attn_bwd_ext).
     Returns (dq like q, dk like k, dv like v, delta [B, Hq, Nq] fp32).
     """
     B, Nq, Hq, Hkv, Nk, d = _check_qkv(q, k, v)
@@ -92,12 +108,24 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
         softmax_scale = 1.0 / math.sqrt(d)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    left, right = (int(x) for x in window)
+    variants = left >= 0 or right >= 0 or alibi_slopes is not None or softcap != 0.0
+    if alibi_slopes is not None:
+        _check_like("alibi_slopes", alibi_slopes, (Hq,), torch.float32, q.device)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        code = attn_bwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                            dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                            dv.data_ptr(), delta.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
-                            softmax_scale, causal, _DTYPE_CODE[q.dtype], stream)
+        if variants:
+            code = attn_bwd_ext_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                    dv.data_ptr(), delta.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
+                                    softmax_scale, causal, left, right,
+                                    alibi_slopes.data_ptr() if alibi_slopes is not None else 0,
+                                    softcap, _DTYPE_CODE[q.dtype], stream)
+        else:
+            code = attn_bwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), delta.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
+                                softmax_scale, causal, _DTYPE_CODE[q.dtype], stream)
     if code != _lib.ATTN_OK:
         raise AttnError(code)
     return dq, dk, dv, delta

@@ -20,11 +20,11 @@ using eta_host::check_device;
 using eta_host::finite_bits;
 using eta_host::overlaps;
 
-template <int D, bool BF16, bool CAUSAL, bool SPARSE>
+template <int D, bool BF16, bool CAUSAL, bool SPARSE, bool MODS = false>
 int launch_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
                int Hkv, int Nq, int Nk, float scale, const eta::BlockMaskArgs& bm,
-               hipStream_t stream) {
+               hipStream_t stream, const eta::ScoreMods& mods) {
   using CQ = eta::DqCfg<D>;
   using CK = eta::DkvCfg<D>;
   const float c_log2 = scale * eta::kLog2e;
@@ -37,16 +37,16 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* out, con
   const auto* Vp = static_cast<const uint16_t*>(v);
   const auto* dO = static_cast<const uint16_t*>(dout);
   if (tq > 0) {
-    hipLaunchKernelGGL((eta::attn_bwd_dq_kernel<D, BF16, CAUSAL, SPARSE>), dim3((int)tq),
+    hipLaunchKernelGGL((eta::attn_bwd_dq_kernel<D, BF16, CAUSAL, SPARSE, false, MODS>), dim3((int)tq),
                        dim3(CQ::kThreads), 0, stream, Q, Kp, Vp, static_cast<const uint16_t*>(out),
                        dO, lse, static_cast<uint16_t*>(dq), delta, Hq, Hkv, Nq, Nk, nqb, (int)tq,
-                       scale, c_log2, bm, eta::VarlenArgs{nullptr, nullptr, 0, 0, 0});
+                       scale, c_log2, bm, eta::VarlenArgs{nullptr, nullptr, 0, 0, 0}, mods);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
   }
-  hipLaunchKernelGGL((eta::attn_bwd_dkdv_kernel<D, BF16, CAUSAL, SPARSE>), dim3((int)tk),
+  hipLaunchKernelGGL((eta::attn_bwd_dkdv_kernel<D, BF16, CAUSAL, SPARSE, false, MODS>), dim3((int)tk),
                      dim3(CK::kThreads), 0, stream, Q, Kp, Vp, dO, lse, delta,
                      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), Hq, Hkv, Nq, Nk, nkb,
-                     (int)tk, scale, c_log2, bm, eta::VarlenArgs{nullptr, nullptr, 0, 0, 0});
+                     (int)tk, scale, c_log2, bm, eta::VarlenArgs{nullptr, nullptr, 0, 0, 0}, mods);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -77,7 +77,7 @@ int launch_bwd_varlen(const void* q, const void* k, const void* v, const void* o
     hipLaunchKernelGGL((eta::attn_bwd_dq_kernel<D, BF16, CAUSAL, false, true>), dim3((int)tq),
                        dim3(CQ::kThreads), 0, stream, Q, Kp, Vp, static_cast<const uint16_t*>(out),
                        dO, lse, static_cast<uint16_t*>(dq), delta, Hq, Hkv, max_q, max_k, nqb,
-                       (int)tq, scale, c_log2, nb, va);
+                       (int)tq, scale, c_log2, nb, va, eta::ScoreMods{-1, -1, nullptr, 0.f, scale});
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
   }
   if (tk > 0) {
@@ -85,39 +85,40 @@ int launch_bwd_varlen(const void* q, const void* k, const void* v, const void* o
     hipLaunchKernelGGL((eta::attn_bwd_dkdv_kernel<D, BF16, CAUSAL, false, true>), dim3((int)tk),
                        dim3(CK::kThreads), 0, stream, Q, Kp, Vp, dO, lse, delta,
                        static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), Hq, Hkv, max_q,
-                       max_k, nkb, (int)tk, scale, c_log2, nb, va);
+                       max_k, nkb, (int)tk, scale, c_log2, nb, va,
+                       eta::ScoreMods{-1, -1, nullptr, 0.f, scale});
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
   }
   return ATTN_OK;
 }
 
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool MODS>
 int dispatch_bwd(bool bf16, bool causal, const void* q, const void* k, const void* v,
                  const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
                  float* delta, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
-                 const eta::BlockMaskArgs& bm, hipStream_t s) {
-#define ETA_BWD_ARGS q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s
+                 const eta::BlockMaskArgs& bm, hipStream_t s, const eta::ScoreMods& m) {
+#define ETA_BWD_ARGS q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, m
   if (bf16) {
-    return causal ? launch_bwd<D, true, true, SPARSE>(ETA_BWD_ARGS)
-                  : launch_bwd<D, true, false, SPARSE>(ETA_BWD_ARGS);
+    return causal ? launch_bwd<D, true, true, SPARSE, MODS>(ETA_BWD_ARGS)
+                  : launch_bwd<D, true, false, SPARSE, MODS>(ETA_BWD_ARGS);
   }
-  return causal ? launch_bwd<D, false, true, SPARSE>(ETA_BWD_ARGS)
-                : launch_bwd<D, false, false, SPARSE>(ETA_BWD_ARGS);
+  return causal ? launch_bwd<D, false, true, SPARSE, MODS>(ETA_BWD_ARGS)
+                : launch_bwd<D, false, false, SPARSE, MODS>(ETA_BWD_ARGS);
 #undef ETA_BWD_ARGS
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool MODS = false>
 int dispatch_hdim(int d, bool bf16, bool c, const void* q, const void* k, const void* v,
                   const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
                   float* delta, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
-                  const eta::BlockMaskArgs& bm, hipStream_t s) {
+                  const eta::BlockMaskArgs& bm, hipStream_t s, const eta::ScoreMods& m) {
   switch (d) {
     case 64:
-      return dispatch_bwd<64, SPARSE>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s);
+      return dispatch_bwd<64, SPARSE, MODS>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, m);
     case 128:
-      return dispatch_bwd<128, SPARSE>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s);
+      return dispatch_bwd<128, SPARSE, MODS>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, m);
     default:
-      return dispatch_bwd<256, SPARSE>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s);
+      return dispatch_bwd<256, SPARSE, MODS>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, m);
   }
 }
 
@@ -126,7 +127,8 @@ int dispatch_hdim(int d, bool bf16, bool c, const void* q, const void* k, const 
 int bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, float* delta,
              const unsigned char* block_mask, int mask_heads, bool sparse, int B, int Hq, int Hkv,
-             int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream) {
+             int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream,
+             const eta::ScoreMods* mods = nullptr) {
   // 1. shape
   if (B < 0 || Nq < 0 || Hq < 1 || Hkv < 1 || Nk < 1 || d < 1) return ATTN_ERR_BAD_SHAPE;
   // 2. empty batch: nothing to do
@@ -151,10 +153,14 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
   if (!finite_bits(scale)) return ATTN_ERR_BAD_SCALE;
   if (sparse && mask_heads != 1 && mask_heads != Hq) return ATTN_ERR_BAD_ARGUMENT;
+  if (mods && (mods->left < -1 || mods->right < -1 || !finite_bits(mods->cap) || mods->cap < 0.f))
+    return ATTN_ERR_BAD_ARGUMENT;
   // 8. alignment
   if (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_MISALIGNED;
   if (rows && (!aligned16(q) || !aligned16(out) || !aligned16(dout) || !aligned16(lse) ||
                !aligned16(dq) || !aligned16(delta)))
+    return ATTN_ERR_MISALIGNED;
+  if (rows && mods && mods->slopes && (reinterpret_cast<uintptr_t>(mods->slopes) & 3))
     return ATTN_ERR_MISALIGNED;
   // 9. aliasing: no output overlaps an input or another output
   const size_t qb = rows ? (size_t)q_elems * 2 : 0, kvb = (size_t)kv_elems * 2;
@@ -162,13 +168,14 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   const int nqbm = (Nq + eta::kMaskBlock - 1) / eta::kMaskBlock;
   const int nkbm = (Nk + eta::kMaskBlock - 1) / eta::kMaskBlock;
   const size_t mb = sparse && rows ? (size_t)B * mask_heads * nqbm * nkbm : 0;
-  const void* in_p[7] = {q, k, v, out, dout, lse, block_mask};
-  const size_t in_n[7] = {qb, kvb, kvb, qb, qb, vb, mb};
+  const size_t sb = rows && mods && mods->slopes ? (size_t)Hq * 4 : 0;
+  const void* in_p[8] = {q, k, v, out, dout, lse, block_mask, mods ? mods->slopes : nullptr};
+  const size_t in_n[8] = {qb, kvb, kvb, qb, qb, vb, mb, sb};
   const void* out_p[4] = {dq, dk, dv, delta};
   const size_t out_n[4] = {qb, kvb, kvb, vb};
   for (int i = 0; i < 4; ++i) {
     if (out_n[i] == 0) continue;
-    for (int j = 0; j < 7; ++j)
+    for (int j = 0; j < 8; ++j)
       if (in_n[j] && overlaps(out_p[i], out_n[i], in_p[j], in_n[j])) return ATTN_ERR_ALIASING;
     for (int j = i + 1; j < 4; ++j)
       if (out_n[j] && overlaps(out_p[i], out_n[i], out_p[j], out_n[j])) return ATTN_ERR_ALIASING;
@@ -181,9 +188,13 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   const bool c = causal != 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const eta::BlockMaskArgs bm{sparse && rows ? block_mask : nullptr, sparse ? mask_heads : 1, nkbm};
+  const bool active = mods && (mods->left >= 0 || mods->right >= 0 || mods->slopes || mods->cap > 0.f);
+  const eta::ScoreMods none{-1, -1, nullptr, 0.f, scale};
   if (sparse)
-    return dispatch_hdim<true>(d, bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s);
-  return dispatch_hdim<false>(d, bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s);
+    return dispatch_hdim<true>(d, bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, none);
+  if (active)
+    return dispatch_hdim<false, true>(d, bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, *mods);
+  return dispatch_hdim<false>(d, bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, none);
 }
 
 }  // namespace
@@ -194,6 +205,16 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
                         int causal, int dtype, void* stream) {
   return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, delta, nullptr, 1, false, B, Hq, Hkv, Nq, Nk,
                   d, scale, causal, dtype, stream);
+}
+
+extern "C" int attn_bwd_ext(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            float* delta, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                            int causal, int window_left, int window_right,
+                            const float* alibi_slopes, float softcap, int dtype, void* stream) {
+  const eta::ScoreMods mods{window_left, window_right, alibi_slopes, softcap, scale};
+  return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, delta, nullptr, 1, false, B, Hq, Hkv, Nq, Nk,
+                  d, scale, causal, dtype, stream, &mods);
 }
 
 extern "C" int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* out,

@@ -118,15 +118,15 @@ __device__ __forceinline__ void tile_issue(rsrc_t r, uint16_t* dst, int wave, co
 // ---------------------------------------------------------------------------
 // dQ (and D).
 // ---------------------------------------------------------------------------
-template <int D, bool BF16, bool CAUSAL, bool SPARSE = false, bool VARLEN = false>
+template <int D, bool BF16, bool CAUSAL, bool SPARSE = false, bool VARLEN = false, bool MODS = false>
 __global__ void __launch_bounds__(DqCfg<D>::kThreads, DqCfg<D>::kMinWavesPerEU)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
                    const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
                    uint16_t* __restrict__ dQ, float* __restrict__ Dlt, int Hq, int Hkv, int Nq,
                    int Nk, int nqb, int total, float scale, float c_log2, BlockMaskArgs bm,
-                   VarlenArgs va) {
-  static_assert(!(SPARSE && VARLEN), "block masks and packed sequences are separate instances");
+                   VarlenArgs va, ScoreMods mods) {
+  static_assert((int)SPARSE + (int)VARLEN + (int)MODS <= 1, "one instance per extension");
   using C = DqCfg<D>;
   static_assert(kMaskBlock == C::BM && kMaskBlock % C::BN == 0, "a mask block is whole tiles");
   using L = typename C::L;
@@ -198,6 +198,23 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int rows_end = min(qw0 + 32, Nq);
   int w_end = rows_end > qw0 ? Nk : 0;
   if (CAUSAL && rows_end > qw0) w_end = min(Nk, rows_end + diag);
+  // Window: keys right of the last row's window are never loaded, tiles left
+  // of the first row's window are skipped (jb = first tile), and a wave
+  // skips tiles outside its own rows' windows.
+  int jb = 0, w_begin = 0;
+  float slope = 0.f;
+  if constexpr (MODS) {
+    if (mods.right >= 0) {
+      kv_end = min(kv_end, max(0, min(q0 + BM, Nq) + diag + mods.right));
+      if (rows_end > qw0) w_end = min(w_end, max(0, rows_end + diag + mods.right));
+    }
+    if (mods.left >= 0) {
+      jb = max(0, q0 + diag - mods.left) / BN;
+      w_begin = qw0 + diag - mods.left;
+    }
+    nt = kv_end > jb * BN ? (kv_end - jb * BN + BN - 1) / BN : 0;
+    slope = mods.slopes ? mods.slopes[w.hq] : 0.f;
+  }
 
   // Block sparsity: the tiles of the flagged key blocks below kv_end, in key
   // order, as in the forward (flags read 64 blocks per ballot; tiles of
@@ -256,12 +273,12 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   if constexpr (SPARSE) {
     if (nt > 0) sp_cur = sparse_next();
   }
-  if (nt > 0) issue_tile(SPARSE ? sp_cur : 0, smem);
+  if (nt > 0) issue_tile(SPARSE ? sp_cur : jb * BN, smem);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < nt; ++t) {
-    const int j0 = SPARSE ? sp_cur : t * BN;
+    const int j0 = SPARSE ? sp_cur : (jb + t) * BN;
     if (t + 1 < nt) {
       int jn = j0 + BN;
       if constexpr (SPARSE) jn = sp_cur = sparse_next();
@@ -272,7 +289,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const uint16_t* ktr = st + C::kKRow;
     const uint16_t* vrow = st + C::kKRow + C::kKTr;
 
-    if (j0 < w_end) {
+    if (j0 < w_end && (!MODS || j0 + BN > w_begin)) {
       f32x16_t s[NKB], dp[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) s[kb] = dp[kb] = f32x16_t{};
@@ -304,6 +321,31 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       // dS^T = P^T (dP^T - D), P^T = 2^(s c - lse2); keys past the end and
       // (causal) above the diagonal get P = 0.
       const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + diag);
+      if constexpr (MODS) {
+        // Score variants on every element: t = sigma s, softcapped, minus
+        // the ALiBi bias (log2 units for p); dS carries the softcap's
+        // derivative 1 - tanh^2.  Keys outside the window get P = 0.
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const int dist = my_q + diag - j;
+            float tv = s[kb][r] * mods.sigma, g = 1.f;
+            if (mods.cap > 0.f) {
+              const float th = tanh_fast(tv * __builtin_amdgcn_rcpf(mods.cap));
+              tv = mods.cap * th;
+              g = 1.f - th * th;
+            }
+            tv -= slope * (float)(dist < 0 ? -dist : dist);
+            const bool vis = j < Nk && (!CAUSAL || dist >= 0) &&
+                             (mods.left < 0 || dist <= mods.left) &&
+                             (mods.right < 0 || -dist <= mods.right);
+            const float p = vis ? exp2_fast(__builtin_fmaf(tv, kLog2e, -lse2)) : 0.f;
+            s[kb][r] = p * (dp[kb][r] - Di) * g;
+          }
+        }
+      } else {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -316,6 +358,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
           }
           s[kb][r] = p * (dp[kb][r] - Di);
         }
+      }
       }
       // dQ^T += K^T dS^T (same operand mapping as the forward's PV product).
       __builtin_amdgcn_s_setprio(1);
@@ -379,15 +422,15 @@ __device__ __forceinline__ WorkItem map_key_block(int wg, int total, int nkb, in
   return w;
 }
 
-template <int D, bool BF16, bool CAUSAL, bool SPARSE = false, bool VARLEN = false>
+template <int D, bool BF16, bool CAUSAL, bool SPARSE = false, bool VARLEN = false, bool MODS = false>
 __global__ void __launch_bounds__(DkvCfg<D>::kThreads, DkvCfg<D>::kMinWavesPerEU)
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                      const float* __restrict__ LSE, const float* __restrict__ Dlt,
                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv,
                      int Nq, int Nk, int nkb, int total, float scale, float c_log2,
-                     BlockMaskArgs bm, VarlenArgs va) {
-  static_assert(!(SPARSE && VARLEN), "block masks and packed sequences are separate instances");
+                     BlockMaskArgs bm, VarlenArgs va, ScoreMods mods) {
+  static_assert((int)SPARSE + (int)VARLEN + (int)MODS <= 1, "one instance per extension");
   using C = DkvCfg<D>;
   static_assert(kMaskBlock == C::BK && kMaskBlock % C::BQ == 0, "a mask block is whole tiles");
   using L = typename C::L;
@@ -444,7 +487,17 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int nqt_all = (Nq + BQ - 1) / BQ;
   int qt_begin = 0;
   if (CAUSAL) qt_begin = min(nqt_all, max(0, k0 - diag) / BQ);
-  const int nqt = nqt_all - qt_begin;
+  int nqt = nqt_all - qt_begin;
+  if constexpr (MODS) {
+    // Window: query rows whose window holds a key of this block.
+    if (mods.right >= 0) qt_begin = max(qt_begin, min(nqt_all, max(0, k0 - diag - mods.right) / BQ));
+    int qt_end = nqt_all;
+    if (mods.left >= 0) {
+      const int i_max = k0 + BK - 1 - diag + mods.left;
+      qt_end = i_max < 0 ? 0 : min(nqt_all, i_max / BQ + 1);
+    }
+    nqt = max(0, qt_end - qt_begin);
+  }
   int nsteps = (k0 < Nk) ? G * nqt : 0;
 
   // Block sparsity: for each query head of the group, the query tiles of the
@@ -546,6 +599,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
   for (int s = 0; s < nsteps; ++s) {
     const int cur_i0 = SPARSE ? sp_i0 : step_rows(s);
+    float slope = 0.f;
+    if constexpr (MODS) slope = mods.slopes ? mods.slopes[w.hq * G + s / nqt] : 0.f;
     if (s + 1 < nsteps) {
       if constexpr (SPARSE) sparse_next();
       issue_step(s + 1, smem + ((s + 1) & 1) * C::kStage);
@@ -559,7 +614,12 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const float* dlt_t = lse_t + C::kVec / 2;
     const int i0 = cur_i0;
 
-    if (w_live && i0 + BQ - 1 >= w_first) {  // wave-uniform: some pair visible
+    bool in_window = true;
+    if constexpr (MODS) {
+      if (mods.right >= 0 && kw0 > i0 + BQ - 1 + diag + mods.right) in_window = false;
+      if (mods.left >= 0 && kw0 + 31 < i0 + diag - mods.left) in_window = false;
+    }
+    if (w_live && i0 + BQ - 1 >= w_first && in_window) {  // wave-uniform: some pair visible
       f32x16_t sc[NQB], dp[NQB];
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) sc[qb] = dp[qb] = f32x16_t{};
@@ -588,6 +648,24 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
+            if constexpr (MODS) {
+              // the score variants, as in the dQ kernel
+              const int i = i0 + row0 + e;
+              const int dist = i + diag - my_k;
+              float tv = sc[qb][r] * mods.sigma, gd = 1.f;
+              if (mods.cap > 0.f) {
+                const float th = tanh_fast(tv * __builtin_amdgcn_rcpf(mods.cap));
+                tv = mods.cap * th;
+                gd = 1.f - th * th;
+              }
+              tv -= slope * (float)(dist < 0 ? -dist : dist);
+              const bool vis = i < Nq && my_k < Nk && (!CAUSAL || dist >= 0) &&
+                               (mods.left < 0 || dist <= mods.left) &&
+                               (mods.right < 0 || -dist <= mods.right);
+              const float p = vis ? exp2_fast(__builtin_fmaf(tv, kLog2e, -l4[e] * kLog2e)) : 0.f;
+              sc[qb][r] = p;
+              dp[qb][r] = p * (dp[qb][r] - d4[e]) * gd;
+            } else {
             float p = exp2_fast(__builtin_fmaf(sc[qb][r], c_log2, -l4[e] * kLog2e));
             if (need_mask) {
               const int i = i0 + row0 + e;
@@ -596,6 +674,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             }
             sc[qb][r] = p;
             dp[qb][r] = p * (dp[qb][r] - d4[e]);
+            }
           }
         }
       }

@@ -109,22 +109,6 @@ struct TileCfg {
 };
 
 
-// Score variants (the sliding window, ALiBi and softcapping of the pages'
-// interface and version history): with diag = Nk - Nq, key j is kept for row
-// i iff i + diag - left <= j <= i + diag + right (negative = no bound); the
-// scaled score t becomes cap * tanh(t / cap) when cap > 0, and then
-// t - slope[h] * |i + diag - j| when slopes is not NULL.
-struct ScoreMods {
-  int left, right;
-  const float* slopes;
-  float cap, sigma;
-};
-
-// tanh(x) = 1 - 2 / (2^(2x log2 e) + 1); saturates to +-1 for large |x|.
-__device__ __forceinline__ float tanh_fast(float x) {
-  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * 2.88539008177792681472f) + 1.0f);
-}
-
 template <int D, bool BF16, bool CAUSAL, bool MODS = false, bool VARLEN = false, bool SPARSE = false>
 __global__ void __launch_bounds__(TileCfg<D>::kThreads, TileCfg<D>::kMinWavesPerEU)
 attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,

@@ -110,6 +110,22 @@ __device__ __forceinline__ u32x2_t lds_read_tr4(const uint16_t* p) {
       u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p));
 }
 
+// Score variants (the sliding window, ALiBi and softcapping of the pages'
+// interface and version history): with diag = Nk - Nq, key j is kept for row
+// i iff i + diag - left <= j <= i + diag + right (negative = no bound); the
+// scaled score t becomes cap * tanh(t / cap) when cap > 0, and then
+// t - slope[h] * |i + diag - j| when slopes is not NULL.
+struct ScoreMods {
+  int left, right;
+  const float* slopes;
+  float cap, sigma;
+};
+
+// tanh(x) = 1 - 2 / (2^(2x log2 e) + 1); saturates to +-1 for large |x|.
+__device__ __forceinline__ float tanh_fast(float x) {
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * 2.88539008177792681472f) + 1.0f);
+}
+
 // Variable-length sequences packed along the row axis: sequence b owns
 // query rows [cu_q[b], cu_q[b+1]) of q/out and key rows [cu_k[b], cu_k[b+1])
 // of k/v; lse (and the backward's delta) is [Hq, total_q].  Offsets are

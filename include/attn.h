@@ -197,6 +197,24 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              float scale, int causal, int dtype, void* stream);
 
 /*
+ * attn_bwd for attn_fwd_ext: gradients of L = sum(dout * out) for
+ * out = attn_fwd_ext(q, k, v, ..., window_left, window_right, alibi_slopes,
+ * softcap).  P is that function's probability matrix; the window and the
+ * ALiBi bias enter through P only, and with a softcap the derivative of
+ * cap * tanh(s / cap) multiplies dS before the products with K and Q:
+ *     dS[i,j] = P[i,j] (dP[i,j] - delta[i]) (1 - tanh(s[i,j] / cap)^2)
+ * with s = scale * <q_i, k_j>.  The arguments are attn_bwd's followed by
+ * attn_fwd_ext's variant arguments (same meanings and checks:
+ * ATTN_ERR_BAD_ARGUMENT after the scale, slopes 4-byte aligned and not
+ * overlapped by an output).  No atomics: bitwise reproducible.
+ */
+int attn_bwd_ext(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, float* delta,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                 int window_left, int window_right, const float* alibi_slopes, float softcap,
+                 int dtype, void* stream);
+
+/*
  * attn_bwd for attn_fwd_blocksparse: gradients of L = sum(dout * out) for
  * out = attn_fwd_blocksparse(q, k, v, block_mask, mask_heads, scale, causal)
  * (P is that function's probability matrix: zero outside the kept blocks).

@@ -40,7 +40,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
-    assert names == ["attn_bwd", "attn_bwd_blocksparse", "attn_bwd_varlen", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_size",
+    assert names == ["attn_bwd", "attn_bwd_blocksparse", "attn_bwd_ext", "attn_bwd_varlen", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_size",
                      "attn_fwd", "attn_fwd_blocksparse", "attn_fwd_ext", "attn_fwd_varlen",
                      "attn_status_string", "attn_version"]
     for n in names:
@@ -600,3 +600,38 @@ def test_bwd_varlen_checks_in_order():
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a HIP device is visible here")
 def test_bwd_varlen_no_device_reported_without_gpu():
     assert call_bvl() == _lib.ATTN_ERR_NO_DEVICE
+
+
+# ---------------------------------------------------------------------------
+# attn_bwd_ext (score variants in the backward)
+# ---------------------------------------------------------------------------
+from exact_tiled_attention_35_amd.attention import attn_bwd_ext_ptr  # noqa: E402
+
+
+def call_bext(left=-1, right=-1, slopes=0, cap=0.0, **over):
+    a = dict(q=Q, k=K, v=V, out=BB_OUT, dout=BB_DOUT, lse=LSE, dq=BB_DQ, dk=BB_DK, dv=BB_DV,
+             delta=BB_DELTA, B=2, Hq=8, Hkv=2, Nq=100, Nk=120, d=128, scale=0.088, causal=True,
+             dtype=_lib.ATTN_DTYPE_BF16)
+    a.update(over)
+    return attn_bwd_ext_ptr(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"], a["dk"],
+                            a["dv"], a["delta"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                            a["scale"], a["causal"], left, right, slopes, cap, a["dtype"])
+
+
+def test_bwd_ext_validation():
+    assert call_bext(B=-1) == _lib.ATTN_ERR_BAD_SHAPE
+    assert call_bext(B=0, q=0) == _lib.ATTN_OK
+    assert call_bext(dk=0) == _lib.ATTN_ERR_NULL_POINTER
+    assert call_bext(Hkv=3) == _lib.ATTN_ERR_GQA_RATIO
+    for args in (dict(left=-2), dict(right=-3), dict(cap=-1.0), dict(cap=float("nan"))):
+        assert call_bext(**args) == _lib.ATTN_ERR_BAD_ARGUMENT, args
+    assert call_bext(left=-2, scale=float("inf")) == _lib.ATTN_ERR_BAD_SCALE
+    assert call_bext(left=-2, q=Q + 8) == _lib.ATTN_ERR_BAD_ARGUMENT
+    assert call_bext(slopes=SLOPES + 2) == _lib.ATTN_ERR_MISALIGNED
+    assert call_bext(slopes=BB_DQ + 64) == _lib.ATTN_ERR_ALIASING
+    assert call_bext(slopes=BB_DELTA) == _lib.ATTN_ERR_ALIASING
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a HIP device is visible here")
+def test_bwd_ext_no_device_reported_without_gpu():
+    assert call_bext(left=5, right=0, slopes=SLOPES, cap=30.0) == _lib.ATTN_ERR_NO_DEVICE

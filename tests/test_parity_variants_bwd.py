@@ -1,0 +1,122 @@
+"""GPU parity of the backward with score variants (attn_bwd_ext: sliding
+window, ALiBi, softcap) against the fp64 oracle (attention_backward with the
+same variants), with the backward's criterion: max and mean error at most
+twice those of a plain low-precision backward that computes the same
+variants in fp32 from the same inputs (P and dS rounded to the element type
+before their products)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attn_workloads import WORKLOADS, make_qkv, make_workload
+from test_parity_bwd import check_delta, check_grads
+
+pytestmark = pytest.mark.gpu
+
+
+def slopes_for(Hq):
+    return torch.tensor([2.0 ** (-8.0 * (h + 1) / Hq) for h in range(Hq)], dtype=torch.float32)
+
+
+def lowp_backward_variants(q, k, v, do, out, scale, causal, window, slopes, cap):
+    dt = q.dtype
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    qf, dof = q.float().transpose(1, 2), do.float().transpose(1, 2)
+    kf = k.float().transpose(1, 2).repeat_interleave(G, 1)
+    vf = v.float().transpose(1, 2).repeat_interleave(G, 1)
+    sc = float(np.float32(scale))
+    s = (qf @ kf.transpose(-1, -2).contiguous()) * sc
+    gcap = torch.ones_like(s)
+    if cap > 0:
+        th = torch.tanh(s / cap)
+        s, gcap = cap * th, 1 - th * th
+    dist = (torch.arange(Nq)[:, None] + (Nk - Nq)) - torch.arange(Nk)[None, :]
+    if slopes is not None:
+        s = s - slopes.float()[None, :, None, None] * dist.abs().float()
+    vis = torch.ones(Nq, Nk, dtype=torch.bool)
+    if causal:
+        vis &= dist >= 0
+    if window[0] >= 0:
+        vis &= dist <= window[0]
+    if window[1] >= 0:
+        vis &= -dist <= window[1]
+    s = s.masked_fill(~vis, float("-inf"))
+    p = torch.softmax(s, -1).nan_to_num(0.0)
+    D = (dof * out.float().transpose(1, 2)).sum(-1, keepdim=True)
+    dv = p.to(dt).float().transpose(-1, -2) @ dof
+    dp = dof @ vf.transpose(-1, -2).contiguous()
+    ds = (p * (dp - D) * gcap).to(dt).float()
+    dq = sc * (ds @ kf)
+    dk = sc * (ds.transpose(-1, -2).contiguous() @ qf)
+    dk = dk.reshape(B, Hkv, G, Nk, d).sum(2)
+    dv = dv.reshape(B, Hkv, G, Nk, d).sum(2)
+    return [x.to(dt).transpose(1, 2).double().numpy() for x in (dq, dk, dv)]
+
+
+def gpu_fwd_bwd(q, k, v, do, scale, causal, window, slopes, cap):
+    from exact_tiled_attention_35_amd import attn_bwd, attn_fwd
+
+    qc, kc, vc, dc = (x.cuda() for x in (q, k, v, do))
+    sl = slopes.cuda() if slopes is not None else None
+    out, lse = attn_fwd(qc, kc, vc, scale, causal, window=window, alibi_slopes=sl, softcap=cap)
+    dq, dk, dv, delta = attn_bwd(qc, kc, vc, out, dc, lse, scale, causal, window=window,
+                                 alibi_slopes=sl, softcap=cap)
+    torch.cuda.synchronize()
+    return [x.cpu() for x in (dq, dk, dv, delta, out, lse)]
+
+
+# (B, Hq, Hkv, Nq, Nk, d, dtype, causal, window, alibi, softcap)
+CASES = [
+    (1, 4, 2, 300, 300, 128, "bf16", True, (100, 0), False, 0.0),
+    (1, 2, 2, 257, 400, 64, "fp16", False, (64, 64), False, 0.0),
+    (2, 4, 1, 200, 200, 128, "bf16", False, (-1, -1), True, 0.0),
+    (1, 2, 2, 300, 260, 128, "bf16", True, (-1, -1), False, 5.0),
+    (1, 4, 2, 129, 500, 256, "bf16", False, (50, 10), True, 20.0),
+    (1, 2, 1, 400, 400, 64, "bf16", True, (255, -1), True, 30.0),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_variant_backward_against_oracle(ci):
+    B, Hq, Hkv, Nq, Nk, d, dt, causal, window, alibi, cap = CASES[ci]
+    q, k, v = make_qkv(B, Nq, Nk, Hq, Hkv, d, dt, 1.0, 1500 + ci)
+    do = make_qkv(B, Nq, Nk, Hq, Hkv, d, dt, 1.0, 1550 + ci)[0]
+    slopes = slopes_for(Hq) if alibi else None
+    scale = 1.0 / np.sqrt(d)
+    dq, dk, dv, delta, out, lse = gpu_fwd_bwd(q, k, v, do, scale, causal, window, slopes, cap)
+    want = oracle.attention_backward(q, k, v, do, scale, causal, window=window,
+                                     alibi_slopes=slopes.numpy() if alibi else None, softcap=cap)
+    base = lowp_backward_variants(q, k, v, do, out, scale, causal, window, slopes, cap)
+    check_grads((dq, dk, dv), want[:3], base, f"case {ci}")
+    check_delta(delta, want[3], do, out)
+
+
+def test_variant_backward_is_deterministic():
+    B, Hq, Hkv, Nq, Nk, d, dt, causal, window, alibi, cap = CASES[4]
+    q, k, v = make_qkv(B, Nq, Nk, Hq, Hkv, d, dt, 1.0, 1590)
+    do = make_qkv(B, Nq, Nk, Hq, Hkv, d, dt, 1.0, 1591)[0]
+    a = gpu_fwd_bwd(q, k, v, do, 0.1, causal, window, slopes_for(Hq), cap)
+    b = gpu_fwd_bwd(q, k, v, do, 0.1, causal, window, slopes_for(Hq), cap)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_headline_shape_softcap_and_alibi_full_size_head():
+    """The headline shape with softcap 30 and ALiBi (the benched forward
+    variants) at full size; one KV group's gradients against the oracle."""
+    w = WORKLOADS["mha_b4_h16_n4096_d128_bf16"]
+    q, k, v = make_workload(w)
+    do = make_qkv(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.dtype, w.sigma, w.seed + 100)[0]
+    slopes = slopes_for(w.Hq)
+    dq, dk, dv, delta, out, lse = gpu_fwd_bwd(q, k, v, do, w.scale, w.causal, (-1, -1), slopes, 30.0)
+    b, h = 1, 5
+    sl = lambda x: x[b:b + 1, :, h:h + 1]  # noqa: E731
+    want = oracle.attention_backward(sl(q), sl(k), sl(v), sl(do), w.scale, w.causal,
+                                     alibi_slopes=slopes.numpy()[h:h + 1], softcap=30.0)
+    base = lowp_backward_variants(sl(q), sl(k), sl(v), sl(do), sl(out), w.scale, w.causal, (-1, -1),
+                                  slopes[h:h + 1], 30.0)
+    check_grads((sl(dq), sl(dk), sl(dv)), want[:3], base, "headline softcap+alibi")
