@@ -336,9 +336,12 @@ def main():
                          "attn_bwd_blocksparse on the same workloads")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--window", nargs=2, type=int, default=(-1, -1), metavar=("LEFT", "RIGHT"),
-                    help="fwd only: sliding window (attn_fwd_ext); flops count the kept pairs")
-    ap.add_argument("--softcap", type=float, default=0.0, help="fwd only: softcap (attn_fwd_ext)")
-    ap.add_argument("--alibi", action="store_true", help="fwd only: ALiBi slopes (attn_fwd_ext)")
+                    help="fwd/bwd: sliding window (attn_fwd_ext / attn_bwd_ext); flops count the "
+                         "kept pairs")
+    ap.add_argument("--softcap", type=float, default=0.0,
+                    help="fwd/bwd: softcap (attn_fwd_ext / attn_bwd_ext)")
+    ap.add_argument("--alibi", action="store_true",
+                    help="fwd/bwd: ALiBi slopes (attn_fwd_ext / attn_bwd_ext)")
     ap.add_argument("--splits", type=int, default=0,
                     help="decode only: number of key splits (0: the library's heuristic)")
     ap.add_argument("--cold-mib", type=int, default=0, metavar="MIB",
@@ -426,9 +429,25 @@ def main():
         ptrs = [t.data_ptr() for t in (dq, dk, dv, out, ddo, lse, gq, gk, gv, delta)]
         code_dt = _DTYPE_CODE[dq.dtype]
 
+        slopes = None
+        if args.alibi:
+            slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / w.Hq) for h in range(w.Hq)],
+                                  dtype=torch.float32, device=dev)
+        if variants:
+            from exact_tiled_attention_35_amd.attention import attn_bwd_ext_ptr
+
+            attn_fwd(dq, dk, dv, w.scale, w.causal, out=out, lse=lse, window=tuple(args.window),
+                     alibi_slopes=slopes, softcap=args.softcap)
+
         def step():
-            code = attn_bwd_ptr(*ptrs, w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.scale, w.causal,
-                                code_dt, stream.cuda_stream)
+            if variants:
+                code = attn_bwd_ext_ptr(*ptrs, w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.scale, w.causal,
+                                        args.window[0], args.window[1],
+                                        slopes.data_ptr() if slopes is not None else 0,
+                                        args.softcap, code_dt, stream.cuda_stream)
+            else:
+                code = attn_bwd_ptr(*ptrs, w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.scale, w.causal,
+                                    code_dt, stream.cuda_stream)
             if code != 0:
                 raise SystemExit(f"attn_bwd failed with status {code}")
 
@@ -452,8 +471,8 @@ def main():
     ms_per_step = wall / K * 1e3
 
     F = flops(w) if args.op == "fwd" else bwd_flops(w)
-    if args.op == "fwd" and variants:
-        F = variant_flops(w, *args.window)
+    if variants:
+        F = variant_flops(w, *args.window) * (1.0 if args.op == "fwd" else 2.5)
     value = F / (wall / K) / 1e12
     achieved = F / avg_kernel_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -499,9 +518,14 @@ def main():
     if variants:
         result["config"]["variants"] = {"window": list(args.window), "softcap": args.softcap,
                                          "alibi": bool(args.alibi)}
-        result["metric"] = ("attention fwd TFLOP/s with score variants (4*d per kept "
-                            "(query, key) pair and head)")
-        result["context"] = "score variants (attn_fwd_ext); the headline metric is plain attn_fwd"
+        if args.op == "fwd":
+            result["metric"] = ("attention fwd TFLOP/s with score variants (4*d per kept "
+                                "(query, key) pair and head)")
+            result["context"] = "score variants (attn_fwd_ext); the headline metric is plain attn_fwd"
+        else:
+            result["metric"] = ("attention bwd TFLOP/s with score variants (10*d per kept "
+                                "(query, key) pair and head)")
+            result["context"] = "score variants in the backward (attn_bwd_ext)"
     if args.op == "bwd":
         result["roofline"]["unit_of_work"] = ("one attn_bwd call: the dQ kernel and the dK/dV "
                                               "kernel back to back")
