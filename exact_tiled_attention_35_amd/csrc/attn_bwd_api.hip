@@ -20,7 +20,7 @@ using eta_host::check_device;
 using eta_host::finite_bits;
 using eta_host::overlaps;
 
-template <int D, bool BF16, bool CAUSAL, bool SPARSE, bool MODS = false>
+template <int D, bool BF16, bool CAUSAL, bool SPARSE, int MK = 0>
 int launch_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
                int Hkv, int Nq, int Nk, float scale, const eta::BlockMaskArgs& bm,
@@ -37,13 +37,13 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* out, con
   const auto* Vp = static_cast<const uint16_t*>(v);
   const auto* dO = static_cast<const uint16_t*>(dout);
   if (tq > 0) {
-    hipLaunchKernelGGL((eta::attn_bwd_dq_kernel<D, BF16, CAUSAL, SPARSE, false, MODS>), dim3((int)tq),
+    hipLaunchKernelGGL((eta::attn_bwd_dq_kernel<D, BF16, CAUSAL, SPARSE, false, MK>), dim3((int)tq),
                        dim3(CQ::kThreads), 0, stream, Q, Kp, Vp, static_cast<const uint16_t*>(out),
                        dO, lse, static_cast<uint16_t*>(dq), delta, Hq, Hkv, Nq, Nk, nqb, (int)tq,
                        scale, c_log2, bm, eta::VarlenArgs{nullptr, nullptr, 0, 0, 0}, mods);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
   }
-  hipLaunchKernelGGL((eta::attn_bwd_dkdv_kernel<D, BF16, CAUSAL, SPARSE, false, MODS>), dim3((int)tk),
+  hipLaunchKernelGGL((eta::attn_bwd_dkdv_kernel<D, BF16, CAUSAL, SPARSE, false, MK>), dim3((int)tk),
                      dim3(CK::kThreads), 0, stream, Q, Kp, Vp, dO, lse, delta,
                      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), Hq, Hkv, Nq, Nk, nkb,
                      (int)tk, scale, c_log2, bm, eta::VarlenArgs{nullptr, nullptr, 0, 0, 0}, mods);
@@ -92,33 +92,33 @@ int launch_bwd_varlen(const void* q, const void* k, const void* v, const void* o
   return ATTN_OK;
 }
 
-template <int D, bool SPARSE, bool MODS>
+template <int D, bool SPARSE, int MK>
 int dispatch_bwd(bool bf16, bool causal, const void* q, const void* k, const void* v,
                  const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
                  float* delta, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
                  const eta::BlockMaskArgs& bm, hipStream_t s, const eta::ScoreMods& m) {
 #define ETA_BWD_ARGS q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, m
   if (bf16) {
-    return causal ? launch_bwd<D, true, true, SPARSE, MODS>(ETA_BWD_ARGS)
-                  : launch_bwd<D, true, false, SPARSE, MODS>(ETA_BWD_ARGS);
+    return causal ? launch_bwd<D, true, true, SPARSE, MK>(ETA_BWD_ARGS)
+                  : launch_bwd<D, true, false, SPARSE, MK>(ETA_BWD_ARGS);
   }
-  return causal ? launch_bwd<D, false, true, SPARSE, MODS>(ETA_BWD_ARGS)
-                : launch_bwd<D, false, false, SPARSE, MODS>(ETA_BWD_ARGS);
+  return causal ? launch_bwd<D, false, true, SPARSE, MK>(ETA_BWD_ARGS)
+                : launch_bwd<D, false, false, SPARSE, MK>(ETA_BWD_ARGS);
 #undef ETA_BWD_ARGS
 }
 
-template <bool SPARSE, bool MODS = false>
+template <bool SPARSE, int MK = 0>
 int dispatch_hdim(int d, bool bf16, bool c, const void* q, const void* k, const void* v,
                   const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
                   float* delta, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
                   const eta::BlockMaskArgs& bm, hipStream_t s, const eta::ScoreMods& m) {
   switch (d) {
     case 64:
-      return dispatch_bwd<64, SPARSE, MODS>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, m);
+      return dispatch_bwd<64, SPARSE, MK>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, m);
     case 128:
-      return dispatch_bwd<128, SPARSE, MODS>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, m);
+      return dispatch_bwd<128, SPARSE, MK>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, m);
     default:
-      return dispatch_bwd<256, SPARSE, MODS>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, m);
+      return dispatch_bwd<256, SPARSE, MK>(bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, m);
   }
 }
 
@@ -192,8 +192,20 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   const eta::ScoreMods none{-1, -1, nullptr, 0.f, scale};
   if (sparse)
     return dispatch_hdim<true>(d, bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, none);
-  if (active)
-    return dispatch_hdim<false, true>(d, bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, *mods);
+  if (active) {
+#define ETA_MODS_ARGS d, bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, *mods
+    using eta::kModsAlibi;
+    using eta::kModsCap;
+    using eta::kModsOn;
+    // One instance per combination of softcap and ALiBi (the window is read
+    // at run time by all four).
+    const bool cap = mods->cap > 0.f, alibi = mods->slopes != nullptr;
+    if (cap && alibi) return dispatch_hdim<false, kModsOn | kModsCap | kModsAlibi>(ETA_MODS_ARGS);
+    if (cap) return dispatch_hdim<false, kModsOn | kModsCap>(ETA_MODS_ARGS);
+    if (alibi) return dispatch_hdim<false, kModsOn | kModsAlibi>(ETA_MODS_ARGS);
+    return dispatch_hdim<false, kModsOn>(ETA_MODS_ARGS);
+#undef ETA_MODS_ARGS
+  }
   return dispatch_hdim<false>(d, bf16, c, q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq, Nk, scale, bm, s, none);
 }
 

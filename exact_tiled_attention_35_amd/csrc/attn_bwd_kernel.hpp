@@ -46,6 +46,12 @@ namespace eta {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// Score-variant instances of the backward kernels (template argument MK):
+// kModsOn marks one (the window is read at run time); kModsCap and
+// kModsAlibi select the softcap and the ALiBi bias at compile time, so that
+// each instance carries only the per-element work it needs.
+constexpr int kModsOn = 1, kModsCap = 2, kModsAlibi = 4;
+
 // LDS row strides (16-byte chunks per row): "row" tiles feed ds_read_b128
 // operand reads (odd multiple of 4 dwords), "tr" tiles feed the transpose
 // reads (odd multiple of 16 dwords); see the forward kernel's tile notes.
@@ -118,7 +124,7 @@ __device__ __forceinline__ void tile_issue(rsrc_t r, uint16_t* dst, int wave, co
 // ---------------------------------------------------------------------------
 // dQ (and D).
 // ---------------------------------------------------------------------------
-template <int D, bool BF16, bool CAUSAL, bool SPARSE = false, bool VARLEN = false, bool MODS = false>
+template <int D, bool BF16, bool CAUSAL, bool SPARSE = false, bool VARLEN = false, int MK = 0>
 __global__ void __launch_bounds__(DqCfg<D>::kThreads, DqCfg<D>::kMinWavesPerEU)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
@@ -126,6 +132,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    uint16_t* __restrict__ dQ, float* __restrict__ Dlt, int Hq, int Hkv, int Nq,
                    int Nk, int nqb, int total, float scale, float c_log2, BlockMaskArgs bm,
                    VarlenArgs va, ScoreMods mods) {
+  constexpr bool MODS = MK != 0;
+  constexpr bool kCap = (MK & kModsCap) != 0, kAlibi = (MK & kModsAlibi) != 0;
   static_assert((int)SPARSE + (int)VARLEN + (int)MODS <= 1, "one instance per extension");
   using C = DqCfg<D>;
   static_assert(kMaskBlock == C::BM && kMaskBlock % C::BN == 0, "a mask block is whole tiles");
@@ -213,8 +221,18 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       w_begin = qw0 + diag - mods.left;
     }
     nt = kv_end > jb * BN ? (kv_end - jb * BN + BN - 1) / BN : 0;
-    slope = mods.slopes ? mods.slopes[w.hq] : 0.f;
+    if constexpr (kAlibi) slope = mods.slopes[w.hq];
   }
+  // Score variants in log2 units (softcap: exp2 argument 2 x log2e with
+  // x = sigma s / cap, output scale cap log2e), and the distances
+  // dist = my_q + diag - j this row sees as one interval [vis_lo, vis_hi]
+  // (keys past the end, causal, window).
+  const float sigma_l2 = mods.sigma * kLog2e, slope_l2 = slope * kLog2e, cap_l2 = mods.cap * kLog2e;
+  const float cap_in = kCap ? mods.sigma * __builtin_amdgcn_rcpf(mods.cap) * (2.0f * kLog2e) : 0.f;
+  int lo_i = my_q - Nq + 1, hi_i = 1 << 30;
+  if (CAUSAL) lo_i = max(lo_i, 0);
+  if (MODS && mods.right >= 0) lo_i = max(lo_i, -mods.right);
+  if (MODS && mods.left >= 0) hi_i = mods.left;
 
   // Block sparsity: the tiles of the flagged key blocks below kv_end, in key
   // order, as in the forward (flags read 64 blocks per ballot; tiles of
@@ -322,27 +340,44 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       // (causal) above the diagonal get P = 0.
       const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + diag);
       if constexpr (MODS) {
-        // Score variants on every element: t = sigma s, softcapped, minus
-        // the ALiBi bias (log2 units for p); dS carries the softcap's
-        // derivative 1 - tanh^2.  Keys outside the window get P = 0.
+        // Score variants on every element: t = sigma s, softcapped, minus the
+        // ALiBi bias (log2 units); dS carries the softcap's derivative
+        // 1 - tanh^2.  Only tiles cut by the end, the diagonal or the window
+        // test distances.
+        const bool mmask = need_mask || (mods.left >= 0 && qw0 + 31 + diag - j0 > mods.left) ||
+                           (mods.right >= 0 && j0 + BN - 1 - qw0 - diag > mods.right);
+        const int fd = my_q + diag - j0 - 4 * hh;  // distance at kb = r = 0
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const int dist = my_q + diag - j;
-            float tv = s[kb][r] * mods.sigma, g = 1.f;
-            if (mods.cap > 0.f) {
-              const float th = tanh_fast(tv * __builtin_amdgcn_rcpf(mods.cap));
-              tv = mods.cap * th;
-              g = 1.f - th * th;
+            const int d = fd - (kb * 32 + 8 * (r >> 2) + (r & 3));
+            const float base = kAlibi ? __builtin_fmaf(-slope_l2, __builtin_fabsf((float)d), -lse2) : -lse2;
+            float p, gd = 1.f;
+            if constexpr (kCap) {
+              const float th =
+                  __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(exp2_fast(s[kb][r] * cap_in) + 1.f), 1.f);
+              gd = __builtin_fmaf(-th, th, 1.f);
+              p = exp2_fast(__builtin_fmaf(th, cap_l2, base));
+            } else {
+              p = exp2_fast(__builtin_fmaf(s[kb][r], sigma_l2, base));
             }
-            tv -= slope * (float)(dist < 0 ? -dist : dist);
-            const bool vis = j < Nk && (!CAUSAL || dist >= 0) &&
-                             (mods.left < 0 || dist <= mods.left) &&
-                             (mods.right < 0 || -dist <= mods.right);
-            const float p = vis ? exp2_fast(__builtin_fmaf(tv, kLog2e, -lse2)) : 0.f;
-            s[kb][r] = p * (dp[kb][r] - Di) * g;
+            const float t = p * (dp[kb][r] - Di);
+            s[kb][r] = kCap ? t * gd : t;
+          }
+        }
+        if (mmask) {
+          // Element offset o = kb * 32 + 8 (r / 4) + r % 4 is visible iff
+          // fd - o lies in [lo_i, hi_i]; a select, so that an infinite or
+          // NaN value of a hidden element goes away.
+          const int o_lo = fd - hi_i, o_hi = fd - lo_i;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int o = kb * 32 + 8 * (r >> 2) + (r & 3);
+              s[kb][r] = (o >= o_lo && o <= o_hi) ? s[kb][r] : 0.f;
+            }
           }
         }
       } else {
@@ -422,7 +457,7 @@ __device__ __forceinline__ WorkItem map_key_block(int wg, int total, int nkb, in
   return w;
 }
 
-template <int D, bool BF16, bool CAUSAL, bool SPARSE = false, bool VARLEN = false, bool MODS = false>
+template <int D, bool BF16, bool CAUSAL, bool SPARSE = false, bool VARLEN = false, int MK = 0>
 __global__ void __launch_bounds__(DkvCfg<D>::kThreads, DkvCfg<D>::kMinWavesPerEU)
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -430,6 +465,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv,
                      int Nq, int Nk, int nkb, int total, float scale, float c_log2,
                      BlockMaskArgs bm, VarlenArgs va, ScoreMods mods) {
+  constexpr bool MODS = MK != 0;
+  constexpr bool kCap = (MK & kModsCap) != 0, kAlibi = (MK & kModsAlibi) != 0;
   static_assert((int)SPARSE + (int)VARLEN + (int)MODS <= 1, "one instance per extension");
   using C = DkvCfg<D>;
   static_assert(kMaskBlock == C::BK && kMaskBlock % C::BQ == 0, "a mask block is whole tiles");
@@ -556,6 +593,15 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   };
   // First query row this wave's keys see (causal), for skipping whole tiles.
   const int w_first = CAUSAL ? kw0 - diag : -(1 << 30);
+  // Score variants in log2 units (as in the dQ kernel), and the distances
+  // dist = i + diag - my_k this key sees as one interval [vis_lo, vis_hi]
+  // (rows past the end, causal, window; none for keys past the end).
+  const float sigma_l2 = mods.sigma * kLog2e, cap_l2 = mods.cap * kLog2e;
+  const float cap_in = kCap ? mods.sigma * __builtin_amdgcn_rcpf(mods.cap) * (2.0f * kLog2e) : 0.f;
+  int lo_i = CAUSAL ? 0 : -(1 << 29), hi_i = Nk - my_k - 1;
+  if (MODS && mods.right >= 0) lo_i = max(lo_i, -mods.right);
+  if (MODS && mods.left >= 0) hi_i = min(hi_i, mods.left);
+  if (my_k >= Nk) hi_i = -(1 << 30);
   const bool w_live = kw0 < Nk;
 
   int roff[kRowPW], toff[kTrPW];
@@ -600,7 +646,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (int s = 0; s < nsteps; ++s) {
     const int cur_i0 = SPARSE ? sp_i0 : step_rows(s);
     float slope = 0.f;
-    if constexpr (MODS) slope = mods.slopes ? mods.slopes[w.hq * G + s / nqt] : 0.f;
+    if constexpr (kAlibi) slope = mods.slopes[w.hq * G + s / nqt];
     if (s + 1 < nsteps) {
       if constexpr (SPARSE) sparse_next();
       issue_step(s + 1, smem + ((s + 1) & 1) * C::kStage);
@@ -638,6 +684,57 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       // registers hold: row 32 qb + 8 (r / 4) + 4 hh + r % 4.  Rows past Nq
       // read lse = D = 0 with zero Q and dO rows: they add nothing.
       const bool need_mask = (i0 + BQ > Nq) || (CAUSAL && i0 + diag < kw0 + 31);
+      if constexpr (MODS) {
+        // The score variants, as in the dQ kernel; row
+        // i = i0 + 32 qb + 8 g + 4 hh + e.
+        const bool mmask = need_mask || (mods.left >= 0 && i0 + BQ - 1 + diag - kw0 > mods.left) ||
+                           (mods.right >= 0 && kw0 + 31 - i0 - diag > mods.right);
+        const int fd = i0 + diag - my_k + 4 * hh;  // distance at qb = g = e = 0
+        const float slope_l2 = slope * kLog2e;
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int row0 = 32 * qb + 8 * g + 4 * hh;
+            const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse_t + row0);
+            const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dlt_t + row0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              const int d = fd + (32 * qb + 8 * g + e);
+              const float nl = l4[e] * -kLog2e;
+              const float base = kAlibi ? __builtin_fmaf(-slope_l2, __builtin_fabsf((float)d), nl) : nl;
+              float p, gd = 1.f;
+              if constexpr (kCap) {
+                const float th =
+                    __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(exp2_fast(sc[qb][r] * cap_in) + 1.f), 1.f);
+                gd = __builtin_fmaf(-th, th, 1.f);
+                p = exp2_fast(__builtin_fmaf(th, cap_l2, base));
+              } else {
+                p = exp2_fast(__builtin_fmaf(sc[qb][r], sigma_l2, base));
+              }
+              sc[qb][r] = p;
+              const float t = p * (dp[qb][r] - d4[e]);
+              dp[qb][r] = kCap ? t * gd : t;
+            }
+          }
+        }
+        if (mmask) {
+          // Row offset o = 32 qb + 8 g + e is visible iff fd + o lies in
+          // [lo_i, hi_i] (selects, as in the dQ kernel).
+          const int o_lo = lo_i - fd, o_hi = hi_i - fd;
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int o = 32 * qb + 8 * (r >> 2) + (r & 3);
+              const bool vis = o >= o_lo && o <= o_hi;
+              sc[qb][r] = vis ? sc[qb][r] : 0.f;
+              dp[qb][r] = vis ? dp[qb][r] : 0.f;
+            }
+          }
+        }
+      } else {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
@@ -648,24 +745,6 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            if constexpr (MODS) {
-              // the score variants, as in the dQ kernel
-              const int i = i0 + row0 + e;
-              const int dist = i + diag - my_k;
-              float tv = sc[qb][r] * mods.sigma, gd = 1.f;
-              if (mods.cap > 0.f) {
-                const float th = tanh_fast(tv * __builtin_amdgcn_rcpf(mods.cap));
-                tv = mods.cap * th;
-                gd = 1.f - th * th;
-              }
-              tv -= slope * (float)(dist < 0 ? -dist : dist);
-              const bool vis = i < Nq && my_k < Nk && (!CAUSAL || dist >= 0) &&
-                               (mods.left < 0 || dist <= mods.left) &&
-                               (mods.right < 0 || -dist <= mods.right);
-              const float p = vis ? exp2_fast(__builtin_fmaf(tv, kLog2e, -l4[e] * kLog2e)) : 0.f;
-              sc[qb][r] = p;
-              dp[qb][r] = p * (dp[qb][r] - d4[e]) * gd;
-            } else {
             float p = exp2_fast(__builtin_fmaf(sc[qb][r], c_log2, -l4[e] * kLog2e));
             if (need_mask) {
               const int i = i0 + row0 + e;
@@ -674,9 +753,9 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             }
             sc[qb][r] = p;
             dp[qb][r] = p * (dp[qb][r] - d4[e]);
-            }
           }
         }
+      }
       }
       // dV^T += dO^T P and dK^T += Q^T dS (the forward's PV operand mapping).
       __builtin_amdgcn_s_setprio(1);
