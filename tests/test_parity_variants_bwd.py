@@ -77,6 +77,16 @@ CASES = [
     (1, 2, 2, 300, 260, 128, "bf16", True, (-1, -1), False, 5.0),
     (1, 4, 2, 129, 500, 256, "bf16", False, (50, 10), True, 20.0),
     (1, 2, 1, 400, 400, 64, "bf16", True, (255, -1), True, 30.0),
+    # every variant kind (window only, softcap, ALiBi, both) at every head
+    # dim on tiles cut by a window, a ragged end or empty rows
+    (1, 2, 1, 190, 333, 256, "fp16", True, (80, 20), False, 0.0),
+    (2, 2, 2, 333, 190, 64, "bf16", False, (40, 70), False, 10.0),
+    (1, 2, 2, 160, 160, 256, "fp16", True, (-1, -1), False, 15.0),
+    (1, 2, 1, 260, 380, 128, "bf16", False, (60, 60), False, 8.0),
+    (1, 4, 4, 250, 300, 64, "fp16", True, (100, 0), True, 0.0),
+    (1, 2, 1, 300, 200, 256, "bf16", False, (-1, 30), True, 0.0),
+    (1, 2, 2, 500, 300, 128, "bf16", True, (150, -1), True, 0.0),
+    (1, 4, 2, 350, 350, 128, "fp16", False, (90, 40), True, 25.0),
 ]
 
 
