@@ -684,6 +684,9 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       // registers hold: row 32 qb + 8 (r / 4) + 4 hh + r % 4.  Rows past Nq
       // read lse = D = 0 with zero Q and dO rows: they add nothing.
       const bool need_mask = (i0 + BQ > Nq) || (CAUSAL && i0 + diag < kw0 + 31);
+      // Causal and block-sparse instances mask in a pass of their own after
+      // P and dS (fewer registers live there); the others per element.
+      constexpr bool kMaskPass = CAUSAL || SPARSE;
       if constexpr (MODS) {
         // The score variants, as in the dQ kernel; row
         // i = i0 + 32 qb + 8 g + 4 hh + e.
@@ -746,13 +749,30 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
             float p = exp2_fast(__builtin_fmaf(sc[qb][r], c_log2, -l4[e] * kLog2e));
-            if (need_mask) {
+            if (!kMaskPass && need_mask) {
               const int i = i0 + row0 + e;
               const bool vis = i < Nq && my_k < Nk && (!CAUSAL || my_k <= i + diag);
               p = vis ? p : 0.f;
             }
             sc[qb][r] = p;
             dp[qb][r] = p * (dp[qb][r] - d4[e]);
+          }
+        }
+      }
+      if (kMaskPass && need_mask) {
+        // Row i = i0 + 4 hh + o, o = 32 qb + 8 (r / 4) + r % 4, is visible
+        // iff i < Nq and (causal) my_k <= i + diag: o in [o_lo, o_hi].
+        // Selects, so that an infinite P of a hidden pair goes away.
+        const int o_lo = CAUSAL ? my_k - diag - i0 - 4 * hh : -(1 << 30);
+        const int o_hi = my_k < Nk ? Nq - i0 - 4 * hh - 1 : -(1 << 30) - 1;
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int o = 32 * qb + 8 * (r >> 2) + (r & 3);
+            const bool vis = o >= o_lo && o <= o_hi;
+            sc[qb][r] = vis ? sc[qb][r] : 0.f;
+            dp[qb][r] = vis ? dp[qb][r] : 0.f;
           }
         }
       }
