@@ -156,6 +156,23 @@ def test_backward_rows_without_keys_and_no_queries():
     assert torch.all(dk0 == 0) and torch.all(dv0 == 0)
 
 
+@pytest.mark.parametrize("Nq,Nk,causal", [(300, 300, True), (333, 190, True), (190, 333, False)])
+def test_backward_large_logits(Nq, Nk, causal):
+    # Inputs with sigma 8 give scaled scores with a spread of ~64: hidden
+    # (causal or past-the-end) pairs then lie up to ~200 above the row's
+    # logsumexp, so their exponential overflows fp32 and must be dropped
+    # before it reaches dS, dK or dV.
+    q, k, v = make_qkv(1, Nq, Nk, 2, 1, 128, "bf16", 8.0, 710)
+    do = make_qkv(1, Nq, Nq, 2, 2, 128, "bf16", 1.0, 711)[0]
+    scale = 1.0 / math.sqrt(128)
+    dq, dk, dv, delta, out, _ = gpu_fwd_bwd(q, k, v, do, scale, causal)
+    assert all(torch.isfinite(x.float()).all() for x in (dq, dk, dv, delta))
+    want = oracle.attention_backward(q, k, v, do, scale, causal)
+    check_grads((dq, dk, dv), want[:3], lowp_backward(q, k, v, do, out, scale, causal),
+                f"large logits {Nq}x{Nk} causal {causal}")
+    check_delta(delta, want[3], do, out)
+
+
 def test_backward_invariants():
     q, k, v = make_qkv(1, 300, 300, 4, 2, 128, "bf16", 1.0, 704)
     do = make_qkv(1, 300, 300, 4, 4, 128, "bf16", 1.0, 705)[0]

@@ -105,6 +105,23 @@ def test_variant_backward_against_oracle(ci):
     check_delta(delta, want[3], do, out)
 
 
+@pytest.mark.parametrize("cap", [0.0, 200.0])
+def test_variant_backward_large_logits(cap):
+    # sigma 8 inputs: hidden pairs of the window's edge tiles overflow the
+    # exponential; the mask pass must drop them (softcap 200 barely caps).
+    B, Hq, Hkv, Nq, Nk, d = 1, 2, 1, 333, 300, 128
+    q, k, v = make_qkv(B, Nq, Nk, Hq, Hkv, d, "bf16", 8.0, 1580)
+    do = make_qkv(B, Nq, Nk, Hq, Hkv, d, "bf16", 1.0, 1581)[0]
+    slopes, window, scale = slopes_for(Hq), (90, 10), 1.0 / np.sqrt(d)
+    dq, dk, dv, delta, out, lse = gpu_fwd_bwd(q, k, v, do, scale, True, window, slopes, cap)
+    assert all(torch.isfinite(x.float()).all() for x in (dq, dk, dv, delta))
+    want = oracle.attention_backward(q, k, v, do, scale, True, window=window,
+                                     alibi_slopes=slopes.numpy(), softcap=cap)
+    base = lowp_backward_variants(q, k, v, do, out, scale, True, window, slopes, cap)
+    check_grads((dq, dk, dv), want[:3], base, f"large logits cap {cap}")
+    check_delta(delta, want[3], do, out)
+
+
 def test_variant_backward_is_deterministic():
     B, Hq, Hkv, Nq, Nk, d, dt, causal, window, alibi, cap = CASES[4]
     q, k, v = make_qkv(B, Nq, Nk, Hq, Hkv, d, dt, 1.0, 1590)
