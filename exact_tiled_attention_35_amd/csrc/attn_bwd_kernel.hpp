@@ -685,7 +685,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       // read lse = D = 0 with zero Q and dO rows: they add nothing.
       const bool need_mask = (i0 + BQ > Nq) || (CAUSAL && i0 + diag < kw0 + 31);
       // Causal and block-sparse instances mask in a pass of their own after
-      // P and dS (fewer registers live there); the others per element.
+      // P and dS, the others per element: at d = 128 each form spills fewer
+      // registers in the instances that use it.
       constexpr bool kMaskPass = CAUSAL || SPARSE;
       if constexpr (MODS) {
         // The score variants, as in the dQ kernel; row
