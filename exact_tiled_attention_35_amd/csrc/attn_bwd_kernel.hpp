@@ -347,12 +347,14 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         const bool mmask = need_mask || (mods.left >= 0 && qw0 + 31 + diag - j0 > mods.left) ||
                            (mods.right >= 0 && j0 + BN - 1 - qw0 - diag > mods.right);
         const int fd = my_q + diag - j0 - 4 * hh;  // distance at kb = r = 0
+        const float fdf = (float)fd;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int d = fd - (kb * 32 + 8 * (r >> 2) + (r & 3));
-            const float base = kAlibi ? __builtin_fmaf(-slope_l2, __builtin_fabsf((float)d), -lse2) : -lse2;
+            // distance as fp32 (exact: far below 2^24)
+            const float d = fdf - (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
+            const float base = kAlibi ? __builtin_fmaf(-slope_l2, __builtin_fabsf(d), -lse2) : -lse2;
             float p, gd = 1.f;
             if constexpr (kCap) {
               const float th =
@@ -694,6 +696,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         const bool mmask = need_mask || (mods.left >= 0 && i0 + BQ - 1 + diag - kw0 > mods.left) ||
                            (mods.right >= 0 && kw0 + 31 - i0 - diag > mods.right);
         const int fd = i0 + diag - my_k + 4 * hh;  // distance at qb = g = e = 0
+        const float fdf = (float)fd;
         const float slope_l2 = slope * kLog2e;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
@@ -705,9 +708,9 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g + e;
-              const int d = fd + (32 * qb + 8 * g + e);
+              const float d = fdf + (float)(32 * qb + 8 * g + e);  // exact in fp32
               const float nl = l4[e] * -kLog2e;
-              const float base = kAlibi ? __builtin_fmaf(-slope_l2, __builtin_fabsf((float)d), nl) : nl;
+              const float base = kAlibi ? __builtin_fmaf(-slope_l2, __builtin_fabsf(d), nl) : nl;
               float p, gd = 1.f;
               if constexpr (kCap) {
                 const float th =
