@@ -388,23 +388,31 @@ def attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
 
 class _Attention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, softmax_scale, causal):
-        out, lse = attn_fwd(q, k, v, softmax_scale, causal)
+    def forward(ctx, q, k, v, softmax_scale, causal, window, alibi_slopes, softcap):
+        out, lse = attn_fwd(q, k, v, softmax_scale, causal, window=window,
+                            alibi_slopes=alibi_slopes, softcap=softcap)
         ctx.save_for_backward(q, k, v, out, lse)
         ctx.softmax_scale, ctx.causal = softmax_scale, causal
+        ctx.window, ctx.alibi_slopes, ctx.softcap = window, alibi_slopes, softcap
         return out
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, out, lse = ctx.saved_tensors
-        dq, dk, dv, _ = attn_bwd(q, k, v, out, dout.contiguous(), lse, ctx.softmax_scale, ctx.causal)
-        return dq, dk, dv, None, None
+        dq, dk, dv, _ = attn_bwd(q, k, v, out, dout.contiguous(), lse, ctx.softmax_scale, ctx.causal,
+                                 window=ctx.window, alibi_slopes=ctx.alibi_slopes,
+                                 softcap=ctx.softcap)
+        return dq, dk, dv, None, None, None, None, None
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-              softmax_scale: float | None = None, causal: bool = False) -> torch.Tensor:
-    """Exact attention with autograd: ``attn_fwd`` forward, ``attn_bwd`` backward."""
-    return _Attention.apply(q, k, v, softmax_scale, causal)
+              softmax_scale: float | None = None, causal: bool = False, *,
+              window: tuple = (-1, -1), alibi_slopes: torch.Tensor | None = None,
+              softcap: float = 0.0) -> torch.Tensor:
+    """Exact attention with autograd: ``attn_fwd`` forward, ``attn_bwd``
+    backward, with the same score variants (sliding ``window``, ALiBi
+    ``alibi_slopes`` [Hq] fp32 -- constants, no gradient -- and ``softcap``)."""
+    return _Attention.apply(q, k, v, softmax_scale, causal, tuple(window), alibi_slopes, softcap)
 
 
 def attn_fwd_ext_ptr(q: int, k: int, v: int, out: int, lse: int, B: int, Hq: int, Hkv: int,

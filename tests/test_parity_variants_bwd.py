@@ -122,6 +122,22 @@ def test_variant_backward_large_logits(cap):
     check_delta(delta, want[3], do, out)
 
 
+def test_autograd_wrapper_with_variants_matches_entry_points():
+    from exact_tiled_attention_35_amd import attention, attn_bwd, attn_fwd
+
+    q, k, v = (x.cuda() for x in make_qkv(1, 200, 230, 4, 2, 128, "bf16", 1.0, 1595))
+    do = make_qkv(1, 200, 230, 4, 2, 128, "bf16", 1.0, 1596)[0].cuda()
+    sl = slopes_for(4).cuda()
+    kw = dict(window=(64, 8), alibi_slopes=sl, softcap=20.0)
+    qa, ka, va = (x.clone().requires_grad_(True) for x in (q, k, v))
+    o = attention(qa, ka, va, None, True, **kw)
+    o.backward(do)
+    out, lse = attn_fwd(q, k, v, None, True, **kw)
+    dq, dk, dv, _ = attn_bwd(q, k, v, out, do, lse, None, True, **kw)
+    assert torch.equal(o.detach(), out)
+    assert torch.equal(qa.grad, dq) and torch.equal(ka.grad, dk) and torch.equal(va.grad, dv)
+
+
 def test_variant_backward_is_deterministic():
     B, Hq, Hkv, Nq, Nk, d, dt, causal, window, alibi, cap = CASES[4]
     q, k, v = make_qkv(B, Nq, Nk, Hq, Hkv, d, dt, 1.0, 1590)
