@@ -144,36 +144,229 @@ def measured_traffic(workload_name: str, op: str = "fwd"):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, budget_s: float):
-    """Time the fp64 oracle head by head on this host until ``budget_s`` is spent."""
-    import numpy as np
 
-    import oracle
+def host_cores() -> int:
+    """Cores this process may run on (its CPU affinity)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux
+        return os.cpu_count() or 1
 
+
+def blas_threads_in_use() -> int:
     try:
         from threadpoolctl import threadpool_info
 
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:  # pragma: no cover - informational only
-        blas_threads = os.cpu_count() or 1
+        return host_cores()
+
+
+def host_info(op: str = "fwd") -> dict:
+    """What ran where: host cores, ROCm / HIP / torch versions, the kernel
+    sources' hash and, where a git checkout is present, its revision."""
+    import subprocess
+
+    import torch
+
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    rev = None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"],
+                           capture_output=True, text=True, timeout=10)
+        if r.returncode == 0:
+            rev = r.stdout.strip()
+            d = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"],
+                               capture_output=True, text=True, timeout=10)
+            if d.returncode == 0 and d.stdout.strip():
+                rev += "+modified"
+    except (OSError, subprocess.SubprocessError):
+        pass
+    src = op if op in OP_SOURCES else "fwd"
+    return {"cores": host_cores(), "rocm": rocm, "hip_runtime": torch.version.hip,
+            "torch": torch.__version__, "git_rev": rev,
+            "kernel_source_hash": kernel_source_hash(src)}
+
+
+def launch_stats(kernel_ms) -> dict:
+    """Median, min and max of the per-launch event times (microseconds); every
+    launch's time goes to stderr, so that a clock ramp over the timed steps
+    can be told apart from a slower box."""
+    us = sorted(1e3 * t for t in kernel_ms)
+    n = len(us)
+    med = us[n // 2] if n % 2 else 0.5 * (us[n // 2 - 1] + us[n // 2])
+    log("[bench] per-launch us, in launch order: " + " ".join(f"{1e3 * t:.1f}" for t in kernel_ms))
+    return {"median_us": round(med, 2), "min_us": round(us[0], 2), "max_us": round(us[-1], 2)}
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock and socket power through amdsmi's GPU
+    metrics on a background thread while the timed steps run.  The metrics
+    are the firmware's running averages; the samples say what clock the
+    kernels met.  Everything here is best effort: without amdsmi, or where a
+    field is missing, the summary says so and timing is unaffected."""
+
+    FIELDS = ("current_gfxclk", "average_gfxclk_frequency", "current_socket_power",
+              "average_socket_power", "temperature_hotspot")
+
+    def __init__(self, interval_s: float = 0.001):
+        self.interval_s = interval_s
+        self.samples = []
+        self.error = None
+        self._stop = None
+        self._thread = None
+        self._handle = None
+        self._amdsmi = None
+
+    def __enter__(self):
+        import threading
+
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if not handles:
+                raise RuntimeError("no GPU handle")
+            self._amdsmi, self._handle = amdsmi, handles[0]
+            self._read()  # one sample before the steps
+        except Exception as e:  # pragma: no cover - depends on the box
+            self.error = f"{type(e).__name__}: {e}"
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                self._read()
+                self._stop.wait(self.interval_s)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def _read(self):
+        try:
+            m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        except Exception as e:  # pragma: no cover - depends on the box
+            self.error = f"{type(e).__name__}: {e}"
+            return
+        rec = {"t": time.perf_counter()}
+        for k in self.FIELDS:
+            v = m.get(k)
+            if isinstance(v, (int, float)) and v not in (0xFFFF, 0xFFFFFFFF):
+                rec[k] = float(v)
+        clks = m.get("current_gfxclks")
+        if isinstance(clks, (list, tuple)):
+            vals = [float(c) for c in clks if isinstance(c, (int, float)) and 0 < c < 0xFFFF]
+            if vals:
+                rec["xcd_gfxclk_mean"] = sum(vals) / len(vals)
+        self.samples.append(rec)
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join(timeout=2.0)
+        if self._amdsmi is not None:
+            try:
+                self._amdsmi.amdsmi_shut_down()
+            except Exception:  # pragma: no cover
+                pass
+        return False
+
+    def summary(self, t0: float, t1: float, achieved: float, peak: float, nominal_mhz: float = 2400.0):
+        """Clock during [t0, t1] (host perf_counter times of the timed region)
+        and the fraction of the peak scaled to that clock."""
+        inside = [r for r in self.samples if t0 <= r["t"] <= t1]
+        out = {"source": "amdsmi GPU metrics, sampled on a host thread during the timed steps",
+               "samples_in_timed_region": len(inside), "nominal_mhz": nominal_mhz}
+        if self.error:
+            out["error"] = self.error
+        use = inside or self.samples[-1:]
+        if not inside and use:
+            out["note"] = "no sample fell inside the timed region; the last one is reported"
+        for key in ("xcd_gfxclk_mean", "current_gfxclk", "average_gfxclk_frequency"):
+            vals = [r[key] for r in use if key in r]
+            if vals:
+                out["gfxclk_mhz"] = round(sum(vals) / len(vals), 1)
+                out["gfxclk_mhz_min"] = round(min(vals), 1)
+                out["gfxclk_mhz_max"] = round(max(vals), 1)
+                out["gfxclk_field"] = key
+                out["frac_of_peak_at_this_clock"] = round(
+                    achieved / (peak * out["gfxclk_mhz"] / nominal_mhz), 4)
+                break
+        for key in ("current_socket_power", "average_socket_power"):
+            vals = [r[key] for r in use if key in r]
+            if vals:
+                out["socket_power_w"] = round(sum(vals) / len(vals), 1)
+                break
+        vals = [r["temperature_hotspot"] for r in use if "temperature_hotspot" in r]
+        if vals:
+            out["hotspot_c"] = round(max(vals), 1)
+        return out
+
+def cpu_baseline(w, q, k, v, budget_s: float, out=None, lse=None):
+    """Time the fp64 oracle head by head (all rows of each) on this host until
+    ``budget_s`` is spent, with BLAS on every core of the process's affinity.
+    Given this run's GPU ``out`` / ``lse`` (CPU copies), also compare them
+    with the oracle on every head it evaluated (outside the oracle's timing):
+    max-abs and mean-abs over all those output elements, the logsumexp error
+    over their rows, and the floor max |dtype(O_64) - O_64|."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    cores = host_cores()
     heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
-    done = 0
-    t0 = time.perf_counter()
-    for (b, h) in heads:
-        oracle.attention_rows(q, k, v, w.scale, w.causal, b, h, np.arange(w.Nq))
-        done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+    done, t_oracle = 0, 0.0
+    par = {"max_abs": 0.0, "sum_abs": 0.0, "n": 0, "lse_abs": 0.0, "floor": 0.0}
+    with threadpool_limits(limits=cores, user_api="blas"):
+        blas = blas_threads_in_use()
+        for (b, h) in heads:
+            t0 = time.perf_counter()
+            O, L = oracle.attention_rows(q, k, v, w.scale, w.causal, b, h, np.arange(w.Nq))
+            t_oracle += time.perf_counter() - t0
+            done += 1
+            if out is not None:
+                err = np.abs(out[b, :, h, :].double().numpy() - O)
+                par["max_abs"] = max(par["max_abs"], float(err.max()))
+                par["sum_abs"] += float(err.sum())
+                par["n"] += err.size
+                fin = np.isfinite(L)
+                lg = lse[b, h].double().numpy()
+                if fin.any():
+                    par["lse_abs"] = max(par["lse_abs"], float(np.abs(lg[fin] - L[fin]).max()))
+                rounded = torch.from_numpy(O).to(out.dtype).double().numpy()
+                par["floor"] = max(par["floor"], float(np.abs(rounded - O).max()))
+            if t_oracle >= budget_s:
+                break
     f = flops(w) * done / len(heads)
-    return {
-        "value": f / dt / 1e12,
+    res = {
+        "value": f / t_oracle / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(blas_threads),
+        "cores": cores,
+        "blas_threads": blas,
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} (batch, head) pairs, all {w.Nq} query rows each, "
-                  f"fp64 NumPy, {dt:.1f} s wall",
+                  f"fp64 NumPy, {t_oracle:.1f} s of oracle time",
     }
+    if out is not None:
+        res["parity"] = {
+            "compared": f"this run's GPU output on every row of the {done} oracle heads",
+            "max_abs": par["max_abs"], "mean_abs": par["sum_abs"] / max(1, par["n"]),
+            "lse_abs": par["lse_abs"], "floor": par["floor"],
+            "tolerance": {"max_abs": 1e-2, "mean_abs": 1e-3, "lse_abs": 1e-3},
+        }
+        res["parity"]["pass"] = bool(res["parity"]["max_abs"] <= 1e-2
+                                     and res["parity"]["mean_abs"] <= 1e-3
+                                     and res["parity"]["lse_abs"] <= 1e-3)
+    return res
 
 
 def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
@@ -182,12 +375,6 @@ def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - informational only
-        blas_threads = os.cpu_count() or 1
     G = w.Hq // w.Hkv
     groups = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
     done = 0
@@ -204,7 +391,8 @@ def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
     return {
         "value": f / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(blas_threads),
+        "cores": host_cores(),
+        "blas_threads": blas_threads_in_use(),
         "kind": "oracle",
         "sample": f"{done} of {len(groups)} (batch, KV head) groups, all rows, fp64 NumPy, "
                   f"{dt:.1f} s wall",
@@ -215,12 +403,6 @@ def cpu_baseline_decode(w, q, kc, vc, budget_s: float):
     """Time the fp64 oracle on whole sequences of the decode workload."""
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - informational only
-        blas_threads = os.cpu_count() or 1
     done = 0
     t0 = time.perf_counter()
     for b in range(w.B):
@@ -232,7 +414,8 @@ def cpu_baseline_decode(w, q, kc, vc, budget_s: float):
     return {
         "value": decode_bytes(w) * done / w.B / dt / 1e9,
         "unit": "GB/s",
-        "cores": int(blas_threads),
+        "cores": host_cores(),
+        "blas_threads": blas_threads_in_use(),
         "kind": "oracle",
         "sample": f"{done} of {w.B} sequences, every query head, fp64 NumPy, {dt:.1f} s wall",
     }
@@ -459,16 +642,19 @@ def main():
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()  # one rank: the barrier is this synchronisation
-    t0 = time.perf_counter()
-    for i in range(K):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for i in range(K):
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    wall = t1 - t0
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_kernel_s = sum(kernel_ms) / K / 1e3
     ms_per_step = wall / K * 1e3
+    per_launch = launch_stats(kernel_ms)
 
     F = flops(w) if args.op == "fwd" else bwd_flops(w)
     if variants:
@@ -478,7 +664,8 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     traffic = None if variants else measured_traffic(w.name, args.op)
     log(f"[bench] {K} steps: {ms_per_step:.4f} ms/step wall, kernel avg {avg_kernel_s*1e6:.1f} us "
-        f"(min {min(kernel_ms)*1e3:.1f} us), {achieved:.1f} TFLOP/s = {100*achieved/peak:.1f}% of peak")
+        f"(median {per_launch['median_us']:.1f}, min {per_launch['min_us']:.1f} us), "
+        f"{achieved:.1f} TFLOP/s = {100*achieved/peak:.1f}% of peak")
 
     result = {
         "metric": METRIC if args.op == "fwd" else METRIC_BWD,
@@ -505,7 +692,13 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes": algorithmic_bytes(w) if args.op == "fwd" else bwd_algorithmic_bytes(w),
             "kernel_avg_us": round(avg_kernel_s * 1e6, 2),
+            "kernel_median_us": per_launch["median_us"],
+            "kernel_min_us": per_launch["min_us"],
+            "kernel_max_us": per_launch["max_us"],
+            "achieved_at_median": round(F / (per_launch["median_us"] * 1e-6) / 1e12, 3),
         },
+        "clock": clock.summary(t0, t1, achieved, peak),
+        "host": host_info(args.op),
         "cpu_baseline": None,
         "context": "FlexAttention with the FA4 backend reports 1.2x-3.2x speedups on NVIDIA "
                    "Hopper/Blackwell (liora.io news item); other hardware, not a target",
@@ -535,7 +728,9 @@ def main():
         if args.op == "fwd" and variants:
             result["cpu_baseline"] = None  # the oracle baseline is timed on the plain forward
         elif args.op == "fwd":
-            result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+            # the output of the last timed step, compared with the oracle
+            out_c, lse_c = out.cpu(), lse.cpu()
+            result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget, out_c, lse_c)
         else:
             result["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do, args.cpu_budget)
     print(json.dumps(result), flush=True)
@@ -605,15 +800,18 @@ def bench_decode(args, w, dev):
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for i in range(K):
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    wall = t1 - t0
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_s = sum(kernel_ms) / K / 1e3
+    per_launch = launch_stats(kernel_ms)
     nbytes = decode_bytes(w)
     value = nbytes / (wall / K) / 1e9
     achieved = nbytes / avg_s / 1e9
@@ -648,8 +846,12 @@ def bench_decode(args, w, dev):
             "traffic": measured_traffic(w.name, "decode"),
             "algorithmic_bytes": nbytes,
             "kernel_avg_us": round(avg_s * 1e6, 2),
+            "kernel_median_us": per_launch["median_us"],
+            "kernel_min_us": per_launch["min_us"],
             "unit_of_work": "one attn_decode call: append, split attention and merge kernels",
         },
+        "clock": clock.summary(t0, t1, achieved, peak),
+        "host": host_info("decode"),
         "cpu_baseline": None,
         "context": "KV-cache decode; the headline metric is the forward (--op fwd)",
     }
@@ -673,12 +875,6 @@ def cpu_baseline_varlen(wl, lens, q, k, v, scale, budget_s: float):
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - informational only
-        blas_threads = os.cpu_count() or 1
     starts = [0]
     for n in lens:
         starts.append(starts[-1] + n)
@@ -699,7 +895,8 @@ def cpu_baseline_varlen(wl, lens, q, k, v, scale, budget_s: float):
     return {
         "value": f / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(blas_threads),
+        "cores": host_cores(),
+        "blas_threads": blas_threads_in_use(),
         "kind": "oracle",
         "sample": f"{done} of {len(lens) * wl['H']} (sequence, head) pairs in packing order, all "
                   f"rows each, fp64 NumPy, {dt:.1f} s wall",
@@ -744,15 +941,18 @@ def bench_varlen(args, wl, backward=False):
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for i in range(K):
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    wall = t1 - t0
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_s = sum(kernel_ms) / K / 1e3
+    per_launch = launch_stats(kernel_ms)
     F = sum((10.0 if backward else 4.0) * H * d * visible_pairs(n, n, causal, -1, -1) for n in lens)
     value = F / (wall / K) / 1e12
     achieved = F / avg_s / 1e12
@@ -792,7 +992,11 @@ def bench_varlen(args, wl, backward=False):
             "traffic": None,
             "algorithmic_bytes": nbytes,
             "kernel_avg_us": round(avg_s * 1e6, 2),
+            "kernel_median_us": per_launch["median_us"],
+            "kernel_min_us": per_launch["min_us"],
         },
+        "clock": clock.summary(t0, t1, achieved, peak),
+        "host": host_info("bwd" if backward else "fwd"),
         "cpu_baseline": None,
         "context": ("packed variable-length backward" if backward else
                     "packed variable-length forward") + "; the headline metric is the forward (--op fwd)",
@@ -827,12 +1031,6 @@ def cpu_baseline_blocksparse(w, q, k, v, mask, counts, budget_s: float):
     import oracle
     from attn_workloads import BLOCK
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - informational only
-        blas_threads = os.cpu_count() or 1
     m = mask.numpy() != 0
     done, f = 0, 0.0
     t0 = time.perf_counter()
@@ -850,7 +1048,8 @@ def cpu_baseline_blocksparse(w, q, k, v, mask, counts, budget_s: float):
     return {
         "value": f / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(blas_threads),
+        "cores": host_cores(),
+        "blas_threads": blas_threads_in_use(),
         "kind": "oracle",
         "sample": f"{done} of {w.B * w.Hq} (batch, head) pairs, all rows each, fp64 NumPy, "
                   f"{dt:.1f} s wall",
@@ -898,15 +1097,18 @@ def bench_blocksparse(args, name, backward=False):
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for i in range(K):
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    wall = t1 - t0
     kernel_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
     avg_s = sum(kernel_ms) / K / 1e3
+    per_launch = launch_stats(kernel_ms)
     counts = blocksparse_pair_counts(w.Nq, w.Nk, w.causal, BLOCK)
     kept_blocks = mask.numpy() != 0
     pairs = float((kept_blocks * counts[None, None]).sum())
@@ -948,7 +1150,11 @@ def bench_blocksparse(args, name, backward=False):
             "frac": round(achieved / peak, 4),
             "traffic": None,
             "kernel_avg_us": round(avg_s * 1e6, 2),
+            "kernel_median_us": per_launch["median_us"],
+            "kernel_min_us": per_launch["min_us"],
         },
+        "clock": clock.summary(t0, t1, achieved, peak),
+        "host": host_info("bwd" if backward else "fwd"),
         "cpu_baseline": None,
         "context": ("block-sparse backward (the dQ and dK/dV kernels)" if backward else
                     "block-sparse forward") + "; the headline metric is the plain forward (--op fwd)",

@@ -109,7 +109,9 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     left, right = (int(x) for x in window)
-    variants = left >= 0 or right >= 0 or alibi_slopes is not None or softcap != 0.0
+    # Any window other than (-1, -1) goes to the variant entry point, which
+    # rejects bounds below -1 with ATTN_ERR_BAD_ARGUMENT.
+    variants = (left, right) != (-1, -1) or alibi_slopes is not None or softcap != 0.0
     if alibi_slopes is not None:
         _check_like("alibi_slopes", alibi_slopes, (Hq,), torch.float32, q.device)
     with torch.cuda.device(q.device):
@@ -391,17 +393,20 @@ class _Attention(torch.autograd.Function):
     def forward(ctx, q, k, v, softmax_scale, causal, window, alibi_slopes, softcap):
         out, lse = attn_fwd(q, k, v, softmax_scale, causal, window=window,
                             alibi_slopes=alibi_slopes, softcap=softcap)
-        ctx.save_for_backward(q, k, v, out, lse)
+        # The slopes are saved like the tensors, so that autograd's version
+        # check catches an in-place change between the forward and backward.
+        extra = (alibi_slopes,) if alibi_slopes is not None else ()
+        ctx.save_for_backward(q, k, v, out, lse, *extra)
         ctx.softmax_scale, ctx.causal = softmax_scale, causal
-        ctx.window, ctx.alibi_slopes, ctx.softcap = window, alibi_slopes, softcap
+        ctx.window, ctx.softcap = window, softcap
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v, out, lse = ctx.saved_tensors
+        q, k, v, out, lse, *extra = ctx.saved_tensors
+        slopes = extra[0] if extra else None
         dq, dk, dv, _ = attn_bwd(q, k, v, out, dout.contiguous(), lse, ctx.softmax_scale, ctx.causal,
-                                 window=ctx.window, alibi_slopes=ctx.alibi_slopes,
-                                 softcap=ctx.softcap)
+                                 window=ctx.window, alibi_slopes=slopes, softcap=ctx.softcap)
         return dq, dk, dv, None, None, None, None, None
 
 
@@ -453,7 +458,9 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: f
             or lse.device != q.device:
         raise ValueError("lse must be a contiguous fp32 tensor [B, Hq, Nq]")
     left, right = (int(x) for x in window)
-    variants = left >= 0 or right >= 0 or alibi_slopes is not None or softcap != 0.0
+    # Any window other than (-1, -1) goes to the variant entry point, which
+    # rejects bounds below -1 with ATTN_ERR_BAD_ARGUMENT.
+    variants = (left, right) != (-1, -1) or alibi_slopes is not None or softcap != 0.0
     if alibi_slopes is not None:
         _check_like("alibi_slopes", alibi_slopes, (Hq,), torch.float32, q.device)
     with torch.cuda.device(q.device):

@@ -1,8 +1,8 @@
 """Build the HIP library in-tree: ``python -m exact_tiled_attention_35_amd.build``.
 
 Compiles ``csrc/attn_api.hip``, ``csrc/attn_bwd_api.hip`` and
-``csrc/attn_decode_api.hip`` (C ABI + kernels) for gfx950 into
-``libattn.so`` next to this file, and writes the compiler's per-kernel
+``csrc/attn_decode_api.hip`` (C ABI + kernels) for gfx950, one hipcc per
+source in parallel, and links them into ``libattn.so`` next to this file, and writes the compiler's per-kernel
 resource report (VGPRs, AGPRs, LDS, scratch, occupancy) to
 ``_build/resource_usage.txt``.
 """
@@ -54,18 +54,35 @@ def compile_flags() -> list:
 
 
 def build_library(verbose: bool = False) -> str:
+    """Compile each source to an object in parallel (one hipcc per source),
+    then link the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
     os.makedirs(BUILD_DIR, exist_ok=True)
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc()] + compile_flags() + ["-Rpass-analysis=kernel-resource-usage"] + SOURCES + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    proc = subprocess.run(cmd, capture_output=True, text=True)
+    flags = [f for f in compile_flags() if f != "-shared"]
+    objs = [os.path.join(BUILD_DIR, os.path.basename(src) + ".o") for src in SOURCES]
+
+    def compile_one(src, obj):
+        cmd = [hipcc()] + flags + ["-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        return subprocess.run(cmd, capture_output=True, text=True)
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        procs = list(ex.map(compile_one, SOURCES, objs))
     report = os.path.join(BUILD_DIR, "resource_usage.txt")
     with open(report, "w") as f:
-        f.write(proc.stderr)
-    if proc.returncode != 0:
-        errors = [ln for ln in proc.stderr.splitlines() if "error" in ln]
-        raise RuntimeError("hipcc failed:\n" + "\n".join(errors[:40] or proc.stderr.splitlines()[-40:]))
+        for p in procs:
+            f.write(p.stderr)
+    for p in procs:
+        if p.returncode != 0:
+            errors = [ln for ln in p.stderr.splitlines() if "error" in ln]
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errors[:40] or p.stderr.splitlines()[-40:]))
+    tmp = LIB_PATH + ".tmp"
+    link = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp],
+                          capture_output=True, text=True)
+    if link.returncode != 0:
+        raise RuntimeError("link failed:\n" + link.stderr[-4000:])
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -306,10 +306,18 @@ int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Ncap, int d);
 /* Workspace bytes attn_decode needs for `num_splits` splits (0 for one split). */
 size_t attn_decode_workspace_size(int B, int Hq, int Nq, int d, int num_splits);
 
-/* A fixed, static message for a status code (never NULL). */
+/* A fixed, static message for a status code (never NULL; unknown codes get a
+ * message of their own).  tokenwerk.de's "FlashAttention" page (section
+ * "Fehler und Leistungsversprechen richtig einordnen") asks that a failing
+ * call's exact message be recorded: each code maps to one unchanging string,
+ * so a caller can log it verbatim and compare it across runs.  The pointer
+ * refers to static storage; the caller does not free it. */
 const char* attn_status_string(int status);
 
-/* Library version and build description, e.g. "0.1.0 gfx950". */
+/* Library version and build description, e.g. "0.2.0 gfx950 ...".  The same
+ * page asks that a performance claim name what was measured; the version
+ * string identifies the library build behind a measurement.  Static storage,
+ * never NULL. */
 const char* attn_version(void);
 
 #ifdef __cplusplus

@@ -171,3 +171,41 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_launch_stats_median_min_max(capsys):
+    st = bench.launch_stats([0.5, 0.7, 0.4, 0.6])  # milliseconds
+    assert st == {"median_us": 550.0, "min_us": 400.0, "max_us": 700.0}
+    assert bench.launch_stats([0.3, 0.1, 0.2])["median_us"] == 200.0
+    # every launch, in launch order, goes to stderr
+    assert "500.0 700.0 400.0 600.0" in capsys.readouterr().err
+
+
+def test_clock_summary_uses_samples_inside_the_timed_region():
+    c = bench.ClockSampler()
+    c.samples = [
+        {"t": 0.5, "current_gfxclk": 2400.0},  # before the timed region: ignored
+        {"t": 1.1, "current_gfxclk": 1600.0, "current_socket_power": 1300.0},
+        {"t": 1.4, "current_gfxclk": 1800.0, "current_socket_power": 1400.0},
+        {"t": 2.5, "current_gfxclk": 2400.0},  # after it: ignored
+    ]
+    s = c.summary(1.0, 2.0, achieved=1000.0, peak=2500.0)
+    assert s["samples_in_timed_region"] == 2
+    assert s["gfxclk_mhz"] == 1700.0 and s["gfxclk_mhz_min"] == 1600.0
+    assert s["socket_power_w"] == 1350.0
+    # 1000 TFLOP/s against 2500 * 1700 / 2400
+    assert s["frac_of_peak_at_this_clock"] == round(1000.0 / (2500.0 * 1700.0 / 2400.0), 4)
+    # per-XCD clocks win over the single clock field when present
+    c.samples = [{"t": 1.5, "current_gfxclk": 2000.0, "xcd_gfxclk_mean": 1650.0}]
+    assert c.summary(1.0, 2.0, 1000.0, 2500.0)["gfxclk_mhz"] == 1650.0
+    # nothing inside: the last sample, flagged
+    c.samples = [{"t": 0.2, "current_gfxclk": 2100.0}]
+    s = c.summary(1.0, 2.0, 1000.0, 2500.0)
+    assert s["gfxclk_mhz"] == 2100.0 and "note" in s
+
+
+def test_host_info_names_cores_and_versions():
+    info = bench.host_info("fwd")
+    assert info["cores"] == len(os.sched_getaffinity(0))
+    assert info["kernel_source_hash"] == bench.kernel_source_hash("fwd")
+    assert "torch" in info and "rocm" in info

@@ -163,3 +163,33 @@ def test_headline_shape_softcap_and_alibi_full_size_head():
     base = lowp_backward_variants(sl(q), sl(k), sl(v), sl(do), sl(out), w.scale, w.causal, (-1, -1),
                                   slopes[h:h + 1], 30.0)
     check_grads((sl(dq), sl(dk), sl(dv)), want[:3], base, "headline softcap+alibi")
+
+
+def test_binding_sends_every_window_to_the_checked_entry_point():
+    # A window bound below -1 is an error of the C ABI; the binding must not
+    # take (-2, -2) for "no window" and run the plain kernel.
+    from exact_tiled_attention_35_amd import attn_bwd, attn_fwd
+    from exact_tiled_attention_35_amd.attention import AttnError
+
+    q, k, v = (t.cuda() for t in make_qkv(1, 64, 64, 2, 2, 64, "bf16", 1.0, 611))
+    for win in ((-2, -2), (-2, -1), (-1, -5)):
+        with pytest.raises(AttnError) as e:
+            attn_fwd(q, k, v, 0.125, False, window=win)
+        assert "BAD_ARGUMENT" in str(e.value)
+    out, lse = attn_fwd(q, k, v, 0.125, False)
+    with pytest.raises(AttnError):
+        attn_bwd(q, k, v, out, torch.ones_like(out), lse, 0.125, False, window=(-2, -2))
+
+
+def test_autograd_detects_slopes_changed_in_place():
+    # The ALiBi slopes are saved for the backward like the tensors: changing
+    # them in place between forward and backward is an error, not silently
+    # wrong gradients.
+    from exact_tiled_attention_35_amd import attention
+
+    q, k, v = (t.cuda().requires_grad_() for t in make_qkv(1, 64, 64, 2, 2, 64, "bf16", 1.0, 612))
+    slopes = slopes_for(2).cuda()
+    out = attention(q, k, v, 0.125, True, alibi_slopes=slopes)
+    slopes.mul_(2.0)
+    with pytest.raises(RuntimeError, match="modified by an inplace operation"):
+        out.float().sum().backward()
