@@ -16,6 +16,8 @@ from .attention import (  # noqa: F401
     attn_bwd_varlen,
     attn_bwd_varlen_ptr,
     attn_decode,
+    attn_decode_noalloc,
+    attn_decode_noalloc_ptr,
     attn_decode_num_splits,
     attn_decode_ptr,
     attn_decode_workspace_size,

@@ -24,6 +24,10 @@ ATTN_ERR_NO_DEVICE = -9
 ATTN_ERR_LAUNCH = -10
 ATTN_ERR_WORKSPACE = -11
 ATTN_ERR_BAD_ARGUMENT = -12
+ATTN_ERR_SCRATCH_LIMIT = -13
+
+# attn_decode_noalloc's scratch array, per GPU (include/attn.h)
+ATTN_DECODE_SCRATCH_BYTES = 8 << 20
 
 # attn_dtype values.
 ATTN_DTYPE_F16 = 0
@@ -61,6 +65,8 @@ def load() -> ctypes.CDLL:
     lib.attn_bwd_ext.restype = ci
     lib.attn_decode.argtypes = [vp] * 9 + [ctypes.c_size_t] + [ci] * 7 + [cf, ci, ci, ci, vp]
     lib.attn_decode.restype = ci
+    lib.attn_decode_noalloc.argtypes = [vp] * 8 + [ci] * 7 + [cf, ci, ci, ci, vp]
+    lib.attn_decode_noalloc.restype = ci
     lib.attn_decode_num_splits.argtypes = [ci] * 6
     lib.attn_decode_num_splits.restype = ci
     lib.attn_decode_workspace_size.argtypes = [ci] * 5

@@ -193,6 +193,59 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out, lse
 
 
+def attn_decode_noalloc_ptr(q: int, k_cache: int, v_cache: int, cache_seqlens: int, k_new: int,
+                            v_new: int, out: int, lse: int, B: int, Hq: int, Hkv: int, Nq: int,
+                            Ncap: int, Nnew: int, d: int, scale: float, causal: bool, dtype: int,
+                            num_splits: int = 0, stream: int = 0) -> int:
+    """attn_decode_noalloc with raw integer pointers; returns the attn_status."""
+    return _lib.load().attn_decode_noalloc(q or None, k_cache or None, v_cache or None,
+                                           cache_seqlens or None, k_new or None, v_new or None,
+                                           out or None, lse or None, int(B), int(Hq), int(Hkv),
+                                           int(Nq), int(Ncap), int(Nnew), int(d), float(scale),
+                                           int(bool(causal)), int(dtype), int(num_splits),
+                                           stream or None)
+
+
+def attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        cache_seqlens: torch.Tensor, k_new: torch.Tensor | None = None,
+                        v_new: torch.Tensor | None = None, softmax_scale: float | None = None,
+                        causal: bool = True, num_splits: int = 0, out: torch.Tensor | None = None,
+                        lse: torch.Tensor | None = None):
+    """``attn_decode`` through the entry point that allocates nothing: the
+    split partials live in the library's own per-GPU scratch array.  Pass
+    ``out`` and ``lse`` to keep this call free of allocations as well (they
+    are allocated here otherwise).  Returns (out, lse)."""
+    B, Nq, Hq, Hkv, Ncap, d = _check_qkv(q, k_cache, v_cache)
+    _check_like("cache_seqlens", cache_seqlens, (B,), torch.int32, q.device)
+    Nnew = 0
+    if k_new is not None or v_new is not None:
+        if k_new is None or v_new is None:
+            raise ValueError("k_new and v_new go together")
+        Nnew = k_new.shape[1]
+        _check_like("k_new", k_new, (B, Nnew, Hkv, d), q.dtype, q.device)
+        _check_like("v_new", v_new, (B, Nnew, Hkv, d), q.dtype, q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check_like("out", out, tuple(q.shape), q.dtype, q.device)
+    _check_like("lse", lse, (B, Hq, Nq), torch.float32, q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        code = attn_decode_noalloc_ptr(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                       cache_seqlens.data_ptr(),
+                                       k_new.data_ptr() if Nnew else 0,
+                                       v_new.data_ptr() if Nnew else 0, out.data_ptr(),
+                                       lse.data_ptr(), B, Hq, Hkv, Nq, Ncap, Nnew, d,
+                                       softmax_scale, causal, _DTYPE_CODE[q.dtype], num_splits,
+                                       stream)
+    if code != _lib.ATTN_OK:
+        raise AttnError(code)
+    return out, lse
+
+
 def attn_fwd_varlen_ptr(q: int, k: int, v: int, out: int, lse: int, cu_q: int, cu_k: int, B: int,
                         Hq: int, Hkv: int, total_q: int, total_k: int, max_seqlen_q: int, d: int,
                         scale: float, causal: bool, dtype: int, stream: int = 0) -> int:

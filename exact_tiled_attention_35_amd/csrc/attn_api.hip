@@ -289,6 +289,9 @@ extern "C" const char* attn_status_string(int status) {
     case ATTN_ERR_BAD_ARGUMENT:
       return "ATTN_ERR_BAD_ARGUMENT: window bounds must be >= -1, softcap finite and >= 0, "
              "mask_heads 1 or Hq";
+    case ATTN_ERR_SCRATCH_LIMIT:
+      return "ATTN_ERR_SCRATCH_LIMIT: the split partials exceed the 8 MiB scratch of "
+             "attn_decode_noalloc; use fewer splits, or attn_decode with a workspace";
     default: return "unknown attn status";
   }
 }

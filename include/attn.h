@@ -72,7 +72,8 @@ typedef enum {
   ATTN_ERR_NO_DEVICE = -9,         /* no HIP device, or the current device is not gfx950 */
   ATTN_ERR_LAUNCH = -10,           /* the kernel launch failed                            */
   ATTN_ERR_WORKSPACE = -11,        /* attn_decode: workspace smaller than required       */
-  ATTN_ERR_BAD_ARGUMENT = -12      /* window bound < -1, bad softcap; mask_heads not 1/Hq */
+  ATTN_ERR_BAD_ARGUMENT = -12,     /* window bound < -1, bad softcap; mask_heads not 1/Hq */
+  ATTN_ERR_SCRATCH_LIMIT = -13     /* attn_decode_noalloc: partials exceed its scratch   */
 } attn_status;
 
 /*
@@ -299,6 +300,31 @@ int attn_decode(const void* q, void* k_cache, void* v_cache, const int* cache_se
                 void* workspace, size_t workspace_bytes,
                 int B, int Hq, int Hkv, int Nq, int Ncap, int Nnew, int d,
                 float scale, int causal, int dtype, int num_splits, void* stream);
+
+/*
+ * attn_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, results and validation as
+ * attn_decode, minus workspace and workspace_bytes.  The split partials live
+ * in a device array of ATTN_DECODE_SCRATCH_BYTES inside the library, one per
+ * GPU it runs on, held until the process ends; no call allocates anything.
+ *   num_splits == 0  attn_decode_num_splits' choice, lowered to the largest
+ *                    count whose partials fit the array (1 split needs none);
+ *   num_splits >= 2  ATTN_ERR_SCRATCH_LIMIT when
+ *                    attn_decode_workspace_size(B, Hq, Nq, d, num_splits) >
+ *                    ATTN_DECODE_SCRATCH_BYTES (checked before any HIP call).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs to start at zero: each partial is written
+ * before it is read).  Calls that overlap in time on one GPU race: issue them
+ * on one stream, or order them.  The first call on a device looks up the
+ * array's address on that device (hipGetSymbolAddress); ATTN_ERR_LAUNCH when
+ * that fails.
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)8 << 20)
+int attn_decode_noalloc(const void* q, void* k_cache, void* v_cache, const int* cache_seqlens,
+                        const void* k_new, const void* v_new, void* out, float* lse,
+                        int B, int Hq, int Hkv, int Nq, int Ncap, int Nnew, int d,
+                        float scale, int causal, int dtype, int num_splits, void* stream);
 
 /* The split count attn_decode uses for num_splits == 0 (always >= 1). */
 int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Ncap, int d);

@@ -40,7 +40,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
-    assert names == ["attn_bwd", "attn_bwd_blocksparse", "attn_bwd_ext", "attn_bwd_varlen", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_size",
+    assert names == ["attn_bwd", "attn_bwd_blocksparse", "attn_bwd_ext", "attn_bwd_varlen", "attn_decode",
+                     "attn_decode_noalloc", "attn_decode_num_splits", "attn_decode_workspace_size",
                      "attn_fwd", "attn_fwd_blocksparse", "attn_fwd_ext", "attn_fwd_varlen",
                      "attn_status_string", "attn_version"]
     for n in names:
@@ -50,7 +51,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_messages():
     assert "gfx950" in attn_version()
-    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, -12]
+    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, -12, -13]
     msgs = [attn_status_string(c) for c in codes]
     assert len(set(msgs)) == len(codes)
     assert msgs[0].startswith("ATTN_OK")
@@ -281,6 +282,14 @@ def test_decode_null_pointer(field):
     assert call_dec(**{field: 0}) == _lib.ATTN_ERR_NULL_POINTER
 
 
+# Calls that pass validation reach the device check: where a GPU is visible
+# they would launch kernels on the fake addresses, so they run on GPU-less
+# hosts only.
+NO_GPU = torch.cuda.device_count() == 0
+needs_no_gpu = pytest.mark.skipif(not NO_GPU, reason="would launch kernels on fake addresses")
+
+
+@needs_no_gpu
 def test_decode_optional_pointers():
     # no new rows: k_new / v_new may be NULL; one split: no workspace needed
     assert call_dec(Nnew=0, k_new=0, v_new=0) in (_lib.ATTN_ERR_NO_DEVICE, _lib.ATTN_OK)
@@ -290,12 +299,14 @@ def test_decode_optional_pointers():
         _lib.ATTN_ERR_NO_DEVICE, _lib.ATTN_OK)
 
 
+@needs_no_gpu
 def test_decode_workspace_too_small():
     need = attn_decode_workspace_size(4, 16, 2, 128, 4)
     assert call_dec(workspace_bytes=need - 1) == _lib.ATTN_ERR_WORKSPACE
     assert call_dec(workspace_bytes=need) in (_lib.ATTN_ERR_NO_DEVICE, _lib.ATTN_OK)
 
 
+@needs_no_gpu
 def test_decode_validation_order_and_alignment():
     assert call_dec(q=0, Hkv=3) == _lib.ATTN_ERR_NULL_POINTER
     assert call_dec(Hkv=3, d=100) == _lib.ATTN_ERR_GQA_RATIO
@@ -318,6 +329,74 @@ def test_decode_aliasing():
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a HIP device is visible here")
 def test_decode_no_device_reported_without_gpu():
     assert call_dec() == _lib.ATTN_ERR_NO_DEVICE
+
+
+# ---------------------------------------------------------------------------
+# attn_decode_noalloc (no workspace argument; the library's scratch array)
+# ---------------------------------------------------------------------------
+from exact_tiled_attention_35_amd.attention import attn_decode_noalloc_ptr  # noqa: E402
+
+NOALLOC_ORDER = [n for n in DEC_ORDER if n not in ("workspace", "workspace_bytes")]
+
+
+def call_noalloc(**over):
+    a = dict(GOOD_DEC)
+    a.update(over)
+    return attn_decode_noalloc_ptr(*[a[n] for n in NOALLOC_ORDER])
+
+
+def test_noalloc_scratch_size_is_the_declared_one():
+    with open(os.path.join(ROOT, "include", "attn.h")) as f:
+        m = re.search(r"#define ATTN_DECODE_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.ATTN_DECODE_SCRATCH_BYTES == 8 << 20
+
+
+@pytest.mark.parametrize("field,value", [("B", -1), ("Nq", -1), ("Hq", 0), ("Ncap", 0),
+                                         ("Nnew", 5000), ("num_splits", 129)])
+def test_noalloc_bad_shape(field, value):
+    assert call_noalloc(**{field: value}) == _lib.ATTN_ERR_BAD_SHAPE
+
+
+def test_noalloc_noops():
+    nulls = {n: 0 for n in NOALLOC_ORDER[:8]}
+    assert call_noalloc(B=0, **nulls) == _lib.ATTN_OK
+    assert call_noalloc(Nq=0, Nnew=0, **nulls) == _lib.ATTN_OK
+
+
+@pytest.mark.parametrize("field", ["q", "k_cache", "v_cache", "cache_seqlens", "k_new", "v_new",
+                                   "out", "lse"])
+def test_noalloc_null_pointer(field):
+    assert call_noalloc(**{field: 0}) == _lib.ATTN_ERR_NULL_POINTER
+
+
+def test_noalloc_scratch_limit_before_any_hip_call():
+    # partials of 2 splits: 2 * B*Hq*Nq * (d + 1) * 4 bytes against 8 MiB
+    per_row = (128 + 1) * 4
+    fits = (8 << 20) // (2 * per_row)  # 8128 rows of (batch, head, query)
+    big = dict(B=1, Hq=fits + 1, Hkv=1, Nq=1, num_splits=2, Nnew=0)
+    assert call_noalloc(**big) == _lib.ATTN_ERR_SCRATCH_LIMIT
+    assert call_noalloc(**dict(big, num_splits=64)) == _lib.ATTN_ERR_SCRATCH_LIMIT
+    # the limit is checked in the workspace step of the documented order
+    assert call_noalloc(**dict(big, scale=float("nan"))) == _lib.ATTN_ERR_BAD_SCALE
+    assert call_noalloc(**dict(big, k_cache=KC + 8)) == _lib.ATTN_ERR_SCRATCH_LIMIT
+    assert "8 MiB" in attn_status_string(_lib.ATTN_ERR_SCRATCH_LIMIT)
+
+
+@needs_no_gpu
+def test_noalloc_fitting_sizes_pass_validation():
+    per_row = (128 + 1) * 4
+    fits = (8 << 20) // (2 * per_row)
+    assert call_noalloc(B=1, Hq=fits, Hkv=1, Nq=1, num_splits=2, Nnew=0) == _lib.ATTN_ERR_NO_DEVICE
+    # the library's choice is lowered to what fits instead of failing: here
+    # 32 splits (16.9 MB of partials) for attn_decode
+    assert attn_decode_num_splits(1, 64, 8, 16, 4096, 128) == 32
+    assert attn_decode_workspace_size(1, 64, 16, 128, 32) > (8 << 20)
+    assert call_noalloc(B=1, Hq=64, Hkv=8, Nq=16, Ncap=4096, num_splits=0) == _lib.ATTN_ERR_NO_DEVICE
+    assert call_noalloc(B=1, Hq=64, Hkv=8, Nq=16, Ncap=4096, num_splits=32) == _lib.ATTN_ERR_SCRATCH_LIMIT
+    # one split needs no scratch
+    assert call_noalloc(B=64, Hq=64, Hkv=8, Nq=16, num_splits=1) == _lib.ATTN_ERR_NO_DEVICE
+    assert call_noalloc(k_cache=KC + 8) == _lib.ATTN_ERR_MISALIGNED
+    assert call_noalloc(out=KC) == _lib.ATTN_ERR_ALIASING
 
 
 # ---------------------------------------------------------------------------
