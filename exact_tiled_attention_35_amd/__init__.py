@@ -33,4 +33,4 @@ from .attention import (  # noqa: F401
     attn_version,
 )
 
-__version__ = "0.2.0"
+__version__ = "0.3.0"

@@ -13,6 +13,7 @@
 #include <cstdint>
 
 #include "attn_fwd_kernel.hpp"
+#include "attn_fwd_splitk_kernel.hpp"
 #include "attn_host.hpp"
 
 namespace {
@@ -22,7 +23,8 @@ using eta_host::check_device;
 using eta_host::finite_bits;
 using eta_host::overlaps;
 
-constexpr const char* kVersion = "0.2.0 gfx950 exact-tiled-attention fwd+bwd";
+constexpr const char* kVersion = "0.3.0 gfx950 exact-tiled-attention fwd+bwd";
+constexpr int kSmallGrid = 128;  // 128-row workgroups below which attn_fwd splits the keys
 
 template <int D, bool BF16, bool CAUSAL, bool MODS, bool VARLEN = false, bool SPARSE = false>
 int launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
@@ -35,6 +37,22 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, i
   if (total64 > 0x7fffffff) return ATTN_ERR_BAD_SHAPE;
   const int total = (int)total64;
   const float c_log2 = scale * 1.44269504088896340736f;
+  // Grids that leave most compute units idle (fewer workgroups of 128 rows
+  // than half the 256 CUs) take the key-split kernel: 32 rows per workgroup,
+  // the keys shared out between its four waves.
+  if constexpr (!MODS && !VARLEN && !SPARSE && D <= 128) {
+    if (total < kSmallGrid && Nk > eta::SplitCfg<D>::BN) {
+      using S = eta::SplitCfg<D>;
+      const int nqb32 = (Nq + S::BM - 1) / S::BM;
+      const int prescale = !(scale > 0.f) ? 1 : 0;
+      hipLaunchKernelGGL((eta::attn_fwd_splitk_kernel<D, BF16, CAUSAL>),
+                         dim3((unsigned)((int64_t)B * Hq * nqb32)), dim3(S::kThreads), 0, stream,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq,
+                         Hkv, Nq, Nk, nqb32, c_log2, prescale);
+      return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    }
+  }
   // Softcap and ALiBi transform the raw scores themselves (no prescaling);
   // a window alone keeps the plain kernel's scaling.
   const bool transform = MODS && (mods.slopes || mods.cap > 0.f);

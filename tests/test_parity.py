@@ -82,6 +82,43 @@ def test_small_grid_against_oracle(case):
     assert_close(out, lse, O, L, str(case))
 
 
+# Grids of fewer than 128 workgroups of 128 rows go to the key-split kernel
+# (most of SMALL above); these shapes keep the edge cases on the 128-row
+# kernel: B * Hq * ceil(Nq / 128) >= 128, few rows and keys each.
+WIDE = [
+    (1, 128, 16, 65, 130, 128, "bf16", True),
+    (1, 128, 128, 127, 300, 128, "bf16", False),
+    (2, 64, 64, 100, 33, 64, "fp16", True),     # Nq > Nk: rows without keys
+    (1, 128, 8, 200, 200, 64, "bf16", True),
+    (1, 128, 32, 129, 97, 128, "fp16", False),
+    (1, 64, 1, 300, 513, 128, "bf16", True),    # MQA, 3 row blocks per head
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "B%dH%d-%dN%dx%dd%d%s%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], "c" if c[7] else ""))
+def test_wide_grid_against_oracle(case):
+    B, Hq, Hkv, Nq, Nk, d, dt, causal = case
+    assert B * Hq * ((Nq + 127) // 128) >= 128  # the 128-row kernel
+    q, k, v = make_qkv(B, Nq, Nk, Hq, Hkv, d, dt, 1.0, 250 + WIDE.index(case))
+    scale = 1.0 / math.sqrt(d)
+    out, lse = gpu_attn(q, k, v, scale, causal)
+    O, L = oracle.attention(q, k, v, scale, causal)
+    assert_close(out, lse, O, L, str(case))
+
+
+@pytest.mark.parametrize("Nk", [33, 64, 65, 200, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_split_small_grid_edges(Nk, causal):
+    # the key-split kernel: quarter ranges of 1..8 tiles per wave, waves
+    # without keys, ragged last tiles, causal blocks whose rows see few keys
+    Nq = 70
+    q, k, v = make_qkv(1, Nq, Nk, 4, 2, 128, "bf16", 1.0, 260 + Nk)
+    out, lse = gpu_attn(q, k, v, 1.0 / math.sqrt(128), causal)
+    O, L = oracle.attention(q, k, v, 1.0 / math.sqrt(128), causal)
+    assert_close(out, lse, O, L, f"Nk {Nk}")
+
+
 def lowp_baseline(q, k, v, scale, causal):
     """Plain low-precision attention (CPU, fp32): scores and softmax in fp32
     from the rounded inputs, P rounded to the element type, fp32 PV, output
