@@ -43,7 +43,8 @@
 //    early causal rows -- where one P entry carries most of the weight -- at
 //    the accuracy of the output rounding.
 //  * The row sum l is accumulated from the unrounded fp32 p.
-//  * Epilogue: O /= l, rounded to nearest-even; lse = (m + log2 l) * ln 2.
+//  * Epilogue: O /= l, rounded to nearest-even, staged through LDS so that
+//    each store writes 16 contiguous bytes per lane; lse = (m + log2 l) * ln 2.
 //  * Template switches: MODS adds the score variants (sliding window, ALiBi,
 //    softcap), VARLEN takes the rows of packed variable-length sequences
 //    from prefix sums, SPARSE visits only the key blocks a block mask flags;
@@ -601,20 +602,38 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
   for (; t < nt; ++t) tile(t, MaskedMode{});
 
-  // ---- Epilogue: normalise, round, store O and the logsumexp.  Stores of
-  // rows >= Nq fall outside the descriptors' ranges and are dropped.
+  // ---- Epilogue: normalise, round, store O and the logsumexp.  Each lane
+  // holds 4-element pieces of one row; the wave stages its 32 rounded rows in
+  // its own slice of the (now idle) LDS stages and reads them back 16
+  // contiguous bytes per lane, so that each store instruction writes whole
+  // row segments (4 rows x D elements) instead of 16 bytes of 32 rows.
+  // Stores of rows >= Nq fall outside the descriptors' ranges and are dropped.
   const float lt = lsum + __shfl_xor(lsum, 32);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  const rsrc_t orr = make_rsrc(O + qo_off, span_bytes(qw0, 32, Nq, q_rs, D));
-  const int ovoff = (int)(l32 * q_rs * 2) + 8 * hh;
+  {
+    constexpr int ORS = D + 8;  // staged row stride (elements)
+    static_assert(C::kWaves * 32 * ORS <= C::kLdsElems, "the staged rows fit the stages");
+    uint16_t* const ost = smem + wave * 32 * ORS;
+    // (every wave passed the last tile's barrier: no wave reads the stages)
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4_t o4;
+      for (int g = 0; g < 4; ++g) {
+        f32x4_t o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * g + e] * inv;
-      buf_store8(pack4<BF16>(o4), orr, ovoff + 2 * (32 * db + 8 * g));
+        for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * g + e] * inv;
+        *reinterpret_cast<u32x2_t*>(ost + l32 * ORS + 32 * db + 8 * g + 4 * hh) = pack4<BF16>(o4);
+      }
+    }
+    constexpr int CPR = D / 8;        // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;     // rows per store instruction
+    const rsrc_t orr = make_rsrc(O + qo_off, span_bytes(qw0, 32, Nq, q_rs, D));
+    const int rr = lane / CPR, cc = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = RPI * i + rr;
+      const u32x4_t v16 = *reinterpret_cast<const u32x4_t*>(ost + row * ORS + 8 * cc);
+      buf_store16(v16, orr, (int)(row * q_rs * 2) + 16 * cc);
     }
   }
   const int nrows = max(0, min(32, Nq - qw0));

@@ -88,6 +88,10 @@ __device__ __forceinline__ void buf_store8(u32x2_t v, rsrc_t r, int voff) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
 }
 
+__device__ __forceinline__ void buf_store16(u32x4_t v, rsrc_t r, int voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
+}
+
 __device__ __forceinline__ void buf_store4(float v, rsrc_t r, int voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, 0, 0);
 }

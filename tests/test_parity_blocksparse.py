@@ -88,8 +88,9 @@ def test_against_oracle(ci, causal):
 def test_all_ones_is_bitwise_attn_fwd(causal):
     # the same tiles in the same order through the same bodies (key count a
     # multiple of 64, so that no ragged tile takes the split-P path only the
-    # block-sparse instance uses when not causal)
-    B, Nq, Nk, Hq, Hkv, d = 2, 320, 448, 8, 2, 128
+    # block-sparse instance uses when not causal; 144 blocks of 128 rows, so
+    # that attn_fwd runs its 128-row kernel rather than the key-split one)
+    B, Nq, Nk, Hq, Hkv, d = 2, 320, 448, 24, 6, 128
     q, k, v = make_qkv(B, Nq, Nk, Hq, Hkv, d, "bf16", 1.0, 971)
     mask = torch.ones((B, 1, nblocks(Nq), nblocks(Nk)), dtype=torch.uint8)
     a, la = gpu_bs(q, k, v, mask, 0.09, causal)

@@ -80,9 +80,11 @@ def test_ragged_against_oracle(ci, causal):
 @pytest.mark.parametrize("causal", [False, True])
 def test_each_sequence_is_bitwise_the_batched_forward(causal):
     # The varlen kernel is the batched kernel with per-sequence row offsets:
-    # every sequence must equal attn_fwd run on that sequence alone, bit for bit.
+    # every sequence must equal attn_fwd run on that sequence alone, bit for
+    # bit.  (128 heads: even a one-row sequence has the 128 row blocks above
+    # which attn_fwd runs its 128-row kernel rather than the key-split one.)
     lens_q, lens_k = [129, 1, 1, 700], [64, 1000, 2, 700]
-    q, k, v, cu_q, cu_k = make_varlen(lens_q, lens_k, 6, 3, 128, "bf16", 1.0, 510)
+    q, k, v, cu_q, cu_k = make_varlen(lens_q, lens_k, 128, 32, 128, "bf16", 1.0, 510)
     scale = 1.0 / math.sqrt(128)
     out, lse = gpu_varlen(q, k, v, cu_q, cu_k, max(lens_q), scale, causal)
     for b in range(len(lens_q)):
@@ -94,7 +96,7 @@ def test_each_sequence_is_bitwise_the_batched_forward(causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_equal_lengths_are_bitwise_the_padded_batch(causal):
-    B, N, Hq, Hkv, d = 3, 300, 4, 2, 64
+    B, N, Hq, Hkv, d = 3, 300, 16, 2, 64  # 144 row blocks: attn_fwd's 128-row kernel
     q, k, v = make_qkv(B, N, N, Hq, Hkv, d, "fp16", 1.0, 511)
     cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32)
     out, lse = gpu_varlen(q.reshape(B * N, Hq, d), k.reshape(B * N, Hkv, d),

@@ -77,17 +77,22 @@ def test_varlen_backward_against_oracle(ci, causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_each_sequence_is_bitwise_attn_bwd(causal):
-    from exact_tiled_attention_35_amd import attn_bwd, attn_fwd
+    from exact_tiled_attention_35_amd import attn_bwd
 
     lens_q, lens_k, Hq, Hkv, d = [300, 129, 64], [200, 129, 500], 4, 2, 128
     q, k, v, cu_q, cu_k = make_varlen(lens_q, lens_k, Hq, Hkv, d, "bf16", 1.0, 1390)
     do = make_varlen(lens_q, lens_k, Hq, Hkv, d, "bf16", 1.0, 1391)[0]
-    dq, dk, dv, delta, _, _ = gpu_fwd_bwd(q, k, v, do, cu_q, cu_k, max(lens_q), max(lens_k), 0.1, causal)
+    dq, dk, dv, delta, outv, lsev = gpu_fwd_bwd(q, k, v, do, cu_q, cu_k, max(lens_q), max(lens_k),
+                                                0.1, causal)
     for b in range(len(lens_q)):
         qs, qe, ks, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
         qc, dc = q[None, qs:qe].cuda(), do[None, qs:qe].cuda()
         kc, vc = k[None, ks:ke].cuda(), v[None, ks:ke].cuda()
-        out, lse = attn_fwd(qc, kc, vc, 0.1, causal)
+        # the backward of each sequence alone, from the same forward output
+        # (a sequence's own attn_fwd may take the key-split kernel for its
+        # small grid, whose output differs in rounding order)
+        out = outv[None, qs:qe].contiguous().cuda()
+        lse = lsev[None, :, qs:qe].contiguous().cuda()
         g = [x.cpu() for x in attn_bwd(qc, kc, vc, out, dc, lse, 0.1, causal)]
         torch.cuda.synchronize()
         assert torch.equal(dq[qs:qe], g[0][0]) and torch.equal(dk[ks:ke], g[1][0])
