@@ -205,110 +205,98 @@ def launch_stats(kernel_ms) -> dict:
     return {"median_us": round(med, 2), "min_us": round(us[0], 2), "max_us": round(us[-1], 2)}
 
 
-class ClockSampler:
-    """Samples the GPU's graphics clock and socket power through amdsmi's GPU
-    metrics on a background thread while the timed steps run.  The metrics
-    are the firmware's running averages; the samples say what clock the
-    kernels met.  Everything here is best effort: without amdsmi, or where a
-    field is missing, the summary says so and timing is unaffected."""
+def sustained_clock(step, stream, seconds: float, achieved: float, peak: float,
+                    nominal_mhz: float = 2400.0):
+    """The GPU's graphics clock and socket power under this step's load, read
+    from amdsmi's GPU metrics while the step runs back to back for `seconds`
+    after the timed region (outside it).  The firmware refreshes that table
+    about once per second, so only refreshes at least 0.5 s into the load
+    count; a timed region of milliseconds cannot be sampled this way.  The
+    clock also rescales the peak: frac_of_peak_at_this_clock is the timed
+    steps' achieved rate against the peak at this clock.  Best effort: without
+    amdsmi, or without a refresh, the summary says so."""
+    import threading
 
-    FIELDS = ("current_gfxclk", "average_gfxclk_frequency", "current_socket_power",
-              "average_socket_power", "temperature_hotspot")
+    import torch
 
-    def __init__(self, interval_s: float = 0.001):
-        self.interval_s = interval_s
-        self.samples = []
-        self.error = None
-        self._stop = None
-        self._thread = None
-        self._handle = None
-        self._amdsmi = None
-
-    def __enter__(self):
-        import threading
-
-        try:
-            import amdsmi
-
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            if not handles:
-                raise RuntimeError("no GPU handle")
-            self._amdsmi, self._handle = amdsmi, handles[0]
-            self._read()  # one sample before the steps
-        except Exception as e:  # pragma: no cover - depends on the box
-            self.error = f"{type(e).__name__}: {e}"
-            return self
-        self._stop = threading.Event()
-
-        def run():
-            while not self._stop.is_set():
-                self._read()
-                self._stop.wait(self.interval_s)
-
-        self._thread = threading.Thread(target=run, daemon=True)
-        self._thread.start()
-        return self
-
-    def _read(self):
-        try:
-            m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
-        except Exception as e:  # pragma: no cover - depends on the box
-            self.error = f"{type(e).__name__}: {e}"
-            return
-        rec = {"t": time.perf_counter()}
-        for k in self.FIELDS:
-            v = m.get(k)
-            if isinstance(v, (int, float)) and v not in (0xFFFF, 0xFFFFFFFF):
-                rec[k] = float(v)
-        clks = m.get("current_gfxclks")
-        if isinstance(clks, (list, tuple)):
-            vals = [float(c) for c in clks if isinstance(c, (int, float)) and 0 < c < 0xFFFF]
-            if vals:
-                rec["xcd_gfxclk_mean"] = sum(vals) / len(vals)
-        self.samples.append(rec)
-
-    def __exit__(self, *exc):
-        if self._thread is not None:
-            self._stop.set()
-            self._thread.join(timeout=2.0)
-        if self._amdsmi is not None:
-            try:
-                self._amdsmi.amdsmi_shut_down()
-            except Exception:  # pragma: no cover
-                pass
-        return False
-
-    def summary(self, t0: float, t1: float, achieved: float, peak: float, nominal_mhz: float = 2400.0):
-        """Clock during [t0, t1] (host perf_counter times of the timed region)
-        and the fraction of the peak scaled to that clock."""
-        inside = [r for r in self.samples if t0 <= r["t"] <= t1]
-        out = {"source": "amdsmi GPU metrics, sampled on a host thread during the timed steps",
-               "samples_in_timed_region": len(inside), "nominal_mhz": nominal_mhz}
-        if self.error:
-            out["error"] = self.error
-        use = inside or self.samples[-1:]
-        if not inside and use:
-            out["note"] = "no sample fell inside the timed region; the last one is reported"
-        for key in ("xcd_gfxclk_mean", "current_gfxclk", "average_gfxclk_frequency"):
-            vals = [r[key] for r in use if key in r]
-            if vals:
-                out["gfxclk_mhz"] = round(sum(vals) / len(vals), 1)
-                out["gfxclk_mhz_min"] = round(min(vals), 1)
-                out["gfxclk_mhz_max"] = round(max(vals), 1)
-                out["gfxclk_field"] = key
-                out["frac_of_peak_at_this_clock"] = round(
-                    achieved / (peak * out["gfxclk_mhz"] / nominal_mhz), 4)
-                break
-        for key in ("current_socket_power", "average_socket_power"):
-            vals = [r[key] for r in use if key in r]
-            if vals:
-                out["socket_power_w"] = round(sum(vals) / len(vals), 1)
-                break
-        vals = [r["temperature_hotspot"] for r in use if "temperature_hotspot" in r]
-        if vals:
-            out["hotspot_c"] = round(max(vals), 1)
+    out = {"source": "amdsmi GPU metrics, refreshed by the firmware about once per second, "
+                     "sampled while the step ran back to back after the timed region",
+           "seconds": seconds, "nominal_mhz": nominal_mhz}
+    if seconds <= 0:
+        out["error"] = "disabled"
         return out
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # pragma: no cover - depends on the box
+        out["error"] = f"{type(e).__name__}: {e}"
+        return out
+    samples, stop = [], threading.Event()
+
+    def read():
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+        except Exception:  # pragma: no cover
+            return
+        clks = [float(c) for c in (m.get("current_gfxclks") or [])
+                if isinstance(c, (int, float)) and 0 < c < 0xFFFF]
+        samples.append({"t": time.perf_counter(), "acc": m.get("accumulation_counter"),
+                         "clk": sum(clks) / len(clks) if clks else None,
+                         "clk_min": min(clks) if clks else None,
+                         "power": m.get("current_socket_power")})
+
+    def loop():
+        while not stop.is_set():
+            read()
+            stop.wait(0.02)
+
+    read()
+    th = threading.Thread(target=loop, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        n += 10
+    stop.set()
+    th.join(timeout=2.0)
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:  # pragma: no cover
+        pass
+    out["steps_run"] = n
+    out.update(clock_summary(samples, t0, achieved, peak, nominal_mhz))
+    return out
+
+
+def clock_summary(samples, t0: float, achieved: float, peak: float, nominal_mhz: float = 2400.0):
+    """Keep one sample per refresh of the GPU metrics table (its
+    accumulation counter changes at each refresh) taken at least 0.5 s after
+    the load started at t0, the first sample (before the load) excluded, and
+    average the mean-over-XCDs clock and the socket power over them."""
+    first_acc = samples[0]["acc"] if samples else None
+    fresh, seen = [], set()
+    for r in samples:
+        if r["t"] >= t0 + 0.5 and r["acc"] != first_acc and r["acc"] not in seen and r["clk"]:
+            seen.add(r["acc"])
+            fresh.append(r)
+    out = {"refreshes_under_load": len(fresh)}
+    if not fresh:
+        out["error"] = "no refresh of the GPU metrics under the load"
+        return out
+    clk = sum(r["clk"] for r in fresh) / len(fresh)
+    out["gfxclk_mhz_mean_over_xcds"] = round(clk, 1)
+    out["gfxclk_mhz_slowest_xcd"] = round(min(r["clk_min"] for r in fresh), 1)
+    pw = [r["power"] for r in fresh if isinstance(r["power"], (int, float))]
+    if pw:
+        out["socket_power_w"] = round(sum(pw) / len(pw), 1)
+    out["frac_of_peak_at_this_clock"] = round(achieved / (peak * clk / nominal_mhz), 4)
+    return out
+
 
 def cpu_baseline(w, q, k, v, budget_s: float, out=None, lse=None):
     """Time the fp64 oracle head by head (all rows of each) on this host until
@@ -534,6 +522,9 @@ def main():
                          "and the Infinity Cache; outside the timed region) and report them "
                          "as \"cold\"; the headline figures stay the warm ones")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--clock-seconds", type=float, default=2.5,
+                    help="after the timed steps, run the step back to back this long and read "
+                         "the GPU clock and power from amdsmi's GPU metrics (0: skip)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain elementwise copy kernel that "
                          "reads and writes MIB MiB (the reference for scaling HBM byte counters "
@@ -643,14 +634,13 @@ def main():
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()  # one rank: the barrier is this synchronisation
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        for i in range(K):
-            starts[i].record(stream)
-            step()
-            ends[i].record(stream)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     wall = t1 - t0
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_kernel_s = sum(kernel_ms) / K / 1e3
@@ -698,7 +688,7 @@ def main():
             "kernel_max_us": per_launch["max_us"],
             "achieved_at_median": round(F / (per_launch["median_us"] * 1e-6) / 1e12, 3),
         },
-        "clock": clock.summary(t0, t1, achieved, peak),
+        "clock": sustained_clock(step, stream, args.clock_seconds, achieved, peak),
         "host": host_info(args.op),
         "cpu_baseline": None,
         "context": "FlexAttention with the FA4 backend reports 1.2x-3.2x speedups on NVIDIA "
@@ -801,14 +791,13 @@ def bench_decode(args, w, dev):
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        for i in range(K):
-            starts[i].record(stream)
-            step()
-            ends[i].record(stream)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     wall = t1 - t0
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_s = sum(kernel_ms) / K / 1e3
@@ -851,7 +840,7 @@ def bench_decode(args, w, dev):
             "kernel_min_us": per_launch["min_us"],
             "unit_of_work": "one attn_decode call: append, split attention and merge kernels",
         },
-        "clock": clock.summary(t0, t1, achieved, peak),
+        "clock": sustained_clock(step, stream, args.clock_seconds, achieved, peak),
         "host": host_info("decode"),
         "cpu_baseline": None,
         "context": "KV-cache decode; the headline metric is the forward (--op fwd)",
@@ -942,14 +931,13 @@ def bench_varlen(args, wl, backward=False):
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        for i in range(K):
-            starts[i].record(stream)
-            step()
-            ends[i].record(stream)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     wall = t1 - t0
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_s = sum(kernel_ms) / K / 1e3
@@ -996,7 +984,7 @@ def bench_varlen(args, wl, backward=False):
             "kernel_median_us": per_launch["median_us"],
             "kernel_min_us": per_launch["min_us"],
         },
-        "clock": clock.summary(t0, t1, achieved, peak),
+        "clock": sustained_clock(step, stream, args.clock_seconds, achieved, peak),
         "host": host_info("bwd" if backward else "fwd"),
         "cpu_baseline": None,
         "context": ("packed variable-length backward" if backward else
@@ -1098,14 +1086,13 @@ def bench_blocksparse(args, name, backward=False):
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        for i in range(K):
-            starts[i].record(stream)
-            step()
-            ends[i].record(stream)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     wall = t1 - t0
     kernel_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
     avg_s = sum(kernel_ms) / K / 1e3
@@ -1154,7 +1141,7 @@ def bench_blocksparse(args, name, backward=False):
             "kernel_median_us": per_launch["median_us"],
             "kernel_min_us": per_launch["min_us"],
         },
-        "clock": clock.summary(t0, t1, achieved, peak),
+        "clock": sustained_clock(step, stream, args.clock_seconds, achieved, peak),
         "host": host_info("bwd" if backward else "fwd"),
         "cpu_baseline": None,
         "context": ("block-sparse backward (the dQ and dK/dV kernels)" if backward else

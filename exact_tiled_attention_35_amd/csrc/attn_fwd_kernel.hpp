@@ -611,9 +611,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const float lt = lsum + __shfl_xor(lsum, 32);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   {
-    constexpr int ORS = D + 8;  // staged row stride (elements)
+    // Staged row stride D + 8 elements (16-byte aligned rows).  Rows 16-31
+    // swap the two 8-byte halves of each 16-byte chunk (the reads swap them
+    // back), which spreads a write's 32 rows over all 64 banks if a pass
+    // serves 32 lanes; the counters still show 96 bank-conflict cycles per
+    // wave in this staging (none in the tile loop), about 1 % of the LDS's
+    // busy cycles, once per workgroup.
+    constexpr int ORS = D + 8;
     static_assert(C::kWaves * 32 * ORS <= C::kLdsElems, "the staged rows fit the stages");
     uint16_t* const ost = smem + wave * 32 * ORS;
+    const int half = 4 * (hh ^ (l32 >> 4));
     // (every wave passed the last tile's barrier: no wave reads the stages)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -622,7 +629,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         f32x4_t o4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * g + e] * inv;
-        *reinterpret_cast<u32x2_t*>(ost + l32 * ORS + 32 * db + 8 * g + 4 * hh) = pack4<BF16>(o4);
+        *reinterpret_cast<u32x2_t*>(ost + l32 * ORS + 32 * db + 8 * g + half) = pack4<BF16>(o4);
       }
     }
     constexpr int CPR = D / 8;        // 16-byte chunks per row
@@ -632,7 +639,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
       const int row = RPI * i + rr;
-      const u32x4_t v16 = *reinterpret_cast<const u32x4_t*>(ost + row * ORS + 8 * cc);
+      u32x4_t v16 = *reinterpret_cast<const u32x4_t*>(ost + row * ORS + 8 * cc);
+      if (row >= 16) v16 = u32x4_t{v16[2], v16[3], v16[0], v16[1]};
       buf_store16(v16, orr, (int)(row * q_rs * 2) + 16 * cc);
     }
   }

@@ -181,27 +181,24 @@ def test_launch_stats_median_min_max(capsys):
     assert "500.0 700.0 400.0 600.0" in capsys.readouterr().err
 
 
-def test_clock_summary_uses_samples_inside_the_timed_region():
-    c = bench.ClockSampler()
-    c.samples = [
-        {"t": 0.5, "current_gfxclk": 2400.0},  # before the timed region: ignored
-        {"t": 1.1, "current_gfxclk": 1600.0, "current_socket_power": 1300.0},
-        {"t": 1.4, "current_gfxclk": 1800.0, "current_socket_power": 1400.0},
-        {"t": 2.5, "current_gfxclk": 2400.0},  # after it: ignored
+def test_clock_summary_keeps_one_sample_per_refresh_under_load():
+    # the table refreshes about once per second: repeated reads of one refresh
+    # count once, the pre-load refresh and the first 0.5 s are left out
+    S = [
+        {"t": 0.9, "acc": 100, "clk": 150.0, "clk_min": 140.0, "power": 250},    # before the load
+        {"t": 1.2, "acc": 100, "clk": 150.0, "clk_min": 140.0, "power": 250},    # stale
+        {"t": 1.3, "acc": 101, "clk": 1900.0, "clk_min": 1800.0, "power": 900},  # < 0.5 s in
+        {"t": 1.7, "acc": 102, "clk": 1700.0, "clk_min": 1600.0, "power": 1300},
+        {"t": 1.8, "acc": 102, "clk": 1700.0, "clk_min": 1600.0, "power": 1300},  # same refresh
+        {"t": 2.7, "acc": 103, "clk": 1660.0, "clk_min": 1550.0, "power": 1350},
     ]
-    s = c.summary(1.0, 2.0, achieved=1000.0, peak=2500.0)
-    assert s["samples_in_timed_region"] == 2
-    assert s["gfxclk_mhz"] == 1700.0 and s["gfxclk_mhz_min"] == 1600.0
-    assert s["socket_power_w"] == 1350.0
-    # 1000 TFLOP/s against 2500 * 1700 / 2400
-    assert s["frac_of_peak_at_this_clock"] == round(1000.0 / (2500.0 * 1700.0 / 2400.0), 4)
-    # per-XCD clocks win over the single clock field when present
-    c.samples = [{"t": 1.5, "current_gfxclk": 2000.0, "xcd_gfxclk_mean": 1650.0}]
-    assert c.summary(1.0, 2.0, 1000.0, 2500.0)["gfxclk_mhz"] == 1650.0
-    # nothing inside: the last sample, flagged
-    c.samples = [{"t": 0.2, "current_gfxclk": 2100.0}]
-    s = c.summary(1.0, 2.0, 1000.0, 2500.0)
-    assert s["gfxclk_mhz"] == 2100.0 and "note" in s
+    c = bench.clock_summary(S, t0=1.0, achieved=1000.0, peak=2500.0)
+    assert c["refreshes_under_load"] == 2
+    assert c["gfxclk_mhz_mean_over_xcds"] == 1680.0 and c["gfxclk_mhz_slowest_xcd"] == 1550.0
+    assert c["socket_power_w"] == 1325.0
+    assert c["frac_of_peak_at_this_clock"] == round(1000.0 / (2500.0 * 1680.0 / 2400.0), 4)
+    # a timed region too short for any refresh: reported, not invented
+    assert "error" in bench.clock_summary(S[:3], t0=1.0, achieved=1000.0, peak=2500.0)
 
 
 def test_host_info_names_cores_and_versions():
