@@ -42,8 +42,8 @@ METRIC_BWD = ("attention bwd TFLOP/s (10*B*Hq*Nq*Nk*d per call, halved for causa
 # figures, and the kernels one call launches.
 _CSRC = os.path.join(ROOT, "exact_tiled_attention_35_amd", "csrc")
 OP_SOURCES = {
-    "fwd": ("gfx950_ops.hpp", "attn_fwd_kernel.hpp", "attn_fwd_splitk_kernel.hpp", "attn_api.hip",
-            "attn_host.hpp"),
+    "fwd": ("gfx950_ops.hpp", "attn_fwd_kernel.hpp", "attn_fwd_splitk_kernel.hpp",
+            "attn_fwd_pipe_kernel.hpp", "attn_api.hip", "attn_host.hpp"),
     "bwd": ("gfx950_ops.hpp", "attn_bwd_kernel.hpp", "attn_bwd_api.hip", "attn_host.hpp"),
     "decode": ("gfx950_ops.hpp", "attn_decode_kernel.hpp", "attn_decode_api.hip", "attn_host.hpp"),
 }
@@ -51,7 +51,9 @@ KERNEL_SOURCES = [os.path.join(_CSRC, n) for n in OP_SOURCES["fwd"]]
 TRAFFIC_FILES = {op: os.path.join(ROOT, "profiles", f"attn_{op}_traffic.json") for op in OP_SOURCES}
 TRAFFIC_FILE = TRAFFIC_FILES["fwd"]
 OP_KERNELS = {
-    "fwd": ("attn_fwd_kernel",),  # the headline launches; small grids use attn_fwd_splitk_kernel
+    # one of these per forward call: the tile kernel, or at d = 256 the
+    # pipelined one (small grids use attn_fwd_splitk_kernel)
+    "fwd": ("attn_fwd_kernel", "attn_fwd_pipe_kernel"),
     "bwd": ("attn_bwd_dq_kernel", "attn_bwd_dkdv_kernel"),
     "decode": ("kv_append_kernel", "attn_decode_kernel", "attn_decode_merge_kernel"),
 }
@@ -473,9 +475,12 @@ def write_traffic_summary(fetch_csv: str, write_csv: str, copy_mib, workload=Non
         per_kernel = []
         for kern in OP_KERNELS[op]:
             vals = [v for (k, v) in rows if kern + "<" in k]
-            if not vals:
+            if not vals and op != "fwd":
                 raise SystemExit(f"{csv_path}: no {kern} dispatches for {counter}")
-            per_kernel.append(sum(vals) / len(vals))
+            if vals:
+                per_kernel.append(sum(vals) / len(vals))
+        if not per_kernel:
+            raise SystemExit(f"{csv_path}: no forward kernel dispatches for {counter}")
         if not copy:
             raise SystemExit(f"{csv_path}: no copy dispatch for {counter}")
         factor = copy_bytes / (max(copy) * 1024.0)

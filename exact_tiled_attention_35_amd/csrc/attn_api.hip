@@ -13,6 +13,7 @@
 #include <cstdint>
 
 #include "attn_fwd_kernel.hpp"
+#include "attn_fwd_pipe_kernel.hpp"
 #include "attn_fwd_splitk_kernel.hpp"
 #include "attn_host.hpp"
 
@@ -50,6 +51,18 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, i
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                          static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq,
                          Hkv, Nq, Nk, nqb32, c_log2, prescale);
+      return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    }
+  }
+  // d = 256, plain: the kernel that overlaps each wave's softmax with the
+  // next tile's S^T product.
+  if constexpr (!MODS && !VARLEN && !SPARSE && D == 256) {
+    if (scale > 0.f) {
+      hipLaunchKernelGGL((eta::attn_fwd_pipe_kernel<D, BF16, CAUSAL>), dim3(total),
+                         dim3(eta::PipeCfg<D>::kThreads), 0, stream,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq,
+                         Hkv, Nq, Nk, nqb, total, c_log2);
       return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
     }
   }

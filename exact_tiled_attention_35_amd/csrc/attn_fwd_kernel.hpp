@@ -66,6 +66,49 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units: p <= 256 between resca
 // exceeds this (every p then stays far inside the fp16 range of P).
 constexpr float kSumLimit = 32768.0f;
 
+// Epilogue of a wave's 32 query rows: O^T accumulators (lane l holds
+// 4-element pieces of row l % 32) are scaled by inv, rounded to the element
+// type and stored.  The wave stages its rounded rows in its own slice of LDS
+// (row stride D + 8 elements, 16-byte aligned rows) and reads them back 16
+// contiguous bytes per lane, so that each store instruction writes whole row
+// segments (64 / (D / 8) rows x D elements) instead of 16 bytes of 32 rows.
+// Rows 16-31 swap the two 8-byte halves of each 16-byte chunk (the reads
+// swap them back), which spreads a write's 32 rows over all 64 banks if a
+// pass serves 32 lanes; the counters still show 96 bank-conflict cycles per
+// wave in this staging at d = 128 (none in the tile loops), about 1 % of the
+// LDS's busy cycles, once per workgroup.  The caller guarantees that no wave
+// still reads the LDS area (4 x 32 x (D + 8) elements from smem).  Stores of
+// rows past the descriptor's range (rows >= Nq) are dropped.
+template <int D, bool BF16>
+__device__ __forceinline__ void store_rows(uint16_t* smem, int wave, int lane,
+                                           const f32x16_t (&oacc)[D / 32], float inv, rsrc_t orr,
+                                           int64_t q_rs) {
+  constexpr int ORS = D + 8;
+  const int l32 = lane & 31, hh = lane >> 5;
+  uint16_t* const ost = smem + wave * 32 * ORS;
+  const int half = 4 * (hh ^ (l32 >> 4));
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4_t o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * g + e] * inv;
+      *reinterpret_cast<u32x2_t*>(ost + l32 * ORS + 32 * db + 8 * g + half) = pack4<BF16>(o4);
+    }
+  }
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+  const int rr = lane / CPR, cc = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = RPI * i + rr;
+    u32x4_t v16 = *reinterpret_cast<const u32x4_t*>(ost + row * ORS + 8 * cc);
+    if (row >= 16) v16 = u32x4_t{v16[2], v16[3], v16[0], v16[1]};
+    buf_store16(v16, orr, (int)(row * q_rs * 2) + 16 * cc);
+  }
+}
+
 // Tile shape per head dimension.
 //
 // LDS holds two stages; each stage has a K region and a V region, both
@@ -602,48 +645,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
   for (; t < nt; ++t) tile(t, MaskedMode{});
 
-  // ---- Epilogue: normalise, round, store O and the logsumexp.  Each lane
-  // holds 4-element pieces of one row; the wave stages its 32 rounded rows in
-  // its own slice of the (now idle) LDS stages and reads them back 16
-  // contiguous bytes per lane, so that each store instruction writes whole
-  // row segments (4 rows x D elements) instead of 16 bytes of 32 rows.
-  // Stores of rows >= Nq fall outside the descriptors' ranges and are dropped.
+  // ---- Epilogue: normalise, round, store O and the logsumexp (every wave
+  // passed the last tile's barrier: no wave reads the stages any more).
+  static_assert(C::kWaves * 32 * (D + 8) <= C::kLdsElems, "the staged rows fit the stages");
   const float lt = lsum + __shfl_xor(lsum, 32);
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  {
-    // Staged row stride D + 8 elements (16-byte aligned rows).  Rows 16-31
-    // swap the two 8-byte halves of each 16-byte chunk (the reads swap them
-    // back), which spreads a write's 32 rows over all 64 banks if a pass
-    // serves 32 lanes; the counters still show 96 bank-conflict cycles per
-    // wave in this staging (none in the tile loop), about 1 % of the LDS's
-    // busy cycles, once per workgroup.
-    constexpr int ORS = D + 8;
-    static_assert(C::kWaves * 32 * ORS <= C::kLdsElems, "the staged rows fit the stages");
-    uint16_t* const ost = smem + wave * 32 * ORS;
-    const int half = 4 * (hh ^ (l32 >> 4));
-    // (every wave passed the last tile's barrier: no wave reads the stages)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4_t o4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * g + e] * inv;
-        *reinterpret_cast<u32x2_t*>(ost + l32 * ORS + 32 * db + 8 * g + half) = pack4<BF16>(o4);
-      }
-    }
-    constexpr int CPR = D / 8;        // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;     // rows per store instruction
-    const rsrc_t orr = make_rsrc(O + qo_off, span_bytes(qw0, 32, Nq, q_rs, D));
-    const int rr = lane / CPR, cc = lane % CPR;
-#pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int row = RPI * i + rr;
-      u32x4_t v16 = *reinterpret_cast<const u32x4_t*>(ost + row * ORS + 8 * cc);
-      if (row >= 16) v16 = u32x4_t{v16[2], v16[3], v16[0], v16[1]};
-      buf_store16(v16, orr, (int)(row * q_rs * 2) + 16 * cc);
-    }
-  }
+  store_rows<D, BF16>(smem, wave, lane, oacc, lt > 0.f ? 1.0f / lt : 0.f,
+                      make_rsrc(O + qo_off, span_bytes(qw0, 32, Nq, q_rs, D)), q_rs);
   const int nrows = max(0, min(32, Nq - qw0));
   const rsrc_t lr = make_rsrc(LSE + lse_off + qw0, nrows * 4);
   buf_store4(lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY, lr, 4 * l32);

@@ -145,8 +145,15 @@ def test_traffic_summary_needs_the_kernel_and_the_copy(tmp_path, monkeypatch):
     with pytest.raises(SystemExit, match="no copy dispatch"):
         bench.write_traffic_summary(str(fetch), str(write), 1, workload=HEADLINE, op="fwd")
     _write_counter_csv(fetch, "FETCH_SIZE", [("neg_kernel", 512.0)])  # no kernel dispatch
-    with pytest.raises(SystemExit, match="no attn_fwd_kernel dispatches"):
+    with pytest.raises(SystemExit, match="no forward kernel dispatches"):
         bench.write_traffic_summary(str(fetch), str(write), 1, workload=HEADLINE, op="fwd")
+    # the d = 256 workloads run the pipelined kernel
+    pipe = "void eta::attn_fwd_pipe_kernel<256, false, true>(...)"
+    _write_counter_csv(fetch, "FETCH_SIZE", [(pipe, 200.0), ("neg_kernel", 512.0)])
+    _write_counter_csv(write, "WRITE_SIZE", [(pipe, 30.0), ("neg_kernel", 1024.0)])
+    bench.write_traffic_summary(str(fetch), str(write), 1, workload=HEADLINE, op="fwd")
+    rec = json.load(open(tmp_path / "t.json"))["workloads"][HEADLINE]
+    assert rec["FETCH_SIZE_KiB_per_launch"] == 200.0
 
 
 def test_kernel_source_hash_ignores_comments_only(tmp_path, monkeypatch):

@@ -119,6 +119,25 @@ def test_key_split_small_grid_edges(Nk, causal):
     assert_close(out, lse, O, L, f"Nk {Nk}")
 
 
+# d = 256 goes to the kernel that computes S^T of tile t+1 during the
+# softmax of tile t: key counts around the 32-key tile (one tile, a tile and
+# one key, tiles that end before a wave's diagonal), Nq != Nk both ways,
+# query blocks whose waves compute different numbers of tiles.
+D256_EDGES = [(128, 1), (128, 31), (128, 32), (128, 33), (128, 64), (200, 96),
+              (300, 97), (129, 160), (64, 1000), (1000, 64), (256, 288)]
+
+
+@pytest.mark.parametrize("nq_nk", D256_EDGES, ids=lambda c: "N%dx%d" % c)
+@pytest.mark.parametrize("causal", [False, True])
+def test_d256_tile_edges(nq_nk, causal):
+    Nq, Nk = nq_nk
+    dt = "fp16" if causal else "bf16"
+    q, k, v = make_qkv(1, Nq, Nk, 2, 1, 256, dt, 1.0, 300 + D256_EDGES.index(nq_nk))
+    out, lse = gpu_attn(q, k, v, 1.0 / 16.0, causal)
+    O, L = oracle.attention(q, k, v, 1.0 / 16.0, causal)
+    assert_close(out, lse, O, L, f"d256 Nq {Nq} Nk {Nk}")
+
+
 def lowp_baseline(q, k, v, scale, causal):
     """Plain low-precision attention (CPU, fp32): scores and softmax in fp32
     from the rounded inputs, P rounded to the element type, fp32 PV, output
