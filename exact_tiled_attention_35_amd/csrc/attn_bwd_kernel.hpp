@@ -383,19 +383,28 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
           }
         }
       } else {
+        // Tiles cut by the end or the diagonal test every element; the
+        // others take a body without the test (as one body, the compiler
+        // turns the test into selects that every tile pays for).
+        auto p_ds = [&](auto masked) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+          for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = exp2_fast(__builtin_fmaf(s[kb][r], c_log2, -lse2));
-          if (need_mask) {
-            const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool vis = j < Nk && (!CAUSAL || j <= my_q + diag);
-            p = vis ? p : 0.f;
+            for (int r = 0; r < 16; ++r) {
+              float p = exp2_fast(__builtin_fmaf(s[kb][r], c_log2, -lse2));
+              if constexpr (decltype(masked)::value) {
+                const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const bool vis = j < Nk && (!CAUSAL || j <= my_q + diag);
+                p = vis ? p : 0.f;
+              }
+              s[kb][r] = p * (dp[kb][r] - Di);
+            }
           }
-          s[kb][r] = p * (dp[kb][r] - Di);
-        }
-      }
+        };
+        if (need_mask)
+          p_ds(std::true_type{});
+        else
+          p_ds(std::false_type{});
       }
       // dQ^T += K^T dS^T (same operand mapping as the forward's PV product).
       __builtin_amdgcn_s_setprio(1);
@@ -684,8 +693,13 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       __builtin_amdgcn_s_setprio(0);
       // P = 2^(s c - lse2) and dS = P (dP - D) for the rows this lane's
       // registers hold: row 32 qb + 8 (r / 4) + 4 hh + r % 4.  Rows past Nq
-      // read lse = D = 0 with zero Q and dO rows: they add nothing.
-      const bool need_mask = (i0 + BQ > Nq) || (CAUSAL && i0 + diag < kw0 + 31);
+      // read zero Q and dO rows and lse = D = 0: their P is 1 and their dS
+      // 0, and they add nothing to dV^T (dO rows zero) or dK^T (Q rows
+      // zero); keys past Nk are never stored.  So only causal tiles that
+      // cross the diagonal need masking (the score variants test their
+      // window and ragged ends below).
+      const bool need_mask = MODS ? (i0 + BQ > Nq) || (CAUSAL && i0 + diag < kw0 + 31)
+                                  : (CAUSAL && i0 + diag < kw0 + 31);
       // Causal and block-sparse instances mask in a pass of their own after
       // P and dS, the others per element: at d = 128 each form spills fewer
       // registers in the instances that use it.
@@ -781,7 +795,50 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         }
       }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS (the forward's PV operand mapping).
+      // dV^T += dO^T P and dK^T += Q^T dS (the forward's PV operand
+      // mapping).  At d <= 128 (two waves per SIMD, 256 registers each) P
+      // and dS are packed first and the transposed operands read one step
+      // ahead, each step fenced, so that at most four of them occupy
+      // registers; at d = 256 the compiler schedules the loop.
+      if constexpr (D <= 128) {
+      u32x4_t pbs[NKK], sbs[NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        f32x8_t pv, sv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = sc[kk >> 1][8 * (kk & 1) + e];
+          sv[e] = dp[kk >> 1][8 * (kk & 1) + e];
+        }
+        pbs[kk] = pack8<BF16>(pv);
+        sbs[kk] = pack8<BF16>(sv);
+      }
+      // operand reads one step (two MFMAs) ahead, each step fenced: at most
+      // four transposed operands in registers
+      constexpr int NM = NKK * NDB;
+      auto rd_pair = [&](int i, const uint16_t* base) {
+        const int kk = i / NDB, db = i % NDB;
+        const int o0 = t_rd + 16 * kk * TS + 32 * db, o1 = t_rd + (16 * kk + 8) * TS + 32 * db;
+        const u32x2_t a0 = lds_read_tr4(base + o0), a1 = lds_read_tr4(base + o1);
+        return u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+      };
+      u32x4_t va[2], qa[2];
+      va[0] = rd_pair(0, dtr);
+      qa[0] = rd_pair(0, qtr);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        if (i + 1 < NM) {
+          va[(i + 1) & 1] = rd_pair(i + 1, dtr);
+          qa[(i + 1) & 1] = rd_pair(i + 1, qtr);
+        }
+        const int kk = i / NDB, db = i % NDB;
+        dv[db] = mfma_32x32x16<BF16>(va[i & 1], pbs[kk], dv[db]);
+        dk[db] = mfma_32x32x16<BF16>(qa[i & 1], sbs[kk], dk[db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      } else {
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
@@ -802,6 +859,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         }
       }
       __builtin_amdgcn_s_setprio(0);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
