@@ -45,14 +45,18 @@ int launch_decode(const void* q, void* kc, void* vc, const int* seqlens, const v
                   int Nq, int Ncap, int Nnew, float scale, int splits, hipStream_t s) {
   auto* K = static_cast<uint16_t*>(kc);
   auto* V = static_cast<uint16_t*>(vc);
-  if (Nnew > 0) {
-    const int64_t n = (int64_t)B * Nnew * Hkv * (D / 8);
-    hipLaunchKernelGGL((eta::kv_append_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                       s, static_cast<const uint16_t*>(kn), static_cast<const uint16_t*>(vn), K, V,
-                       seqlens, B, Nnew, Hkv, Ncap);
-    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+  // With query rows the attention kernel appends the new rows itself; a
+  // call without query rows only appends.
+  if (Nq == 0) {
+    if (Nnew > 0) {
+      const int64_t n = (int64_t)B * Nnew * Hkv * (D / 8);
+      hipLaunchKernelGGL((eta::kv_append_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+                         0, s, static_cast<const uint16_t*>(kn), static_cast<const uint16_t*>(vn), K,
+                         V, seqlens, B, Nnew, Hkv, Ncap);
+      if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+    }
+    return ATTN_OK;
   }
-  if (Nq == 0) return ATTN_OK;
   const int nrb = row_blocks(Hq, Hkv, Nq);
   const int64_t grid = (int64_t)B * Hkv * nrb * splits;
   float* opart = splits > 1 ? static_cast<float*>(ws) : nullptr;
@@ -62,7 +66,8 @@ int launch_decode(const void* q, void* kc, void* vc, const int* seqlens, const v
   const float c_log2 = scale * 1.44269504088896340736f;
   hipLaunchKernelGGL((eta::attn_decode_kernel<D, BF16, CAUSAL>), dim3((unsigned)grid),
                      dim3(eta::DecCfg<D>::kThreads), 0, s, static_cast<const uint16_t*>(q), K, V,
-                     seqlens, static_cast<uint16_t*>(out), lse, opart, lpart, B, Hq, Hkv, Nq, Ncap,
+                     seqlens, static_cast<const uint16_t*>(kn), static_cast<const uint16_t*>(vn),
+                     static_cast<uint16_t*>(out), lse, opart, lpart, B, Hq, Hkv, Nq, Ncap,
                      Nnew, nrb, splits, c_log2, scale > 0.f ? 0 : 1);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
   if (splits > 1) {

@@ -9,9 +9,12 @@
 // after it; the query rows attend to all of those (causal: bottom-right
 // aligned, as everywhere in this library).
 //
-// Three kernels:
+// Kernels:
 //  * kv_append_kernel: copies k_new / v_new rows into the cache at row
-//    cache_seqlens[b] + t (16 bytes per thread).
+//    cache_seqlens[b] + t (16 bytes per thread); used only when there are no
+//    query rows (Nq = 0).  Otherwise attn_decode_kernel appends them itself:
+//    the tiles that hold new rows take them from k_new / v_new, and the
+//    workgroups of the first row block write them to the cache.
 //  * attn_decode_kernel: one workgroup per (b, KV head, block of 128 packed
 //    query rows, key split).  The query heads of a GQA group are packed into
 //    the rows of one MFMA tile (packed row r = (head g*G + r / Nq, query
@@ -83,8 +86,9 @@ kv_append_kernel(const uint16_t* __restrict__ Kn, const uint16_t* __restrict__ V
 
 template <int D, bool BF16, bool CAUSAL>
 __global__ void __launch_bounds__(DecCfg<D>::kThreads, DecCfg<D>::kMinWavesPerEU)
-attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                   const uint16_t* __restrict__ V, const int* __restrict__ seqlens,
+attn_decode_kernel(const uint16_t* __restrict__ Q, uint16_t* __restrict__ K,
+                   uint16_t* __restrict__ V, const int* __restrict__ seqlens,
+                   const uint16_t* __restrict__ Kn, const uint16_t* __restrict__ Vn,
                    uint16_t* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Opart,
                    float* __restrict__ Lpart, int B, int Hq, int Hkv, int Nq, int Ncap, int Nnew,
                    int nrb, int splits, float c_log2, int prescale) {
@@ -117,8 +121,10 @@ attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int i = row_ok ? r % Nq : 0;
   const bool wave_live = rw0 < rows;
 
-  // Keys of batch b and of this split (whole tiles).
-  const int nk = min(Ncap, max(0, seqlens[b] + Nnew));
+  // Keys of batch b and of this split (whole tiles).  Rows [sl_b, nk) are
+  // the new ones (row sl_b + t of the cache is new row t, clipped to Ncap).
+  const int sl_b = seqlens[b];
+  const int nk = min(Ncap, max(0, sl_b + Nnew));
   const int diag = nk - Nq;
   const int tiles = (nk + BN - 1) / BN;
   const int tps = (tiles + splits - 1) / splits;
@@ -128,8 +134,8 @@ attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int nt = kv_end > t0 * BN ? (kv_end - t0 * BN + BN - 1) / BN : 0;
 
   const int64_t q_rs = (int64_t)Hq * D, kv_rs = (int64_t)Hkv * D;
-  const uint16_t* Kh = K + ((int64_t)b * Ncap * Hkv + hkv) * D;
-  const uint16_t* Vh = V + ((int64_t)b * Ncap * Hkv + hkv) * D;
+  uint16_t* const Kh = K + ((int64_t)b * Ncap * Hkv + hkv) * D;
+  uint16_t* const Vh = V + ((int64_t)b * Ncap * Hkv + hkv) * D;
 
   // Q^T fragments of this lane's row; rows past the packed rows read 0.
   const int qbytes = (int)((int64_t)Nq * q_rs * 2);
@@ -194,6 +200,29 @@ attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     if (t + 1 < nt) issue_tile(t + 1, smem + ((t + 1) & 1) * C::kStage);
     const uint16_t* st = smem + (t & 1) * C::kStage;
     const int j0 = (t0 + t) * BN;
+    // The new rows of this tile come from k_new / v_new: they replace what
+    // the tile load brought from those cache rows (which another workgroup
+    // may be writing just now), and the workgroups of the first row block
+    // write them to the cache (each cache row belongs to one split).
+    // Workgroup-uniform; at most a few tiles per call.
+    const int new_lo = max(sl_b, j0), new_hi = min(nk, j0 + BN);
+    if (new_lo < new_hi) {
+      uint16_t* const sw = smem + (t & 1) * C::kStage;
+      const int items = (new_hi - new_lo) * C::kChunks;
+      for (int it = tid; it < items; it += C::kThreads) {
+        const int pos = new_lo + it / C::kChunks, c = it % C::kChunks;
+        const int64_t src = (((int64_t)b * Nnew + (pos - sl_b)) * Hkv + hkv) * D + 8 * c;
+        const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(Kn + src);
+        const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(Vn + src);
+        *reinterpret_cast<u32x4_t*>(sw + (pos - j0) * KS + 8 * c) = kv;
+        *reinterpret_cast<u32x4_t*>(sw + C::kKElems + (pos - j0) * VS + 8 * c) = vv;
+        if (rb == 0) {
+          *reinterpret_cast<u32x4_t*>(Kh + (int64_t)pos * kv_rs + 8 * c) = kv;
+          *reinterpret_cast<u32x4_t*>(Vh + (int64_t)pos * kv_rs + 8 * c) = vv;
+        }
+      }
+      __syncthreads();
+    }
 
     if (wave_live) {
       f32x16_t sacc[NKB];

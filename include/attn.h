@@ -293,7 +293,9 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* out
  * Validation as attn_fwd; B == 0, or Nq == 0 with Nnew == 0, is a no-op;
  * ATTN_ERR_WORKSPACE when workspace_bytes is too small; ATTN_ERR_ALIASING
  * when a written buffer (caches, out, lse, workspace) overlaps another
- * buffer.  Up to three kernels are enqueued on `stream`.
+ * buffer.  One or two kernels are enqueued on `stream` (the split attention,
+ * which also appends the new rows, and with several splits their merge;
+ * with Nq == 0 one append kernel).
  */
 int attn_decode(const void* q, void* k_cache, void* v_cache, const int* cache_seqlens,
                 const void* k_new, const void* v_new, void* out, float* lse,

@@ -30,11 +30,12 @@ def run_case(B, Hq, Hkv, Nq, Ncap, Nnew, d, dt, causal, lens, splits, seed, scal
     _, kn, vn = make_qkv(B, 1, max(Nnew, 1), 1, Hkv, d, dt, 1.0, seed + 2)
     kn, vn = kn[:, :Nnew].contiguous(), vn[:, :Nnew].contiguous()
     seqlens = torch.tensor(lens, dtype=torch.int32)
-    # expected caches after the append
+    # expected caches after the append (rows at or past Ncap are not written)
     ke, ve = kc.clone(), vc.clone()
     for b in range(B):
-        ke[b, lens[b]:lens[b] + Nnew] = kn[b]
-        ve[b, lens[b]:lens[b] + Nnew] = vn[b]
+        m = max(0, min(Nnew, Ncap - lens[b]))
+        ke[b, lens[b]:lens[b] + m] = kn[b, :m]
+        ve[b, lens[b]:lens[b] + m] = vn[b, :m]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     kg, vg = kc.cuda(), vc.cuda()
     out, lse = attn_decode(q.cuda(), kg, vg, seqlens.cuda(), kn.cuda() if Nnew else None,
@@ -44,7 +45,7 @@ def run_case(B, Hq, Hkv, Nq, Ncap, Nnew, d, dt, causal, lens, splits, seed, scal
     out, lse = out.cpu().double().numpy(), lse.cpu().double().numpy()
     worst = 0.0
     for b in range(B):
-        n = lens[b] + Nnew
+        n = min(Ncap, lens[b] + Nnew)
         O, L = oracle.attention(q[b:b + 1], ke[b:b + 1, :n], ve[b:b + 1, :n], scale, causal)
         err = np.abs(out[b:b + 1] - O)
         assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (b, err.max(), err.mean())
@@ -69,6 +70,9 @@ CASES = [  # B, Hq, Hkv, Nq, Ncap, Nnew, d, dtype, causal, lens, splits
     (2, 64, 8, 1, 4096, 1, 128, "bf16", True, [4095, 1000], 16),
     (1, 32, 4, 16, 513, 16, 128, "bf16", True, [200], 0),              # 128 packed rows per KV head
     (1, 40, 4, 16, 300, 2, 64, "bf16", True, [40], 4),                 # 160 packed rows: two row blocks
+    (2, 8, 2, 2, 700, 40, 64, "fp16", True, [20, 600], 5),             # new rows across tiles and splits
+    (1, 8, 2, 3, 300, 16, 128, "bf16", True, [290], 3),                # new rows past Ncap are dropped
+    (1, 48, 4, 12, 400, 12, 128, "bf16", True, [100], 4),              # two row blocks append once
 ]
 
 
@@ -137,3 +141,29 @@ def test_decode_workload_full_size(name):
         assert np.abs(lse[b:b + 1] - L).max() <= LSE_ABS
         worst = max(worst, float(err.max()))
     print(f"[parity-decode] {name}: worst max-abs {worst:.3e}", flush=True)
+
+
+def test_decode_append_only_without_query_rows():
+    # Nq = 0: the call only appends (the append kernel); with query rows the
+    # attention kernel appends, and both leave the same caches.
+    from exact_tiled_attention_35_amd import attn_decode
+
+    B, Hkv, Ncap, Nnew, d = 2, 4, 200, 5, 128
+    _, kc, vc = make_qkv(B, 1, Ncap, 1, Hkv, d, "bf16", 1.0, 950)
+    _, kn, vn = make_qkv(B, 1, Nnew, 1, Hkv, d, "bf16", 1.0, 951)
+    lens = [10, 197]  # the second sequence's last two new rows fall past Ncap
+    sl = torch.tensor(lens, dtype=torch.int32).cuda()
+    caches = []
+    for Nq in (0, 1):
+        q = make_qkv(B, max(Nq, 1), 1, 8, 8, d, "bf16", 1.0, 952)[0][:, :Nq].contiguous()
+        kg, vg = kc.cuda(), vc.cuda()
+        attn_decode(q.cuda(), kg, vg, sl, kn.cuda(), vn.cuda(), None, True)
+        torch.cuda.synchronize()
+        caches.append((kg.cpu(), vg.cpu()))
+    ke, ve = kc.clone(), vc.clone()
+    for b in range(B):
+        m = max(0, min(Nnew, Ncap - lens[b]))
+        ke[b, lens[b]:lens[b] + m] = kn[b, :m]
+        ve[b, lens[b]:lens[b] + m] = vn[b, :m]
+    for kg, vg in caches:
+        assert torch.equal(kg, ke) and torch.equal(vg, ve)
