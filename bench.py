@@ -55,7 +55,8 @@ OP_KERNELS = {
     # pipelined one (small grids use attn_fwd_splitk_kernel)
     "fwd": ("attn_fwd_kernel", "attn_fwd_pipe_kernel"),
     "bwd": ("attn_bwd_dq_kernel", "attn_bwd_dkdv_kernel"),
-    "decode": ("kv_append_kernel", "attn_decode_kernel", "attn_decode_merge_kernel"),
+    # the split attention kernel appends the new rows itself
+    "decode": ("attn_decode_kernel", "attn_decode_merge_kernel"),
 }
 
 
@@ -843,7 +844,7 @@ def bench_decode(args, w, dev):
             "kernel_avg_us": round(avg_s * 1e6, 2),
             "kernel_median_us": per_launch["median_us"],
             "kernel_min_us": per_launch["min_us"],
-            "unit_of_work": "one attn_decode call: append, split attention and merge kernels",
+            "unit_of_work": "one attn_decode call: split attention (appending the new rows) and merge kernels",
         },
         "clock": sustained_clock(step, stream, args.clock_seconds, achieved, peak),
         "host": host_info("decode"),
