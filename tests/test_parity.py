@@ -107,16 +107,20 @@ def test_wide_grid_against_oracle(case):
     assert_close(out, lse, O, L, str(case))
 
 
-@pytest.mark.parametrize("Nk", [33, 64, 65, 200, 1000])
+@pytest.mark.parametrize("Nk", [33, 64, 65, 97, 200, 1000, 2100])
 @pytest.mark.parametrize("causal", [False, True])
-def test_key_split_small_grid_edges(Nk, causal):
-    # the key-split kernel: quarter ranges of 1..8 tiles per wave, waves
-    # without keys, ragged last tiles, causal blocks whose rows see few keys
+@pytest.mark.parametrize("d", [64, 128])
+def test_key_split_small_grid_edges(d, Nk, causal):
+    # the key-split kernel: quarter ranges of 1..17 tiles per wave, waves
+    # without keys, ragged last tiles, causal blocks whose rows see few keys;
+    # at d = 64 a wave computes S^T of its next tile during the softmax of
+    # the current one, which these tile counts start, run and end
     Nq = 70
-    q, k, v = make_qkv(1, Nq, Nk, 4, 2, 128, "bf16", 1.0, 260 + Nk)
-    out, lse = gpu_attn(q, k, v, 1.0 / math.sqrt(128), causal)
-    O, L = oracle.attention(q, k, v, 1.0 / math.sqrt(128), causal)
-    assert_close(out, lse, O, L, f"Nk {Nk}")
+    dt = "fp16" if (d == 64 and causal) else "bf16"
+    q, k, v = make_qkv(1, Nq, Nk, 4, 2, d, dt, 1.0, 260 + Nk + d)
+    out, lse = gpu_attn(q, k, v, 1.0 / math.sqrt(d), causal)
+    O, L = oracle.attention(q, k, v, 1.0 / math.sqrt(d), causal)
+    assert_close(out, lse, O, L, f"d {d} Nk {Nk}")
 
 
 # d = 256 goes to the kernel that computes S^T of tile t+1 during the
@@ -158,7 +162,8 @@ def lowp_baseline(q, k, v, scale, causal):
 
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 1.0, 0.02])
 @pytest.mark.parametrize("causal", [False, True])
-def test_unusual_scales(scale, causal):
+@pytest.mark.parametrize("d", [64, 128])
+def test_unusual_scales(d, scale, causal):
     # Negative scale (softmax of negated scores), zero (uniform weights),
     # large (near one-hot rows: stresses the running-max updates), tiny.
     # Away from the workloads' score distribution the 1e-2 bound can sit
@@ -167,7 +172,7 @@ def test_unusual_scales(scale, causal):
     # (hysenlabs.com page, section "Tests, BSD-3-Clause und Zitierpraxis"):
     # the max error is at most twice that of a plain low-precision attention
     # against the same fp64 reference.  The mean bound is kept as well.
-    q, k, v = make_qkv(1, 300, 300, 2, 1, 128, "bf16", 1.0, 300)
+    q, k, v = make_qkv(1, 300, 300, 2, 1, d, "bf16", 1.0, 300)
     out, lse = gpu_attn(q, k, v, scale, causal)
     O, L = oracle.attention(q, k, v, scale, causal)
     base = np.abs(lowp_baseline(q, k, v, scale, causal) - O)
