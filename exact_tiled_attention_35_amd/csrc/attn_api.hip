@@ -14,6 +14,7 @@
 
 #include "attn_fwd_kernel.hpp"
 #include "attn_fwd_pipe_kernel.hpp"
+#include "attn_fwd_k16_kernel.hpp"
 #include "attn_fwd_splitk_kernel.hpp"
 #include "attn_host.hpp"
 
@@ -63,6 +64,18 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, i
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                          static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq,
                          Hkv, Nq, Nk, nqb, total, c_log2);
+      return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    }
+  }
+  // d = 128 without score variants (plain, packed sequences, block mask):
+  // the same tiling on 16x16x32 matrix instructions.
+  if constexpr (!MODS && D == 128) {
+    if (scale > 0.f) {
+      hipLaunchKernelGGL((eta::attn_fwd_k16_kernel<D, BF16, CAUSAL, VARLEN, SPARSE>), dim3(total),
+                         dim3(eta::K16Cfg<D>::kThreads), 0, stream,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq,
+                         Hkv, Nq, Nk, nqb, total, c_log2, va, bm);
       return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
     }
   }

@@ -32,6 +32,20 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t
   }
 }
 
+// D = A B + C with A 16x32, B 32x16 (v_mfma_f32_16x16x32_{bf16,f16}): lane l
+// holds A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16] for e = 0..7,
+// and D[4 (l / 16) + r][l % 16] for r = 0..3.
+template <bool BF16>
+__device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
 // Round 8 floats to the element type (nearest-even) and pack them.
 template <bool BF16>
 __device__ __forceinline__ u32x4_t pack8(f32x8_t x) {

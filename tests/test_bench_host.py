@@ -154,6 +154,13 @@ def test_traffic_summary_needs_the_kernel_and_the_copy(tmp_path, monkeypatch):
     bench.write_traffic_summary(str(fetch), str(write), 1, workload=HEADLINE, op="fwd")
     rec = json.load(open(tmp_path / "t.json"))["workloads"][HEADLINE]
     assert rec["FETCH_SIZE_KiB_per_launch"] == 200.0
+    # the plain d = 128 workloads run the 16x16x32 kernel
+    k16 = "void eta::attn_fwd_k16_kernel<128, true, false>(...)"
+    _write_counter_csv(fetch, "FETCH_SIZE", [(k16, 300.0), ("neg_kernel", 512.0)])
+    _write_counter_csv(write, "WRITE_SIZE", [(k16, 30.0), ("neg_kernel", 1024.0)])
+    bench.write_traffic_summary(str(fetch), str(write), 1, workload=HEADLINE, op="fwd")
+    rec = json.load(open(tmp_path / "t.json"))["workloads"][HEADLINE]
+    assert rec["FETCH_SIZE_KiB_per_launch"] == 300.0
 
 
 def test_kernel_source_hash_ignores_comments_only(tmp_path, monkeypatch):

@@ -273,6 +273,58 @@ def test_rising_scores(d, dt, slope, causal):
     assert_close(out, lse, O, L, f"slope {slope}")
 
 
+@pytest.mark.parametrize("slope", [-0.5, 0.05, 0.4, 3.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_wide_grid(slope, causal):
+    # The same ramps on a grid of 128 row blocks (one query head per block,
+    # all sharing the one ramped K head), so that d = 128 runs the 128-row
+    # kernel instead of the key-split one.
+    N, Hq = 128, 128
+    q, k, v = make_qkv(1, N, N, Hq, 1, 128, "bf16", 1.0, 406)
+    scale = 1.0 / math.sqrt(128)
+    q = q.clone()
+    k = k.clone()
+    q[..., 0] = 1.0
+    ramp = slope * torch.arange(N, dtype=torch.float64) / (scale * math.log2(math.e))
+    k[0, :, 0, 0] = ramp.to(k.dtype)
+    out, lse = gpu_attn(q, k, v, scale, causal)
+    O, L = oracle.attention(q, k, v, scale, causal)
+    if slope < 3.0:
+        assert_close(out, lse, O, L, f"slope {slope}")
+        return
+    # 3 log2 units per key make every row nearly one-hot on its last keys,
+    # |O| then reaches |V| ~ 4 and the bf16 output rounding alone (half-ulp
+    # 7.8e-3 in [2, 4)) nearly fills the 1e-2 bound: this off-distribution
+    # case takes the pages' rule (hysenlabs.com, section "Tests, BSD-3-Clause
+    # und Zitierpraxis") against a plain low-precision attention, as
+    # test_unusual_scales does.
+    base = np.abs(lowp_baseline(q, k, v, scale, causal) - O)
+    err = np.abs(out.double().numpy() - O)
+    assert err.max() <= 2.0 * base.max(), (err.max(), base.max())
+    assert err.mean() <= max(MEAN_ABS, 2.0 * base.mean())
+    assert np.abs(lse.double().numpy() - L).max() <= LSE_ABS
+
+
+# d = 128 grids of 128 or more row blocks (the 16x16x32 kernel): key and row
+# counts around the 64-key tile and the 16-row halves of a wave's rows, both
+# causal alignments (Nq < Nk, Nq > Nk: rows without keys), GQA and MQA.
+K16_EDGES = [(16, 1), (17, 63), (33, 64), (48, 65), (100, 100), (129, 127), (200, 96),
+             (64, 1000), (250, 30), (31, 300)]
+
+
+@pytest.mark.parametrize("nq_nk", K16_EDGES, ids=lambda c: "N%dx%d" % c)
+@pytest.mark.parametrize("causal", [False, True])
+def test_d128_wide_grid_edges(nq_nk, causal):
+    Nq, Nk = nq_nk
+    Hq, Hkv = (128, 8) if causal else (128, 1)
+    dt = "fp16" if Nq % 2 else "bf16"
+    q, k, v = make_qkv(1, Nq, Nk, Hq, Hkv, 128, dt, 1.0, 500 + K16_EDGES.index(nq_nk))
+    scale = 1.0 / math.sqrt(128)
+    out, lse = gpu_attn(q, k, v, scale, causal)
+    O, L = oracle.attention(q, k, v, scale, causal)
+    assert_close(out, lse, O, L, f"Nq {Nq} Nk {Nk}")
+
+
 def test_run_to_run_bitwise_determinism():
     q, k, v = make_qkv(2, 700, 700, 8, 2, 128, "bf16", 1.0, 404)
     a = gpu_attn(q, k, v, 0.088, True)
