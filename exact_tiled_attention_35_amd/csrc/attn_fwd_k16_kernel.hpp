@@ -23,8 +23,8 @@
 //    the registers of S^T blocks 2 kk and 2 kk + 1 -- so P^T packs from the
 //    accumulators without exchanges, and the A operand V^T takes the same
 //    key order from two LDS transpose reads (4 consecutive keys each).
-//  * The V row stride is 8 (mod 16) dwords, so the 8 rows x 32 bytes of a
-//    32-lane transpose-read pass cover the 64 banks once.
+//  * K and V rows are padded to a stride of 8 (mod 16) dwords, which keeps
+//    both operand reads free of LDS bank conflicts (measured).
 //
 // Plain, packed-sequence (VARLEN) and block-mask (SPARSE) instances, with
 // attn_fwd_kernel's work mapping, row offsets and tile walk for the latter
@@ -49,7 +49,7 @@ struct K16Cfg {
   static constexpr int BM = 32 * kWaves;                 // query rows per workgroup
   static constexpr int BN = 64;                          // keys per K/V tile
   static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
-  static constexpr int KCP = kChunks + 1;                // K row, in 16-byte slots
+  static constexpr int KCP = kChunks + 2;                // K row, in 16-byte slots
   static constexpr int VCP = kChunks + 2;                // V row, in 16-byte slots
   static constexpr int KS = 8 * KCP, VS = 8 * VCP;       // row strides (elements)
   static constexpr int kKInst = (BN * KCP + 63) / 64;    // direct-load instructions per K tile
@@ -62,8 +62,12 @@ struct K16Cfg {
   static constexpr int kEpiElems = kWaves * 32 * (D + 8);  // the epilogue's staged rows
   static constexpr int kLdsElems = 2 * kStage > kEpiElems ? 2 * kStage : kEpiElems;
   static_assert(D == 64 || D == 128, "the 16x16x32 kernel serves d = 64 and d = 128");
-  static_assert((KS / 2) % 8 == 4, "16 K rows of a 16-byte read pass on distinct banks");
-  static_assert((VS / 2) % 16 == 8, "8 V rows of a transpose-read pass on distinct banks");
+  // Row strides of 8 (mod 16) dwords: for these read patterns (K: 16 rows x
+  // 64 bytes per 16-byte read; V: 16 rows x 32 bytes per transpose read)
+  // the counters show no bank conflicts in the tile loop, where a K stride
+  // of 4 (mod 8) dwords cost about 4 conflict cycles per K read, and V
+  // strides of 4 (mod 8) or 16 (mod 64) dwords 2 per transpose read.
+  static_assert((KS / 2) % 16 == 8 && (VS / 2) % 16 == 8, "conflict-free row strides");
   static_assert(2 * kLdsElems * 2 <= 160 * 1024, "two workgroups per CU");
 };
 
