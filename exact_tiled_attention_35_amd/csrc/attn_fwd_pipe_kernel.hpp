@@ -14,10 +14,16 @@
 //    softmax and the MFMAs run back to back (counters: 9 of 1,022 MFMA-busy
 //    cycles per tile co-issue a VALU instruction).
 //  * Here each wave computes S^T of tile t+1 while it exponentiates tile t:
-//    the 16 MFMAs of the next S^T product and the exp2 / sum of the current
-//    tile sit in one basic block, interleaved one MFMA to a few VALU
+//    the 32 MFMAs of the next S^T product and the exp2 / sum of the current
+//    tile sit in one basic block, interleaved two MFMAs to a few VALU
 //    instructions, so that the VALU work issues in the shadow of the matrix
 //    work.  Then O^T += V^T P^T for tile t.
+//  * The products run on v_mfma_f32_16x16x32 in the layout of
+//    attn_fwd_k16_kernel (lane group g = l / 16 and c = l % 16: S^T and O^T
+//    in 16 x 16 blocks, two query blocks per wave, P^T packed from the S^T
+//    registers, V^T from two transpose reads per operand; K, Q and V rows
+//    padded to 8 (mod 16) dwords, free of LDS bank conflicts): 1.2-2.7 %
+//    faster than the same pipeline on v_mfma_f32_32x32x16.
 //  * K therefore runs one tile ahead of V: three K stages (tile t for the
 //    rare recomputation of a lean tile, t+1 being multiplied, t+2 loading)
 //    and two V stages (t being multiplied, t+1 loading), plus the LDS copy of
@@ -45,8 +51,8 @@ struct PipeCfg {
   static constexpr int BM = 32 * kWaves;  // query rows per workgroup
   static constexpr int BN = 32;           // keys per K/V tile
   static constexpr int kChunks = D / 8;   // 16-byte chunks per row
-  static constexpr int KCP = kChunks + 1; // K (and Q) row, in 16-byte slots
-  static constexpr int VCP = kChunks + 4; // V row, in 16-byte slots
+  static constexpr int KCP = kChunks + 2; // K (and Q) row, in 16-byte slots
+  static constexpr int VCP = kChunks + 2; // V row, in 16-byte slots
   static constexpr int KS = 8 * KCP;      // K / Q row stride (elements)
   static constexpr int VS = 8 * VCP;      // V row stride (elements)
   static constexpr int kKInst = (BN * KCP + 63) / 64;
@@ -63,7 +69,7 @@ struct PipeCfg {
   static constexpr int kVInstPerWave = (kVInst + kWaves - 1) / kWaves;
   static constexpr int kQInstPerWave = (kQInst + kWaves - 1) / kWaves;
   static_assert(D == 256, "the pipelined kernel is laid out for d = 256");
-  static_assert((KS / 2) % 8 == 4 && (VS / 2) % 32 == 16, "bank-conflict-free strides");
+  static_assert((KS / 2) % 16 == 8 && (VS / 2) % 16 == 8, "conflict-free row strides");
   static_assert(kLdsElems * 2 <= 160 * 1024, "LDS of one workgroup");
   static_assert(kWaves * 32 * (D + 8) <= kLdsElems, "the epilogue's staged rows fit");
 };
@@ -76,21 +82,20 @@ attn_fwd_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                      float c_log2) {
   using C = PipeCfg<D>;
   constexpr int BN = C::BN, BM = C::BM, KS = C::KS, VS = C::VS;
-  constexpr int NKS = D / 16;  // k-steps of the S^T product
-  constexpr int NDB = D / 32;  // 32-column blocks of O^T
-  constexpr int NKK = BN / 16; // 16-key steps of the PV product
+  constexpr int NK4 = D / 32;  // 32-wide k-steps of S^T
+  constexpr int NDB = D / 16;  // 16-dimension blocks of O^T
+  static_assert(BN == 32, "one 32-key step of the PV product per tile");
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::kLdsElems];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int lane = tid & 63, g = lane >> 4, c = lane & 15;
 
   const WorkItem w = map_workgroup<CAUSAL>(blockIdx.x, total, nqb, Hq);
   const int hkv = w.hq / (Hq / Hkv);
   const int q0 = w.qblk * BM;
   const int qw0 = q0 + wave * 32;
-  const int my_q = qw0 + l32;
   const int diag = Nk - Nq;  // causal: key j visible to row i iff j <= i + diag
 
   const int64_t q_rs = (int64_t)Hq * D, kv_rs = (int64_t)Hkv * D;
@@ -108,8 +113,8 @@ attn_fwd_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     for (int i = 0; i < C::kQInstPerWave; ++i) {
       const int j = wave + C::kWaves * i;
       const int sl = 64 * j + lane;
-      const int row = min(sl / C::KCP, BM - 1), c = min(sl % C::KCP, C::kChunks - 1);
-      if (j < C::kQInst) buf_load_lds16(qr, qs + 512 * j, (int)(row * q_rs * 2) + 16 * c);
+      const int row = min(sl / C::KCP, BM - 1), ch = min(sl % C::KCP, C::kChunks - 1);
+      if (j < C::kQInst) buf_load_lds16(qr, qs + 512 * j, (int)(row * q_rs * 2) + 16 * ch);
     }
   }
 
@@ -132,14 +137,14 @@ attn_fwd_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
   for (int i = 0; i < C::kKInstPerWave; ++i) {
     const int sl = 64 * (wave + C::kWaves * i) + lane;
-    const int row = min(sl / C::KCP, BN - 1), c = min(sl % C::KCP, C::kChunks - 1);
-    koff[i] = (int)(row * kv_rs * 2) + 16 * c;
+    const int row = min(sl / C::KCP, BN - 1), ch = min(sl % C::KCP, C::kChunks - 1);
+    koff[i] = (int)(row * kv_rs * 2) + 16 * ch;
   }
 #pragma unroll
   for (int i = 0; i < C::kVInstPerWave; ++i) {
     const int sl = 64 * (wave + C::kWaves * i) + lane;
-    const int row = min(sl / C::VCP, BN - 1), c = min(sl % C::VCP, C::kChunks - 1);
-    voff[i] = (int)(row * kv_rs * 2) + 16 * c;
+    const int row = min(sl / C::VCP, BN - 1), ch = min(sl % C::VCP, C::kChunks - 1);
+    voff[i] = (int)(row * kv_rs * 2) + 16 * ch;
   }
   auto issue_k = [&](int t, uint16_t* __restrict__ st) {
     const int j0 = t * BN;
@@ -162,88 +167,113 @@ attn_fwd_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   auto kstage = [&](int t) { return smem + (t % C::kKStages) * C::kKElems; };
   auto vstage = [&](int t) { return smem + C::kVBase + (t & 1) * C::kVElems; };
 
-  // ---- Operand reads from LDS.
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int k_rd = l32 * KS + 8 * hh;
-  const int q_rd = C::kQBase + (wave * 32 + l32) * KS + 8 * hh;
-  const int v_rd = (4 * hh + (i16 >> 2)) * VS + 16 * (g16 & 1) + 4 * (i16 & 3);
+  // ---- Operand reads from LDS (16x16x32 layout; lane group g = l / 16,
+  // c = l % 16): K row 16 kb + c and Q row 16 qb + c of this wave, columns
+  // 32 k4 + 8 g; for the V transpose reads lane c of group g addresses row
+  // 4 g + c / 4 (+ 16 for the second half of the key step) at column
+  // 4 (c % 4) of the 16-column block.
+  const int k_rd = c * KS + 8 * g;
+  const int q_rd = C::kQBase + (wave * 32 + c) * KS + 8 * g;
+  const int v_rd = (4 * g + (c >> 2)) * VS + 4 * (c & 3);
   auto rd16 = [](const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); };
 
-  f32x16_t oacc[NDB];
+  // O^T in 16 x 16 blocks: oacc[qb][db] register r holds dimension
+  // 16 db + 4 g + r of query qw0 + 16 qb + c.
+  f32x4_t oacc[2][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16_t{};
-  float m = -INFINITY;  // running max of t = s * c_log2 (log2 units)
-  float lsum = 0.f;     // this lane half's share of the running sum
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[qb][db] = f32x4_t{};
+  float m[2] = {-INFINITY, -INFINITY};  // running max of s * c_log2 (log2 units)
+  float lsum[2] = {0.f, 0.f};           // this lane's share of the running sums
 
-  // S^T = K Q^T (32 keys x 32 queries) from the K stage at kst.
-  auto compute_s = [&](const uint16_t* kst, f32x16_t& s) {
-    s = f32x16_t{};
+  // S^T (32 keys x 32 queries) from the K stage at kst in 16 x 16 blocks
+  // s[qb][kb] (register r: key 16 kb + 4 g + r, query 16 qb + c); per
+  // k-step each K operand feeds two consecutive MFMAs (measured 1.5 %
+  // faster here than sharing the Q^T operand instead).
+  using SBlk = f32x4_t[2][2];
+  auto compute_s = [&](const uint16_t* kst, SBlk& s) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      s = mfma_32x32x16<BF16>(rd16(kst + k_rd + 16 * ks), rd16(smem + q_rd + 16 * ks), s);
-  };
-
-  // Tile row maximum; m is raised when the tile max exceeds it by more than
-  // `threshold`, and what was accumulated is rescaled.
-  auto raise_max = [&](const f32x16_t& s, float threshold) {
-    float tmax = -INFINITY;
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) tmax = max3(tmax, s[r], s[r + 1]);
-    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float tm = tmax * c_log2;
-    if (tm > m + threshold) {
-      const float alpha = exp2_fast(m - tm);
-      m = tm;
-      lsum *= alpha;
+      for (int kb = 0; kb < 2; ++kb) s[qb][kb] = f32x4_t{};
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    for (int k4 = 0; k4 < NK4; ++k4) {
+      const u32x4_t b0 = rd16(smem + q_rd + 32 * k4), b1 = rd16(smem + q_rd + 16 * KS + 32 * k4);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4_t a = rd16(kst + k_rd + kb * 16 * KS + 32 * k4);
+        s[0][kb] = mfma_16x16x32<BF16>(a, b0, s[0][kb]);
+        s[1][kb] = mfma_16x16x32<BF16>(a, b1, s[1][kb]);
+      }
     }
   };
 
-  // p = 2^(s*c - m) in place; returns this lane half's sum of the unrounded p.
-  auto exponentiate = [&](f32x16_t& s) {
-    const float mb = m != -INFINITY ? m : 0.f;
+  // Row maximum of block qb over the tile (in-lane, then across the four
+  // lane groups); m is raised when the tile max exceeds it by more than
+  // `threshold`, and what was accumulated is rescaled.
+  auto raise_max = [&](int qb, const f32x4_t (&s)[2], float threshold) {
+    float tmax = max3(max3(s[0][0], s[0][1], s[0][2]), s[0][3], s[1][0]);
+    tmax = max3(tmax, max3(s[1][1], s[1][2], s[1][3]), tmax);
+    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float tm = tmax * c_log2;
+    if (tm > m[qb] + threshold) {
+      const float alpha = exp2_fast(m[qb] - tm);
+      m[qb] = tm;
+      lsum[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
+    }
+  };
+
+  // p = 2^(s*c - m) in place for block qb; returns this lane's sum of the
+  // unrounded p.
+  auto exponentiate = [&](int qb, f32x4_t (&s)[2]) {
+    const float mb = m[qb] != -INFINITY ? m[qb] : 0.f;
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = exp2_fast(__builtin_fmaf(s[r], c_log2, -mb));
-      const float p1 = exp2_fast(__builtin_fmaf(s[r + 1], c_log2, -mb));
-      s[r] = p0;
-      s[r + 1] = p1;
-      ps0 += p0;
-      ps1 += p1;
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const float p0 = exp2_fast(__builtin_fmaf(s[kb][r], c_log2, -mb));
+        const float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], c_log2, -mb));
+        s[kb][r] = p0;
+        s[kb][r + 1] = p1;
+        ps0 += p0;
+        ps1 += p1;
+      }
     }
     return ps0 + ps1;
   };
 
-  // O^T += V^T P^T from the V stage at vst; P as hi + lo on masked causal
-  // tiles.  The V^T operand reads run four MFMAs ahead.
-  auto pv = [&](const uint16_t* vst, const f32x16_t& p, auto with_lo) {
+  // O^T += V^T P^T from the V stage at vst: lane group g feeds the keys
+  // {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3}, the registers of S^T blocks
+  // kb = 0 and 1; P as hi + lo on masked causal tiles.  Each V^T operand
+  // feeds two consecutive MFMAs (the two query blocks).
+  auto pv = [&](const uint16_t* vst, const SBlk& p, auto with_lo) {
+    u32x4_t phi[2], plo[2];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
+    for (int qb = 0; qb < 2; ++qb) {
       f32x8_t pv8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv8[e] = p[8 * kk + e];
-      const u32x4_t phi = pack8<BF16>(pv8);
-      u32x4_t plo;
-      if constexpr (decltype(with_lo)::value) plo = pack8<BF16>(pv8 - unpack8<BF16>(phi));
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2_t x0 = lds_read_tr4(vst + v_rd + 16 * kk * VS + 32 * db);
-        const u32x2_t x1 = lds_read_tr4(vst + v_rd + (16 * kk + 8) * VS + 32 * db);
-        const u32x4_t a = {x0[0], x0[1], x1[0], x1[1]};
-        oacc[db] = mfma_32x32x16<BF16>(a, phi, oacc[db]);
-        if constexpr (decltype(with_lo)::value) oacc[db] = mfma_32x32x16<BF16>(a, plo, oacc[db]);
+      for (int e = 0; e < 4; ++e) {
+        pv8[e] = p[qb][0][e];
+        pv8[4 + e] = p[qb][1][e];
       }
+      phi[qb] = pack8<BF16>(pv8);
+      if constexpr (decltype(with_lo)::value) plo[qb] = pack8<BF16>(pv8 - unpack8<BF16>(phi[qb]));
     }
-    if constexpr (!decltype(with_lo)::value) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int i = 0; i < NKK * NDB - 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    for (int db = 0; db < NDB; ++db) {
+      const u32x2_t x0 = lds_read_tr4(vst + v_rd + 16 * db);
+      const u32x2_t x1 = lds_read_tr4(vst + v_rd + 16 * VS + 16 * db);
+      const u32x4_t a = {x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        oacc[qb][db] = mfma_16x16x32<BF16>(a, phi[qb], oacc[qb][db]);
+        if constexpr (decltype(with_lo)::value) oacc[qb][db] = mfma_16x16x32<BF16>(a, plo[qb], oacc[qb][db]);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
   };
 
@@ -253,88 +283,129 @@ attn_fwd_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // for this wave's loads.  The stages arrive as restrict-qualified
   // parameters: the transpose reads of vc then carry alias information that
   // sets them apart from the direct-to-LDS loads just issued, and need not
-  // wait for them (without it the compiler waits for every outstanding
-  // direct-to-LDS load before a transpose read, and the load latency lands
-  // in every iteration).
+  // wait for them.
   //
   // kLeanNext: a lean tile (every key visible to every row, m finite) whose
-  // successor this wave also computes.  The exponentials of s_cur are
-  // interleaved with the S^T MFMAs of tile t+1 into s_next, one score per
-  // MFMA, each step fenced so that the scheduler keeps the interleave; the K
-  // and Q operand reads run three steps ahead.  A partial row sum above
-  // kSumLimit (a score far above m, rare) recomputes S of tile t from kc and
-  // takes the maximum path.
+  // successor this wave also computes.  The 16 exponentials of s_cur are
+  // interleaved with the 32 S^T MFMAs of tile t+1 into s_next, one score per
+  // two MFMAs (the two that share a K operand), each step fenced so that the
+  // scheduler keeps the interleave; the K and Q operand reads run two
+  // k-steps ahead.  A partial row sum
+  // above kSumLimit (a score far above m, rare) recomputes S of tile t from
+  // kc and takes the maximum path.
   // kOther: any other tile of this wave (the first, the masked ones, a lean
   // tile without a successor): the maximum path with masking where the tile
   // crosses the causal diagonal or the ragged end, then S^T of tile t+1 if
   // this wave computes it.
   constexpr int kLeanNext = 0, kOther = 1;
-  auto step = [&](int t, auto kind, f32x16_t& s_cur, f32x16_t& s_next,
+  auto step = [&](int t, auto kind, SBlk& s_cur, SBlk& s_next,
                   uint16_t* __restrict__ kl, uint16_t* __restrict__ vl,
                   const uint16_t* __restrict__ kc, const uint16_t* __restrict__ kn,
                   const uint16_t* __restrict__ vc) {
     if (t + 2 < nt) issue_k(t + 2, kl);
     if (t + 1 < nt) issue_v(t + 1, vl);
     if constexpr (decltype(kind)::value == kLeanNext) {
-      const float mb = m;
-      float ps0 = 0.f, ps1 = 0.f;
-      f32x16_t sn = f32x16_t{};
-      u32x4_t ka[4], qa[4];
+      float ps[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+      SBlk sn;
 #pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        ka[i] = rd16(kn + k_rd + 16 * i);
-        qa[i] = rd16(smem + q_rd + 16 * i);
-      }
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        if (ks + 3 < NKS) {
-          ka[(ks + 3) & 3] = rd16(kn + k_rd + 16 * (ks + 3));
-          qa[(ks + 3) & 3] = rd16(smem + q_rd + 16 * (ks + 3));
+        for (int kb = 0; kb < 2; ++kb) sn[qb][kb] = f32x4_t{};
+      // operands of k-step k4: ka[k4 % 3][kb], qa[k4 % 3][qb]
+      u32x4_t ka[3][2], qa[3][2];
+      auto fetch = [&](int k4) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          ka[k4 % 3][x] = rd16(kn + k_rd + x * 16 * KS + 32 * k4);
+          qa[k4 % 3][x] = rd16(smem + q_rd + x * 16 * KS + 32 * k4);
         }
-        sn = mfma_32x32x16<BF16>(ka[ks & 3], qa[ks & 3], sn);
-        const float p = exp2_fast(__builtin_fmaf(s_cur[ks], c_log2, -mb));
-        s_cur[ks] = p;
-        if (ks & 1)
-          ps1 += p;
-        else
-          ps0 += p;
-        __builtin_amdgcn_sched_barrier(0);
+      };
+      fetch(0);
+      fetch(1);
+#pragma unroll
+      for (int k4 = 0; k4 < NK4; ++k4) {
+        if (k4 + 2 < NK4) fetch(k4 + 2);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            sn[qb][kb] = mfma_16x16x32<BF16>(ka[k4 % 3][kb], qa[k4 % 3][qb], sn[qb][kb]);
+            if (qb == 1) {
+              // score i = 2 k4 + kb of the 16: block i / 8, kb (i / 4) % 2, r i % 4
+              const int i = 2 * k4 + kb;
+              const int eq = i / 8, ekb = (i / 4) % 2, er = i % 4;
+              const float p = exp2_fast(__builtin_fmaf(s_cur[eq][ekb][er], c_log2, -m[eq]));
+              s_cur[eq][ekb][er] = p;
+              ps[eq][er & 1] += p;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       }
-      s_next = sn;
-      float psum = ps0 + ps1;
-      if (__builtin_amdgcn_ballot_w64(!(psum <= kSumLimit)) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s_next[qb][kb] = sn[qb][kb];
+      float psum[2];
+      bool over = false;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        psum[qb] = ps[qb][0] + ps[qb][1];
+        over = over || !(psum[qb] <= kSumLimit);
+      }
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
         compute_s(kc, s_cur);
-        raise_max(s_cur, 0.0f);
-        psum = exponentiate(s_cur);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          raise_max(qb, s_cur[qb], 0.0f);
+          psum[qb] = exponentiate(qb, s_cur[qb]);
+        }
       }
-      lsum += psum;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) lsum[qb] += psum[qb];
       pv(vc, s_cur, std::false_type{});
     } else if (t < wt) {
       const int j0 = t * BN;
       const bool lean = t >= 1 && t < nf;
       bool need_mask = false;
-      float psum;
       if (lean) {
-        psum = exponentiate(s_cur);
-        if (__builtin_amdgcn_ballot_w64(!(psum <= kSumLimit)) != 0) {
-          compute_s(kc, s_cur);
-          raise_max(s_cur, 0.0f);
-          psum = exponentiate(s_cur);
-        }
-      } else {
-        need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + diag);
-        if (need_mask) {
+        float psum[2];
+        bool over = false;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool vis = j < Nk && (!CAUSAL || j <= my_q + diag);
-            s_cur[r] = vis ? s_cur[r] : -INFINITY;
+        for (int qb = 0; qb < 2; ++qb) {
+          psum[qb] = exponentiate(qb, s_cur[qb]);
+          over = over || !(psum[qb] <= kSumLimit);
+        }
+        if (__builtin_amdgcn_ballot_w64(over) != 0) {
+          compute_s(kc, s_cur);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            raise_max(qb, s_cur[qb], 0.0f);
+            psum[qb] = exponentiate(qb, s_cur[qb]);
           }
         }
-        raise_max(s_cur, kRescaleThreshold);
-        psum = exponentiate(s_cur);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) lsum[qb] += psum[qb];
+      } else {
+        need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + diag);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          if (need_mask) {
+            const int my_q = qw0 + 16 * qb + c;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int j = j0 + 16 * kb + 4 * g + r;
+                const bool vis = j < Nk && (!CAUSAL || j <= my_q + diag);
+                s_cur[qb][kb][r] = vis ? s_cur[qb][kb][r] : -INFINITY;
+              }
+            }
+          }
+          raise_max(qb, s_cur[qb], kRescaleThreshold);
+          lsum[qb] += exponentiate(qb, s_cur[qb]);
+        }
       }
-      lsum += psum;
       if (t + 1 < wt) compute_s(kn, s_next);
       if (CAUSAL && need_mask)
         pv(vc, s_cur, std::true_type{});
@@ -346,9 +417,15 @@ attn_fwd_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   };
   using LeanNext = std::integral_constant<int, kLeanNext>;
   using Other = std::integral_constant<int, kOther>;
-  auto run = [&](int t, auto kind, f32x16_t& s_cur, f32x16_t& s_next) {
+  auto run = [&](int t, auto kind, SBlk& s_cur, SBlk& s_next) {
     step(t, kind, s_cur, s_next, kstage(t + 2), vstage(t + 1), kstage(t), kstage(t + 1),
          vstage(t));
+  };
+  auto copy_s = [](SBlk& dst, const SBlk& src) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) dst[qb][kb] = src[qb][kb];
   };
 
   // ---- Prologue: Q, K tiles 0 and 1, V tile 0; S of tile 0.
@@ -359,7 +436,7 @@ attn_fwd_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   if (nt > 1) issue_k(1, kstage(1));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  f32x16_t sa, sb;
+  SBlk sa, sb;
   if (wt > 0) compute_s(kstage(0), sa);
 
   // Tile 0 (m = -inf: maximum path), then the lean tiles with a successor
@@ -376,21 +453,51 @@ attn_fwd_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
   if (t < lean_end) {
     run(t, LeanNext{}, sb, sa);
-    sb = sa;
+    copy_s(sb, sa);
     ++t;
   }
   for (; t < nt; ++t) {
     run(t, Other{}, sb, sa);
-    sb = sa;
+    copy_s(sb, sa);
   }
 
   // ---- Epilogue (every wave passed the last barrier: the stages are idle).
-  const float lt = lsum + __shfl_xor(lsum, 32);
-  store_rows<D, BF16>(smem, wave, lane, oacc, lt > 0.f ? 1.0f / lt : 0.f,
-                      make_rsrc(O + qo_off, span_bytes(qw0, 32, Nq, q_rs, D)), q_rs);
+  // Rows are normalised, rounded and staged in this wave's slice of LDS (row
+  // 16 qb + c, 4 dimensions per block and lane group), then stored 16
+  // contiguous bytes per lane.
+  constexpr int ORS = D + 8;
+  uint16_t* const ost = smem + wave * 32 * ORS;
+  float lt[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float l = lsum[qb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    lt[qb] = l;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<u32x2_t*>(ost + (16 * qb + c) * ORS + 16 * db + 4 * g) =
+          pack4<BF16>(oacc[qb][db] * inv);
+  }
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+  const int rr = lane / CPR, cc = lane % CPR;
+  const rsrc_t orr = make_rsrc(O + qo_off, span_bytes(qw0, 32, Nq, q_rs, D));
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = RPI * i + rr;
+    buf_store16(*reinterpret_cast<const u32x4_t*>(ost + row * ORS + 8 * cc), orr,
+                (int)(row * q_rs * 2) + 16 * cc);
+  }
   const int nrows = max(0, min(32, Nq - qw0));
   const rsrc_t lr = make_rsrc(LSE + lse_off + qw0, nrows * 4);
-  buf_store4(lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY, lr, 4 * l32);
+  if (g == 0) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+      buf_store4(lt[qb] > 0.f ? (m[qb] + __builtin_amdgcn_logf(lt[qb])) * kLn2 : -INFINITY, lr,
+                 4 * (16 * qb + c));
+  }
 }
 
 }  // namespace eta
