@@ -16,14 +16,16 @@
 // Two kernels, no atomics and no workspace, so results are bitwise
 // reproducible run to run:
 //  * attn_bwd_dq_kernel: one workgroup per 128 query rows of one (b, head),
-//    4 waves x 32 rows, looping over key tiles.  Per tile and wave:
+//    4 waves x 32 rows, looping over key tiles.  Per tile and wave, on
+//    v_mfma_f32_16x16x32 in 16 x 16 blocks (the layout of the forward's
+//    attn_fwd_k16_kernel):
 //        S^T  = K Q^T    (A = K rows from LDS, B = Q^T in VGPRs)
 //        dP^T = V dO^T   (A = V rows from LDS, B = dO^T in VGPRs)
-//        dQ^T += K^T dS^T (A = K^T by LDS transpose reads, B = dS^T packed
-//                          from the accumulators)
-//    Each lane owns one query row, so lse and D are per-lane scalars.  The
-//    kernel first computes D for its rows and stores it (the dK/dV kernel
-//    reads it).
+//        dQ^T += K^T dS^T (A = K^T by LDS transpose reads of the same K
+//                          tile, B = dS^T packed from the accumulators)
+//    Each lane holds two query rows (shared by its four lane groups), so
+//    lse and D are two per-lane scalars.  The kernel first computes D for
+//    its rows and stores it (the dK/dV kernel reads it).
 //  * attn_bwd_dkdv_kernel: one workgroup per 128 keys of one (b, KV head),
 //    4 waves x 32 keys, looping over the query heads of the GQA group and
 //    their query tiles.  The roles of queries and keys are swapped relative
@@ -70,17 +72,31 @@ struct BwdLayout {
   static constexpr int tr_elems() { return ((R * TCP + 63) / 64) * 512; }
 };
 
+// Tiles read by the 16x16x32 products both as rows (16-byte reads, 16 rows
+// x 64 bytes per read) and through transpose reads (16 rows x 32 bytes):
+// rows padded to 8 (mod 16) dwords, free of bank conflicts for both (the
+// forward's attn_fwd_k16_kernel measured it), so one copy of a tile serves
+// both kinds of read.
+template <int D>
+struct Bwd16Layout {
+  static constexpr int kChunks = D / 8;
+  static constexpr int CP = kChunks + 2;   // 16-byte slots per row
+  static constexpr int RS = 8 * CP;        // row stride, elements
+  static_assert((RS / 2) % 16 == 8, "conflict-free row stride");
+  template <int R>
+  static constexpr int elems() { return ((R * CP + 63) / 64) * 512; }
+};
+
 template <int D>
 struct DqCfg {
   static constexpr int kWaves = 4, kThreads = 256, BM = 128;
   // 32-key tiles keep the LDS of a workgroup under half of the CU's, so two
   // workgroups (two waves per SIMD) share a CU.
   static constexpr int BN = 32;  // keys per tile
-  using L = BwdLayout<D>;
-  static constexpr int kKRow = L::template row_elems<BN>();
-  static constexpr int kKTr = L::template tr_elems<BN>();
-  static constexpr int kVRow = kKRow;
-  static constexpr int kStage = kKRow + kKTr + kVRow;
+  using L = Bwd16Layout<D>;
+  static constexpr int kK = L::template elems<BN>();  // K: rows for S^T, transposed for dQ
+  static constexpr int kV = kK;
+  static constexpr int kStage = kK + kV;
   static constexpr int kLdsElems = 2 * kStage;
   static constexpr int kMinWavesPerEU = (D >= 256) ? 1 : 2;
 };
@@ -138,20 +154,26 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   using C = DqCfg<D>;
   static_assert(kMaskBlock == C::BM && kMaskBlock % C::BN == 0, "a mask block is whole tiles");
   using L = typename C::L;
-  constexpr int BN = C::BN, BM = C::BM, RS = L::RS, TS = L::TS;
-  constexpr int NKS = D / 16, NKB = BN / 32, NDB = D / 32, NKK = BN / 16;
-  constexpr int kRowInst = C::kKRow / 512, kTrInst = C::kKTr / 512;
-  constexpr int kRowPW = (kRowInst + 3) / 4, kTrPW = (kTrInst + 3) / 4;
+  constexpr int BN = C::BN, BM = C::BM, RS = L::RS;
+  constexpr int NK4 = D / 32;  // 32-wide k-steps of S^T and dP^T
+  constexpr int NDB = D / 16;  // 16-dimension blocks of dQ^T
+  static_assert(BN == 32, "one 32-key step of the dQ product per tile");
+  constexpr int kInst = C::kK / 512, kPW = (kInst + 3) / 4;
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::kLdsElems];
 
+  // Lane l: group g = l / 16, c = l % 16.  S^T, dP^T and dQ^T are held in
+  // 16 x 16 blocks (v_mfma_f32_16x16x32): block (qb, kb) register r of S^T
+  // is key 16 kb + 4 g + r against query qw0 + 16 qb + c, so each lane owns
+  // the two query rows qw0 + c and qw0 + 16 + c (shared by the four lane
+  // groups); dQ^T block (qb, db) register r is dimension 16 db + 4 g + r.
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int lane = tid & 63, g = lane >> 4, c = lane & 15;
   const WorkItem w = VARLEN ? map_workgroup_packed(blockIdx.x, nqb, Hq, va.pairs)
                            : map_workgroup<CAUSAL>(blockIdx.x, total, nqb, Hq);
   const int hkv = w.hq / (Hq / Hkv);
-  const int q0 = w.qblk * BM, qw0 = q0 + wave * 32, my_q = qw0 + l32;
+  const int q0 = w.qblk * BM, qw0 = q0 + wave * 32;
   // First rows of this (b, head) in q-shaped and k-shaped tensors, and of
   // its lse / delta row; packed sequences take theirs from the prefix sums.
   int64_t q_row0 = (int64_t)w.b * Nq, k_row0 = (int64_t)w.b * Nk;
@@ -173,31 +195,40 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const uint16_t* Kh = K + (k_row0 * Hkv + hkv) * D;
   const uint16_t* Vh = V + (k_row0 * Hkv + hkv) * D;
 
-  // Q^T and dO^T fragments (B operands), O for D.  Rows >= Nq read as 0.
+  // Q^T and dO^T fragments (B operands) of the two row blocks, O for D.
+  // Rows >= Nq read as 0.
   const int rspan = span_bytes(qw0, 32, Nq, q_rs, D);
   const rsrc_t qr = make_rsrc(Q + qo_off, rspan);
   const rsrc_t dor = make_rsrc(dO + qo_off, rspan);
   const rsrc_t orr = make_rsrc(O + qo_off, rspan);
-  const int fvoff = (int)(l32 * q_rs * 2) + 16 * hh;
-  u32x4_t qf[NKS], df[NKS];
-  float dsum = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    qf[ks] = buf_load16(qr, fvoff + 32 * ks);
-    df[ks] = buf_load16(dor, fvoff + 32 * ks);
-    const u32x4_t o = buf_load16(orr, fvoff + 32 * ks);
-    const f32x8_t a = unpack8<BF16>(df[ks]), b = unpack8<BF16>(o);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf(a[e], b[e], dsum);
-  }
-  const float Di = dsum + __shfl_xor(dsum, 32);
+  u32x4_t qf[2][NK4], df[2][NK4];
+  float Di[2], lse2[2];
   const int nrows = max(0, min(32, Nq - qw0));
   const int64_t vec_off = vec_row0 + qw0;
-  if (hh == 0) buf_store4(Di, make_rsrc(Dlt + vec_off, nrows * 4), 4 * l32);
-  // lse in log2 units; an empty row (lse = -inf) has every key masked.
-  const float lse_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                    make_rsrc(LSE + vec_off, nrows * 4), 4 * l32, 0, 0));
-  const float lse2 = lse_v * kLog2e;
+  const rsrc_t lr = make_rsrc(LSE + vec_off, nrows * 4);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int fvoff = (int)((16 * qb + c) * q_rs * 2) + 16 * g;
+    float dsum = 0.f;
+#pragma unroll
+    for (int k4 = 0; k4 < NK4; ++k4) {
+      qf[qb][k4] = buf_load16(qr, fvoff + 64 * k4);
+      df[qb][k4] = buf_load16(dor, fvoff + 64 * k4);
+      const u32x4_t o = buf_load16(orr, fvoff + 64 * k4);
+      const f32x8_t a = unpack8<BF16>(df[qb][k4]), b = unpack8<BF16>(o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf(a[e], b[e], dsum);
+    }
+    dsum += __shfl_xor(dsum, 16);
+    Di[qb] = dsum + __shfl_xor(dsum, 32);
+    // lse in log2 units; an empty row (lse = -inf) has every key masked.
+    lse2[qb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, 4 * (16 * qb + c), 0, 0)) * kLog2e;
+  }
+  if (g == 0) {
+    const rsrc_t dr = make_rsrc(Dlt + vec_off, nrows * 4);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) buf_store4(Di[qb], dr, 4 * (16 * qb + c));
+  }
 
   // Key range of the workgroup and of this wave.
   int kv_end = Nk;
@@ -225,13 +256,17 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   }
   // Score variants in log2 units (softcap: exp2 argument 2 x log2e with
   // x = sigma s / cap, output scale cap log2e), and the distances
-  // dist = my_q + diag - j this row sees as one interval [vis_lo, vis_hi]
+  // dist = row + diag - j each row sees as one interval [vis_lo, vis_hi]
   // (keys past the end, causal, window).
   const float sigma_l2 = mods.sigma * kLog2e, slope_l2 = slope * kLog2e, cap_l2 = mods.cap * kLog2e;
   const float cap_in = kCap ? mods.sigma * __builtin_amdgcn_rcpf(mods.cap) * (2.0f * kLog2e) : 0.f;
-  int lo_i = my_q - Nq + 1, hi_i = 1 << 30;
-  if (CAUSAL) lo_i = max(lo_i, 0);
-  if (MODS && mods.right >= 0) lo_i = max(lo_i, -mods.right);
+  int lo_i[2], hi_i = 1 << 30;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    lo_i[qb] = qw0 + 16 * qb + c - Nq + 1;
+    if (CAUSAL) lo_i[qb] = max(lo_i[qb], 0);
+    if (MODS && mods.right >= 0) lo_i[qb] = max(lo_i[qb], -mods.right);
+  }
   if (MODS && mods.left >= 0) hi_i = mods.left;
 
   // Block sparsity: the tiles of the flagged key blocks below kv_end, in key
@@ -249,11 +284,11 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int last_tiles = (kv_end - kMaskBlock * last + BN - 1) / BN;
     int blocks = 0;
     nt = 0;
-    for (int c = 0; c < sp_nchunks; ++c) {
-      const uint64_t bits = flag_word(sp_mr, c, 1, lane);
-      if (c == 0) sp_bits = bits;
+    for (int ci = 0; ci < sp_nchunks; ++ci) {
+      const uint64_t bits = flag_word(sp_mr, ci, 1, lane);
+      if (ci == 0) sp_bits = bits;
       blocks += __builtin_popcountll(bits);
-      if (last / 64 == c && ((bits >> (last % 64)) & 1)) nt -= TPB - last_tiles;
+      if (last / 64 == ci && ((bits >> (last % 64)) & 1)) nt -= TPB - last_tiles;
     }
     nt += TPB * blocks;
   }
@@ -268,25 +303,29 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     return sp_blk * kMaskBlock + sp_sub * BN;
   };
 
-  int roff[kRowPW], toff[kTrPW];
-  tile_offsets<BN, L::RCP, D>(wave, lane, kv_rs, roff);
-  tile_offsets<BN, L::TCP, D>(wave, lane, kv_rs, toff);
+  // K and V tiles, one padded row-major copy each.
+  int toff[kPW];
+  tile_offsets<BN, L::CP, D>(wave, lane, kv_rs, toff);
   auto issue_tile = [&](int j0, uint16_t* st) {
     const int bytes = span_bytes(j0, BN, Nk, kv_rs, D);
     const rsrc_t kr = make_rsrc(Kh + (int64_t)j0 * kv_rs, bytes);
     const rsrc_t vr = make_rsrc(Vh + (int64_t)j0 * kv_rs, bytes);
-    tile_issue<kRowInst>(kr, st, wave, roff);
-    tile_issue<kTrInst>(kr, st + C::kKRow, wave, toff);
-    tile_issue<kRowInst>(vr, st + C::kKRow + C::kKTr, wave, roff);
+    tile_issue<kInst>(kr, st, wave, toff);
+    tile_issue<kInst>(vr, st + C::kK, wave, toff);
   };
 
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int r_rd = l32 * RS + 8 * hh;
-  const int t_rd = (4 * hh + (i16 >> 2)) * TS + 16 * (g16 & 1) + 4 * (i16 & 3);
+  // A operands: K / V row 16 kb + c at column 32 k4 + 8 g (16-byte reads);
+  // K^T for the dQ product by transpose reads: lane c of group g addresses
+  // K row 4 g + c / 4 (+ 16) at column 4 (c % 4) of a 16-column block and
+  // receives 4 consecutive keys at column c.
+  const int r_rd = c * RS + 8 * g;
+  const int t_rd = (4 * g + (c >> 2)) * RS + 4 * (c & 3);
 
-  f32x16_t acc[NDB];
+  f32x4_t acc[2][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4_t{};
 
   if constexpr (SPARSE) {
     if (nt > 0) sp_cur = sparse_next();
@@ -302,38 +341,33 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       if constexpr (SPARSE) jn = sp_cur = sparse_next();
       issue_tile(jn, smem + ((t + 1) & 1) * C::kStage);
     }
-    const uint16_t* st = smem + (t & 1) * C::kStage;
-    const uint16_t* krow = st;
-    const uint16_t* ktr = st + C::kKRow;
-    const uint16_t* vrow = st + C::kKRow + C::kKTr;
+    const uint16_t* kt = smem + (t & 1) * C::kStage;
+    const uint16_t* vt = kt + C::kK;
 
     if (j0 < w_end && (!MODS || j0 + BN > w_begin)) {
-      f32x16_t s[NKB], dp[NKB];
+      f32x4_t s[2][2], dp[2][2];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = dp[kb] = f32x16_t{};
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[qb][kb] = dp[qb][kb] = f32x4_t{};
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int k4 = 0; k4 < NK4; ++k4) {
+        u32x4_t ak[2], av[2];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const int a_off = r_rd + kb * 32 * RS + 16 * ks;
-          s[kb] = mfma_32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(krow + a_off), qf[ks], s[kb]);
-          dp[kb] = mfma_32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(vrow + a_off), df[ks], dp[kb]);
+        for (int kb = 0; kb < 2; ++kb) {
+          ak[kb] = *reinterpret_cast<const u32x4_t*>(kt + r_rd + kb * 16 * RS + 32 * k4);
+          av[kb] = *reinterpret_cast<const u32x4_t*>(vt + r_rd + kb * 16 * RS + 32 * k4);
         }
-      }
-      if constexpr (D >= 256) {
-        // d = 256 runs one wave per SIMD, so no other wave covers the LDS
-        // latency: the K and V operand reads run three k-steps ahead of the
-        // MFMAs, the K^T reads of the dQ product four MFMAs ahead.  (The
-        // dK/dV kernel already holds 512 registers; there the same pattern
-        // spills.)
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        // each Q^T (dO^T) operand feeds two consecutive MFMAs
 #pragma unroll
-        for (int i = 0; i < NKS - 3; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) s[qb][kb] = mfma_16x16x32<BF16>(ak[kb], qf[qb][k4], s[qb][kb]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) dp[qb][kb] = mfma_16x16x32<BF16>(av[kb], df[qb][k4], dp[qb][kb]);
       }
       __builtin_amdgcn_s_setprio(0);
       // dS^T = P^T (dP^T - D), P^T = 2^(s c - lse2); keys past the end and
@@ -346,39 +380,42 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         // test distances.
         const bool mmask = need_mask || (mods.left >= 0 && qw0 + 31 + diag - j0 > mods.left) ||
                            (mods.right >= 0 && j0 + BN - 1 - qw0 - diag > mods.right);
-        const int fd = my_q + diag - j0 - 4 * hh;  // distance at kb = r = 0
-        const float fdf = (float)fd;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
+        for (int qb = 0; qb < 2; ++qb) {
+          const int fd = qw0 + 16 * qb + c + diag - j0 - 4 * g;  // distance at kb = r = 0
+          const float fdf = (float)fd;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            // distance as fp32 (exact: far below 2^24)
-            const float d = fdf - (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
-            const float base = kAlibi ? __builtin_fmaf(-slope_l2, __builtin_fabsf(d), -lse2) : -lse2;
-            float p, gd = 1.f;
-            if constexpr (kCap) {
-              const float th =
-                  __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(exp2_fast(s[kb][r] * cap_in) + 1.f), 1.f);
-              gd = __builtin_fmaf(-th, th, 1.f);
-              p = exp2_fast(__builtin_fmaf(th, cap_l2, base));
-            } else {
-              p = exp2_fast(__builtin_fmaf(s[kb][r], sigma_l2, base));
+          for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              // distance as fp32 (exact: far below 2^24)
+              const float d = fdf - (float)(16 * kb + r);
+              const float base = kAlibi ? __builtin_fmaf(-slope_l2, __builtin_fabsf(d), -lse2[qb]) : -lse2[qb];
+              float p, gd = 1.f;
+              if constexpr (kCap) {
+                const float th = __builtin_fmaf(
+                    -2.f, __builtin_amdgcn_rcpf(exp2_fast(s[qb][kb][r] * cap_in) + 1.f), 1.f);
+                gd = __builtin_fmaf(-th, th, 1.f);
+                p = exp2_fast(__builtin_fmaf(th, cap_l2, base));
+              } else {
+                p = exp2_fast(__builtin_fmaf(s[qb][kb][r], sigma_l2, base));
+              }
+              const float tv = p * (dp[qb][kb][r] - Di[qb]);
+              s[qb][kb][r] = kCap ? tv * gd : tv;
             }
-            const float t = p * (dp[kb][r] - Di);
-            s[kb][r] = kCap ? t * gd : t;
           }
-        }
-        if (mmask) {
-          // Element offset o = kb * 32 + 8 (r / 4) + r % 4 is visible iff
-          // fd - o lies in [lo_i, hi_i]; a select, so that an infinite or
-          // NaN value of a hidden element goes away.
-          const int o_lo = fd - hi_i, o_hi = fd - lo_i;
+          if (mmask) {
+            // Element offset o = 16 kb + r is visible iff fd - o lies in
+            // [lo_i, hi_i]; a select, so that an infinite or NaN value of a
+            // hidden element goes away.
+            const int o_lo = fd - hi_i, o_hi = fd - lo_i[qb];
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
+            for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int o = kb * 32 + 8 * (r >> 2) + (r & 3);
-              s[kb][r] = (o >= o_lo && o <= o_hi) ? s[kb][r] : 0.f;
+              for (int r = 0; r < 4; ++r) {
+                const int o = 16 * kb + r;
+                s[qb][kb][r] = (o >= o_lo && o <= o_hi) ? s[qb][kb][r] : 0.f;
+              }
             }
           }
         }
@@ -388,16 +425,19 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         // turns the test into selects that every tile pays for).
         auto p_ds = [&](auto masked) {
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
+          for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              float p = exp2_fast(__builtin_fmaf(s[kb][r], c_log2, -lse2));
-              if constexpr (decltype(masked)::value) {
-                const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const bool vis = j < Nk && (!CAUSAL || j <= my_q + diag);
-                p = vis ? p : 0.f;
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                float p = exp2_fast(__builtin_fmaf(s[qb][kb][r], c_log2, -lse2[qb]));
+                if constexpr (decltype(masked)::value) {
+                  const int j = j0 + 16 * kb + 4 * g + r;
+                  const bool vis = j < Nk && (!CAUSAL || j <= qw0 + 16 * qb + c + diag);
+                  p = vis ? p : 0.f;
+                }
+                s[qb][kb][r] = p * (dp[qb][kb][r] - Di[qb]);
               }
-              s[kb][r] = p * (dp[kb][r] - Di);
             }
           }
         };
@@ -406,29 +446,28 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         else
           p_ds(std::false_type{});
       }
-      // dQ^T += K^T dS^T (same operand mapping as the forward's PV product).
-      __builtin_amdgcn_s_setprio(1);
+      // dQ^T += K^T dS^T: lane group g feeds the keys {4 g .. 4 g + 3,
+      // 16 + 4 g .. 16 + 4 g + 3}, the registers of dS^T blocks kb = 0, 1;
+      // each K^T operand feeds two consecutive MFMAs (the two row blocks).
+      u32x4_t b[2];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
+      for (int qb = 0; qb < 2; ++qb) {
         f32x8_t pv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = s[kk >> 1][8 * (kk & 1) + e];
-        const u32x4_t b = pack8<BF16>(pv);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const u32x2_t x0 = lds_read_tr4(ktr + t_rd + 16 * kk * TS + 32 * db);
-          const u32x2_t x1 = lds_read_tr4(ktr + t_rd + (16 * kk + 8) * TS + 32 * db);
-          acc[db] = mfma_32x32x16<BF16>(u32x4_t{x0[0], x0[1], x1[0], x1[1]}, b, acc[db]);
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = s[qb][0][e];
+          pv[4 + e] = s[qb][1][e];
         }
+        b[qb] = pack8<BF16>(pv);
       }
-      if constexpr (D >= 256) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int i = 0; i < NKK * NDB - 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      for (int db = 0; db < NDB; ++db) {
+        const u32x2_t x0 = lds_read_tr4(kt + t_rd + 16 * db);
+        const u32x2_t x1 = lds_read_tr4(kt + t_rd + 16 * RS + 16 * db);
+        const u32x4_t a = {x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) acc[qb][db] = mfma_16x16x32<BF16>(a, b[qb], acc[qb][db]);
       }
       __builtin_amdgcn_s_setprio(0);
     }
@@ -438,16 +477,11 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
   // dQ = scale * acc, rounded; rows >= Nq fall outside the store range.
   const rsrc_t dqr = make_rsrc(dQ + qo_off, rspan);
-  const int ovoff = (int)(l32 * q_rs * 2) + 8 * hh;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
+  for (int qb = 0; qb < 2; ++qb) {
+    const int ovoff = (int)((16 * qb + c) * q_rs * 2) + 8 * g;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4_t o4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = acc[db][4 * g + e] * scale;
-      buf_store8(pack4<BF16>(o4), dqr, ovoff + 2 * (32 * db + 8 * g));
-    }
+    for (int db = 0; db < NDB; ++db) buf_store8(pack4<BF16>(acc[qb][db] * scale), dqr, ovoff + 32 * db);
   }
 }
 
