@@ -28,14 +28,18 @@
 //    its rows and stores it (the dK/dV kernel reads it).
 //  * attn_bwd_dkdv_kernel: one workgroup per 128 keys of one (b, KV head),
 //    4 waves x 32 keys, looping over the query heads of the GQA group and
-//    their query tiles.  The roles of queries and keys are swapped relative
-//    to the dQ kernel:
+//    their query tiles of 32 rows.  The roles of queries and keys are
+//    swapped relative to the dQ kernel; on v_mfma_f32_16x16x32:
 //        S    = Q K^T    (A = Q rows from LDS, B = K^T in VGPRs)
 //        dP   = dO V^T   (A = dO rows from LDS, B = V^T in VGPRs)
-//        dV^T += dO^T P  (A = dO^T by LDS transpose reads, B = P packed)
-//        dK^T += Q^T dS  (A = Q^T by LDS transpose reads, B = dS packed)
-//    Each lane owns one key; lse and D of the tile's query rows come from
-//    LDS.  The GQA group's sum happens in registers.
+//        dV^T += dO^T P  (A = dO^T by LDS transpose reads of the same dO
+//                         tile, B = P packed from the accumulators)
+//        dK^T += Q^T dS  (A = Q^T likewise from the Q tile, B = dS packed)
+//    Each lane owns two keys (shared by its four lane groups); lse and D of
+//    the tile's query rows come from LDS.  The GQA group's sum happens in
+//    registers.  At d = 128 the score-variant and block-sparse instances
+//    keep V^T (with ALiBi also the last K^T k-step) in LDS rather than in
+//    registers.
 // P is rounded to the element type for the dV product and dS for the dQ and
 // dK products (fp32 accumulation throughout).
 #pragma once
@@ -53,24 +57,6 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // kModsAlibi select the softcap and the ALiBi bias at compile time, so that
 // each instance carries only the per-element work it needs.
 constexpr int kModsOn = 1, kModsCap = 2, kModsAlibi = 4;
-
-// LDS row strides (16-byte chunks per row): "row" tiles feed ds_read_b128
-// operand reads (odd multiple of 4 dwords), "tr" tiles feed the transpose
-// reads (odd multiple of 16 dwords); see the forward kernel's tile notes.
-template <int D>
-struct BwdLayout {
-  static constexpr int kChunks = D / 8;
-  static constexpr int RCP = kChunks + 1;  // row tiles
-  static constexpr int TCP = kChunks + 4;  // transpose-read tiles
-  static constexpr int RS = 8 * RCP;       // row stride, elements
-  static constexpr int TS = 8 * TCP;
-  static_assert((RS / 2) % 8 == 4 && (TS / 2) % 32 == 16, "bank-conflict-free strides");
-  // Elements of an R-row tile filled by 64-lane direct loads.
-  template <int R>
-  static constexpr int row_elems() { return ((R * RCP + 63) / 64) * 512; }
-  template <int R>
-  static constexpr int tr_elems() { return ((R * TCP + 63) / 64) * 512; }
-};
 
 // Tiles read by the 16x16x32 products both as rows (16-byte reads, 16 rows
 // x 64 bytes per read) and through transpose reads (16 rows x 32 bytes):
@@ -105,11 +91,10 @@ template <int D>
 struct DkvCfg {
   static constexpr int kWaves = 4, kThreads = 256, BK = 128;
   static constexpr int BQ = 32;  // query rows per tile (two workgroups per CU at d <= 128)
-  using L = BwdLayout<D>;
-  static constexpr int kRow = L::template row_elems<BQ>();
-  static constexpr int kTr = L::template tr_elems<BQ>();
+  using L = Bwd16Layout<D>;
+  static constexpr int kTile = L::template elems<BQ>();  // Q or dO: rows for S / dP, transposed for dK / dV
   static constexpr int kVec = 512;  // 1 KB: lse or D of the tile (64 lanes x 16 B)
-  static constexpr int kStage = 2 * kRow + 2 * kTr + 2 * kVec;
+  static constexpr int kStage = 2 * kTile + 2 * kVec;
   static constexpr int kLdsElems = 2 * kStage;
   static constexpr int kMinWavesPerEU = (D >= 256) ? 1 : 2;
   static_assert(BQ * 4 <= kVec * 2, "lse/D slots cover the tile");
@@ -516,21 +501,38 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   using C = DkvCfg<D>;
   static_assert(kMaskBlock == C::BK && kMaskBlock % C::BQ == 0, "a mask block is whole tiles");
   using L = typename C::L;
-  constexpr int BQ = C::BQ, BK = C::BK, RS = L::RS, TS = L::TS;
-  constexpr int NKS = D / 16, NQB = BQ / 32, NDB = D / 32, NKK = BQ / 16;
-  constexpr int kRowInst = C::kRow / 512, kTrInst = C::kTr / 512;
-  constexpr int kRowPW = (kRowInst + 3) / 4, kTrPW = (kTrInst + 3) / 4;
+  constexpr int BQ = C::BQ, BK = C::BK, RS = L::RS;
+  constexpr int NK4 = D / 32;  // 32-wide k-steps of S and dP
+  constexpr int NDB = D / 16;  // 16-dimension blocks of dK^T and dV^T
+  static_assert(BQ == 32, "one 32-row step of the dK / dV products per tile");
+  constexpr int kInst = C::kTile / 512, kPW = (kInst + 3) / 4;
+  // The score-variant and block-sparse instances at d = 128 carry more
+  // per-lane state than the 256 registers of two waves per SIMD leave room
+  // for; there the V^T fragments sit in LDS (one 16-byte slot per lane and
+  // fragment, conflict-free reads) instead of being spilled to scratch, whose
+  // reloads would wait for the next tile's loads.
+  // With the ALiBi bias the last 32 dimensions of K^T go there too.
+  constexpr bool kStashV = (MODS || SPARSE) && D == 128;
+  constexpr int kStashK = (kAlibi && D == 128) ? 1 : 0;  // K^T k-steps, from the last
+  constexpr int kStashWave = 2 * (NK4 + kStashK) * 64 * 8;  // elements per wave
+  constexpr int kStashElems = kStashV ? 4 * kStashWave : 0;
 
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::kLdsElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::kLdsElems + kStashElems];
 
+  // Lane l: group g = l / 16, c = l % 16.  S, dP and dK^T, dV^T are held in
+  // 16 x 16 blocks (v_mfma_f32_16x16x32): block (qb, kb) register r of S is
+  // query row i0 + 16 qb + 4 g + r against key kw0 + 16 kb + c, so each lane
+  // owns the two keys kw0 + c and kw0 + 16 + c (shared by the four lane
+  // groups); dK^T / dV^T block (db, kb) register r is dimension
+  // 16 db + 4 g + r of key kw0 + 16 kb + c.
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int lane = tid & 63, g = lane >> 4, c = lane & 15;
   // (w.hq is the KV head here, w.qblk the key block.)
   const WorkItem w = VARLEN ? map_workgroup_packed(blockIdx.x, nkb, Hkv, va.pairs)
                            : map_key_block(blockIdx.x, total, nkb, Hkv);
   const int G = Hq / Hkv;
-  const int k0 = w.qblk * BK, kw0 = k0 + wave * 32, my_k = kw0 + l32;
+  const int k0 = w.qblk * BK, kw0 = k0 + wave * 32;
   // First rows of this batch entry (or packed sequence) in q-shaped and
   // k-shaped tensors; lse / delta of query head h start at vec_row0(h).
   int64_t q_row0 = (int64_t)w.b * Nq, k_row0 = (int64_t)w.b * Nk;
@@ -552,16 +554,25 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int64_t q_rs = (int64_t)Hq * D, kv_rs = (int64_t)Hkv * D;
   const int64_t kv_off = (k_row0 + kw0) * kv_rs + (int64_t)w.hq * D;
 
-  // K^T and V^T fragments of this wave's 32 keys (B operands).
+  // K^T and V^T fragments of this wave's two key blocks (B operands): key
+  // kw0 + 16 kb + c, dimensions 32 k4 + 8 g .. + 7.
   const int kspan = span_bytes(kw0, 32, Nk, kv_rs, D);
   const rsrc_t kr = make_rsrc(K + kv_off, kspan);
   const rsrc_t vr = make_rsrc(V + kv_off, kspan);
-  const int fvoff = (int)(l32 * kv_rs * 2) + 16 * hh;
-  u32x4_t kf[NKS], vf[NKS];
+  u32x4_t kf[2][NK4], vf[2][NK4];
+  uint16_t* const vstash = smem + C::kLdsElems + wave * kStashWave + 8 * lane;
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    kf[ks] = buf_load16(kr, fvoff + 32 * ks);
-    vf[ks] = buf_load16(vr, fvoff + 32 * ks);
+  for (int kb = 0; kb < 2; ++kb) {
+    const int fvoff = (int)((16 * kb + c) * kv_rs * 2) + 16 * g;
+#pragma unroll
+    for (int k4 = 0; k4 < NK4; ++k4) {
+      kf[kb][k4] = buf_load16(kr, fvoff + 64 * k4);
+      vf[kb][k4] = buf_load16(vr, fvoff + 64 * k4);
+      if constexpr (kStashV) *reinterpret_cast<u32x4_t*>(vstash + 512 * (kb * NK4 + k4)) = vf[kb][k4];
+      if constexpr (kStashK > 0)
+        if (k4 >= NK4 - kStashK)
+          *reinterpret_cast<u32x4_t*>(vstash + 512 * (2 * NK4 + kb * kStashK + k4 - (NK4 - kStashK))) = kf[kb][k4];
+    }
   }
 
   // Query tiles: every query head of the group, query rows from the first
@@ -595,11 +606,11 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const int64_t base = ((int64_t)w.b * bm.heads + hm) * nqbm * bm.nkb + w.qblk;
     return make_rsrc(SPARSE ? bm.mask + base : nullptr, SPARSE && nqbm > 0 ? (nqbm - 1) * bm.nkb + 1 : 0);
   };
-  // flags of query blocks [64 c, 64 c + 64) of head gi, limited to [qb_lo, qb_hi]
-  auto range_word = [&](int gi, int c) -> uint64_t {
-    uint64_t bits = flag_word(column(gi), c, bm.nkb, lane);
-    if (c == c_lo) bits &= ~0ull << (qb_lo % 64);
-    if (c == c_hi && qb_hi % 64 != 63) bits &= (1ull << (qb_hi % 64 + 1)) - 1;
+  // flags of query blocks [64 ch, 64 ch + 64) of head gi, limited to [qb_lo, qb_hi]
+  auto range_word = [&](int gi, int ch) -> uint64_t {
+    uint64_t bits = flag_word(column(gi), ch, bm.nkb, lane);
+    if (ch == c_lo) bits &= ~0ull << (qb_lo % 64);
+    if (ch == c_hi && qb_hi % 64 != 63) bits &= (1ull << (qb_hi % 64 + 1)) - 1;
     return bits;
   };
   int sp_gi = 0, sp_chunk = c_lo, sp_qt = 0, sp_qt_end = 0, sp_h = 0, sp_i0 = 0;
@@ -608,12 +619,12 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     nsteps = 0;
     if (k0 < Nk && nqt > 0) {
       for (int gi = 0; gi < G; ++gi) {
-        for (int c = c_lo; c <= c_hi; ++c) {
-          const uint64_t bits = range_word(gi, c);
-          if (gi == 0 && c == c_lo) sp_bits = bits;
+        for (int ch = c_lo; ch <= c_hi; ++ch) {
+          const uint64_t bits = range_word(gi, ch);
+          if (gi == 0 && ch == c_lo) sp_bits = bits;
           nsteps += TPQ * __builtin_popcountll(bits);
-          if (qb_lo / 64 == c && ((bits >> (qb_lo % 64)) & 1)) nsteps -= qt_begin - TPQ * qb_lo;
-          if (qb_hi / 64 == c && ((bits >> (qb_hi % 64)) & 1)) nsteps -= TPQ * qb_hi + TPQ - nqt_all;
+          if (qb_lo / 64 == ch && ((bits >> (qb_lo % 64)) & 1)) nsteps -= qt_begin - TPQ * qb_lo;
+          if (qb_hi / 64 == ch && ((bits >> (qb_hi % 64)) & 1)) nsteps -= TPQ * qb_hi + TPQ - nqt_all;
         }
       }
     }
@@ -628,10 +639,10 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         }
         sp_bits = range_word(sp_gi, sp_chunk);
       }
-      const int qb = 64 * sp_chunk + (sp_bits ? __builtin_ctzll(sp_bits) : qb_lo % 64);
+      const int qbm = 64 * sp_chunk + (sp_bits ? __builtin_ctzll(sp_bits) : qb_lo % 64);
       sp_bits &= sp_bits - 1;
-      sp_qt = max(TPQ * qb, qt_begin);
-      sp_qt_end = min(TPQ * qb + TPQ, nqt_all);
+      sp_qt = max(TPQ * qbm, qt_begin);
+      sp_qt_end = min(TPQ * qbm + TPQ, nqt_all);
     }
     sp_h = w.hq * G + sp_gi;
     sp_i0 = sp_qt * BQ;
@@ -639,19 +650,25 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // First query row this wave's keys see (causal), for skipping whole tiles.
   const int w_first = CAUSAL ? kw0 - diag : -(1 << 30);
   // Score variants in log2 units (as in the dQ kernel), and the distances
-  // dist = i + diag - my_k this key sees as one interval [vis_lo, vis_hi]
-  // (rows past the end, causal, window; none for keys past the end).
+  // dist = i + diag - j each of this lane's keys sees as one interval
+  // [lo_i, hi_i[kb]] (rows past the end, causal, window; none for keys past
+  // the end).
   const float sigma_l2 = mods.sigma * kLog2e, cap_l2 = mods.cap * kLog2e;
   const float cap_in = kCap ? mods.sigma * __builtin_amdgcn_rcpf(mods.cap) * (2.0f * kLog2e) : 0.f;
-  int lo_i = CAUSAL ? 0 : -(1 << 29), hi_i = Nk - my_k - 1;
+  int lo_i = CAUSAL ? 0 : -(1 << 29), hi_i[2];
   if (MODS && mods.right >= 0) lo_i = max(lo_i, -mods.right);
-  if (MODS && mods.left >= 0) hi_i = min(hi_i, mods.left);
-  if (my_k >= Nk) hi_i = -(1 << 30);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int j = kw0 + 16 * kb + c;
+    hi_i[kb] = Nk - j - 1;
+    if (MODS && mods.left >= 0) hi_i[kb] = min(hi_i[kb], mods.left);
+    if (j >= Nk) hi_i[kb] = -(1 << 30);
+  }
   const bool w_live = kw0 < Nk;
 
-  int roff[kRowPW], toff[kTrPW];
-  tile_offsets<BQ, L::RCP, D>(wave, lane, q_rs, roff);
-  tile_offsets<BQ, L::TCP, D>(wave, lane, q_rs, toff);
+  // Q and dO tiles, one padded row-major copy each, then lse and D.
+  int toff[kPW];
+  tile_offsets<BQ, L::CP, D>(wave, lane, q_rs, toff);
   // Step s: query head hq = hkv*G + s / nqt, query tile qt_begin + s % nqt.
   auto step_rows = [&](int s) { return (qt_begin + s % nqt) * BQ; };
   auto issue_step = [&](int s, uint16_t* st) {
@@ -659,27 +676,28 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const int i0 = SPARSE ? sp_i0 : step_rows(s);
     const int64_t off = (q_row0 + i0) * q_rs + (int64_t)h * D;
     const int bytes = span_bytes(i0, BQ, Nq, q_rs, D);
-    const rsrc_t qs = make_rsrc(Q + off, bytes);
-    const rsrc_t ds = make_rsrc(dO + off, bytes);
-    tile_issue<kRowInst>(qs, st, wave, roff);
-    tile_issue<kRowInst>(ds, st + C::kRow, wave, roff);
-    tile_issue<kTrInst>(qs, st + 2 * C::kRow, wave, toff);
-    tile_issue<kTrInst>(ds, st + 2 * C::kRow + C::kTr, wave, toff);
+    tile_issue<kInst>(make_rsrc(Q + off, bytes), st, wave, toff);
+    tile_issue<kInst>(make_rsrc(dO + off, bytes), st + C::kTile, wave, toff);
     if (wave == 0) {
       const int64_t voff = vec_row0(h) + i0;
       const int vb = max(0, min(BQ, Nq - i0)) * 4;
-      buf_load_lds16(make_rsrc(LSE + voff, vb), st + 2 * C::kRow + 2 * C::kTr, 16 * lane);
-      buf_load_lds16(make_rsrc(Dlt + voff, vb), st + 2 * C::kRow + 2 * C::kTr + C::kVec, 16 * lane);
+      buf_load_lds16(make_rsrc(LSE + voff, vb), st + 2 * C::kTile, 16 * lane);
+      buf_load_lds16(make_rsrc(Dlt + voff, vb), st + 2 * C::kTile + C::kVec, 16 * lane);
     }
   };
 
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int r_rd = l32 * RS + 8 * hh;
-  const int t_rd = (4 * hh + (i16 >> 2)) * TS + 16 * (g16 & 1) + 4 * (i16 & 3);
+  // A operands: Q / dO row 16 qb + c at column 32 k4 + 8 g (16-byte reads);
+  // Q^T and dO^T for the dK / dV products by transpose reads: lane c of
+  // group g addresses row 4 g + c / 4 (+ 16) at column 4 (c % 4) of a
+  // 16-column block and receives 4 consecutive rows at column c.
+  const int r_rd = c * RS + 8 * g;
+  const int t_rd = (4 * g + (c >> 2)) * RS + 4 * (c & 3);
 
-  f32x16_t dk[NDB], dv[NDB];
+  f32x4_t dk[NDB][2], dv[NDB][2];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16_t{};
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) dk[db][kb] = dv[db][kb] = f32x4_t{};
 
   if constexpr (SPARSE) {
     if (nsteps > 0) sparse_next();
@@ -697,11 +715,9 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       issue_step(s + 1, smem + ((s + 1) & 1) * C::kStage);
     }
     const uint16_t* st = smem + (s & 1) * C::kStage;
-    const uint16_t* qrow = st;
-    const uint16_t* drow = st + C::kRow;
-    const uint16_t* qtr = st + 2 * C::kRow;
-    const uint16_t* dtr = st + 2 * C::kRow + C::kTr;
-    const float* lse_t = reinterpret_cast<const float*>(st + 2 * C::kRow + 2 * C::kTr);
+    const uint16_t* qt = st;
+    const uint16_t* dt = st + C::kTile;
+    const float* lse_t = reinterpret_cast<const float*>(st + 2 * C::kTile);
     const float* dlt_t = lse_t + C::kVec / 2;
     const int i0 = cur_i0;
 
@@ -711,189 +727,169 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       if (mods.left >= 0 && kw0 + 31 < i0 + diag - mods.left) in_window = false;
     }
     if (w_live && i0 + BQ - 1 >= w_first && in_window) {  // wave-uniform: some pair visible
-      f32x16_t sc[NQB], dp[NQB];
+      f32x4_t sc[2][2], dp[2][2];
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) sc[qb] = dp[qb] = f32x16_t{};
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sc[qb][kb] = dp[qb][kb] = f32x4_t{};
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int k4 = 0; k4 < NK4; ++k4) {
+        u32x4_t aq[2], ad[2];
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          const int a_off = r_rd + qb * 32 * RS + 16 * ks;
-          sc[qb] = mfma_32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(qrow + a_off), kf[ks], sc[qb]);
-          dp[qb] = mfma_32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(drow + a_off), vf[ks], dp[qb]);
+        for (int qb = 0; qb < 2; ++qb) {
+          aq[qb] = *reinterpret_cast<const u32x4_t*>(qt + r_rd + qb * 16 * RS + 32 * k4);
+          ad[qb] = *reinterpret_cast<const u32x4_t*>(dt + r_rd + qb * 16 * RS + 32 * k4);
+        }
+        // each K^T (V^T) operand feeds two consecutive MFMAs
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4_t bk =
+              k4 >= NK4 - kStashK
+                  ? *reinterpret_cast<const u32x4_t*>(vstash + 512 * (2 * NK4 + kb * kStashK + k4 - (NK4 - kStashK)))
+                  : kf[kb][k4];
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) sc[qb][kb] = mfma_16x16x32<BF16>(aq[qb], bk, sc[qb][kb]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4_t bv = kStashV ? *reinterpret_cast<const u32x4_t*>(vstash + 512 * (kb * NK4 + k4)) : vf[kb][k4];
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) dp[qb][kb] = mfma_16x16x32<BF16>(ad[qb], bv, dp[qb][kb]);
         }
       }
       __builtin_amdgcn_s_setprio(0);
       // P = 2^(s c - lse2) and dS = P (dP - D) for the rows this lane's
-      // registers hold: row 32 qb + 8 (r / 4) + 4 hh + r % 4.  Rows past Nq
-      // read zero Q and dO rows and lse = D = 0: their P is 1 and their dS
-      // 0, and they add nothing to dV^T (dO rows zero) or dK^T (Q rows
-      // zero); keys past Nk are never stored.  So only causal tiles that
-      // cross the diagonal need masking (the score variants test their
-      // window and ragged ends below).
+      // registers hold: row i0 + 16 qb + 4 g + r.  Rows past Nq read zero Q
+      // and dO rows and lse = D = 0: their P is 1 and their dS 0, and they
+      // add nothing to dV^T (dO rows zero) or dK^T (Q rows zero); keys past
+      // Nk are never stored.  So only causal tiles that cross the diagonal
+      // need masking (the score variants test their window and ragged ends
+      // below).
       const bool need_mask = MODS ? (i0 + BQ > Nq) || (CAUSAL && i0 + diag < kw0 + 31)
                                   : (CAUSAL && i0 + diag < kw0 + 31);
-      // Causal and block-sparse instances mask in a pass of their own after
-      // P and dS, the others per element: at d = 128 each form spills fewer
-      // registers in the instances that use it.
-      constexpr bool kMaskPass = CAUSAL || SPARSE;
+      // dV^T += dO^T P and dK^T += Q^T dS take P and dS of key block kb as
+      // one packed operand each: query rows {4 g .. 4 g + 3} (block qb = 0)
+      // then {16 + 4 g .. 16 + 4 g + 3} (qb = 1).
+      u32x4_t pb[2], sb[2];
+      auto pack_kb = [&](int kb) {
+        f32x8_t pv, sv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = sc[0][kb][e];
+          pv[4 + e] = sc[1][kb][e];
+          sv[e] = dp[0][kb][e];
+          sv[4 + e] = dp[1][kb][e];
+        }
+        pb[kb] = pack8<BF16>(pv);
+        sb[kb] = pack8<BF16>(sv);
+      };
       if constexpr (MODS) {
-        // The score variants, as in the dQ kernel; row
-        // i = i0 + 32 qb + 8 g + 4 hh + e.
+        // The score variants, as in the dQ kernel; distance
+        // d = i + diag - j = fd[kb] + 16 qb + r.  One key block at a time,
+        // packed before the next starts, so that the softcap's temporaries
+        // of both blocks are never live together.
         const bool mmask = need_mask || (mods.left >= 0 && i0 + BQ - 1 + diag - kw0 > mods.left) ||
                            (mods.right >= 0 && kw0 + 31 - i0 - diag > mods.right);
-        const int fd = i0 + diag - my_k + 4 * hh;  // distance at qb = g = e = 0
-        const float fdf = (float)fd;
         const float slope_l2 = slope * kLog2e;
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
+        for (int kb = 0; kb < 2; ++kb) {
+          const int fd = i0 + 4 * g + diag - (kw0 + 16 * kb + c);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int row0 = 32 * qb + 8 * g + 4 * hh;
-            const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse_t + row0);
-            const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dlt_t + row0);
+          for (int qb = 0; qb < 2; ++qb) {
+            const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse_t + 16 * qb + 4 * g);
+            const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dlt_t + 16 * qb + 4 * g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
-              const float d = fdf + (float)(32 * qb + 8 * g + e);  // exact in fp32
-              const float nl = l4[e] * -kLog2e;
+            for (int r = 0; r < 4; ++r) {
+              const float d = (float)fd + (float)(16 * qb + r);  // exact in fp32
+              const float nl = l4[r] * -kLog2e;
               const float base = kAlibi ? __builtin_fmaf(-slope_l2, __builtin_fabsf(d), nl) : nl;
               float p, gd = 1.f;
               if constexpr (kCap) {
-                const float th =
-                    __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(exp2_fast(sc[qb][r] * cap_in) + 1.f), 1.f);
+                const float th = __builtin_fmaf(
+                    -2.f, __builtin_amdgcn_rcpf(exp2_fast(sc[qb][kb][r] * cap_in) + 1.f), 1.f);
                 gd = __builtin_fmaf(-th, th, 1.f);
                 p = exp2_fast(__builtin_fmaf(th, cap_l2, base));
               } else {
-                p = exp2_fast(__builtin_fmaf(sc[qb][r], sigma_l2, base));
+                p = exp2_fast(__builtin_fmaf(sc[qb][kb][r], sigma_l2, base));
               }
-              sc[qb][r] = p;
-              const float t = p * (dp[qb][r] - d4[e]);
-              dp[qb][r] = kCap ? t * gd : t;
+              sc[qb][kb][r] = p;
+              const float tv = p * (dp[qb][kb][r] - d4[r]);
+              dp[qb][kb][r] = kCap ? tv * gd : tv;
             }
           }
-        }
-        if (mmask) {
-          // Row offset o = 32 qb + 8 g + e is visible iff fd + o lies in
-          // [lo_i, hi_i] (selects, as in the dQ kernel).
-          const int o_lo = lo_i - fd, o_hi = hi_i - fd;
+          if (mmask) {
+            // Row offset o = 16 qb + r is visible iff fd + o lies in
+            // [lo_i, hi_i[kb]] (selects, as in the dQ kernel).
+            const int o_lo = lo_i - fd, o_hi = hi_i[kb] - fd;
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
+            for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int o = 32 * qb + 8 * (r >> 2) + (r & 3);
-              const bool vis = o >= o_lo && o <= o_hi;
-              sc[qb][r] = vis ? sc[qb][r] : 0.f;
-              dp[qb][r] = vis ? dp[qb][r] : 0.f;
+              for (int r = 0; r < 4; ++r) {
+                const int o = 16 * qb + r;
+                const bool vis = o >= o_lo && o <= o_hi;
+                sc[qb][kb][r] = vis ? sc[qb][kb][r] : 0.f;
+                dp[qb][kb][r] = vis ? dp[qb][kb][r] : 0.f;
+              }
             }
           }
+          pack_kb(kb);
+          __builtin_amdgcn_sched_barrier(0);
         }
       } else {
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
+        for (int qb = 0; qb < 2; ++qb) {
+          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse_t + 16 * qb + 4 * g);
+          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dlt_t + 16 * qb + 4 * g);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int row0 = 32 * qb + 8 * g + 4 * hh;
-          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse_t + row0);
-          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dlt_t + row0);
+          for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float p = exp2_fast(__builtin_fmaf(sc[qb][r], c_log2, -l4[e] * kLog2e));
-            if (!kMaskPass && need_mask) {
-              const int i = i0 + row0 + e;
-              const bool vis = i < Nq && my_k < Nk && (!CAUSAL || my_k <= i + diag);
-              p = vis ? p : 0.f;
+            for (int r = 0; r < 4; ++r) {
+              const float p = exp2_fast(__builtin_fmaf(sc[qb][kb][r], c_log2, -l4[r] * kLog2e));
+              sc[qb][kb][r] = p;
+              dp[qb][kb][r] = p * (dp[qb][kb][r] - d4[r]);
             }
-            sc[qb][r] = p;
-            dp[qb][r] = p * (dp[qb][r] - d4[e]);
           }
         }
-      }
-      if (kMaskPass && need_mask) {
-        // Row i = i0 + 4 hh + o, o = 32 qb + 8 (r / 4) + r % 4, is visible
-        // iff i < Nq and (causal) my_k <= i + diag: o in [o_lo, o_hi].
-        // Selects, so that an infinite P of a hidden pair goes away.
-        const int o_lo = CAUSAL ? my_k - diag - i0 - 4 * hh : -(1 << 30);
-        const int o_hi = my_k < Nk ? Nq - i0 - 4 * hh - 1 : -(1 << 30) - 1;
+        if (need_mask) {
+          // Row i = i0 + 4 g + o, o = 16 qb + r, is visible to key j iff
+          // i < Nq and (causal) j <= i + diag: o in [o_lo[kb], o_hi[kb]].
+          // Selects, so that an infinite P of a hidden pair goes away.
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
+          for (int kb = 0; kb < 2; ++kb) {
+            const int j = kw0 + 16 * kb + c;
+            const int o_lo = CAUSAL ? j - diag - i0 - 4 * g : -(1 << 30);
+            const int o_hi = j < Nk ? Nq - i0 - 4 * g - 1 : -(1 << 30) - 1;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int o = 32 * qb + 8 * (r >> 2) + (r & 3);
-            const bool vis = o >= o_lo && o <= o_hi;
-            sc[qb][r] = vis ? sc[qb][r] : 0.f;
-            dp[qb][r] = vis ? dp[qb][r] : 0.f;
+            for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int o = 16 * qb + r;
+                const bool vis = o >= o_lo && o <= o_hi;
+                sc[qb][kb][r] = vis ? sc[qb][kb][r] : 0.f;
+                dp[qb][kb][r] = vis ? dp[qb][kb][r] : 0.f;
+              }
+            }
           }
         }
-      }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS (the forward's PV operand
-      // mapping).  At d <= 128 (two waves per SIMD, 256 registers each) P
-      // and dS are packed first and the transposed operands read one step
-      // ahead, each step fenced, so that at most four of them occupy
-      // registers; at d = 256 the compiler schedules the loop.
-      if constexpr (D <= 128) {
-      u32x4_t pbs[NKK], sbs[NKK];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        f32x8_t pv, sv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = sc[kk >> 1][8 * (kk & 1) + e];
-          sv[e] = dp[kk >> 1][8 * (kk & 1) + e];
-        }
-        pbs[kk] = pack8<BF16>(pv);
-        sbs[kk] = pack8<BF16>(sv);
+        for (int kb = 0; kb < 2; ++kb) pack_kb(kb);
       }
-      // operand reads one step (two MFMAs) ahead, each step fenced: at most
-      // four transposed operands in registers
-      constexpr int NM = NKK * NDB;
-      auto rd_pair = [&](int i, const uint16_t* base) {
-        const int kk = i / NDB, db = i % NDB;
-        const int o0 = t_rd + 16 * kk * TS + 32 * db, o1 = t_rd + (16 * kk + 8) * TS + 32 * db;
-        const u32x2_t a0 = lds_read_tr4(base + o0), a1 = lds_read_tr4(base + o1);
-        return u32x4_t{a0[0], a0[1], a1[0], a1[1]};
-      };
-      u32x4_t va[2], qa[2];
-      va[0] = rd_pair(0, dtr);
-      qa[0] = rd_pair(0, qtr);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        if (i + 1 < NM) {
-          va[(i + 1) & 1] = rd_pair(i + 1, dtr);
-          qa[(i + 1) & 1] = rd_pair(i + 1, qtr);
-        }
-        const int kk = i / NDB, db = i % NDB;
-        dv[db] = mfma_32x32x16<BF16>(va[i & 1], pbs[kk], dv[db]);
-        dk[db] = mfma_32x32x16<BF16>(qa[i & 1], sbs[kk], dk[db]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int db = 0; db < NDB; ++db) {
+        const u32x2_t a0 = lds_read_tr4(dt + t_rd + 16 * db);
+        const u32x2_t a1 = lds_read_tr4(dt + t_rd + 16 * RS + 16 * db);
+        const u32x4_t av = {a0[0], a0[1], a1[0], a1[1]};
+        const u32x2_t b0 = lds_read_tr4(qt + t_rd + 16 * db);
+        const u32x2_t b1 = lds_read_tr4(qt + t_rd + 16 * RS + 16 * db);
+        const u32x4_t aq = {b0[0], b0[1], b1[0], b1[1]};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) dv[db][kb] = mfma_16x16x32<BF16>(av, pb[kb], dv[db][kb]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) dk[db][kb] = mfma_16x16x32<BF16>(aq, sb[kb], dk[db][kb]);
       }
       __builtin_amdgcn_s_setprio(0);
-      } else {
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        f32x8_t pv, sv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = sc[kk >> 1][8 * (kk & 1) + e];
-          sv[e] = dp[kk >> 1][8 * (kk & 1) + e];
-        }
-        const u32x4_t pb = pack8<BF16>(pv), sb = pack8<BF16>(sv);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int o0 = t_rd + 16 * kk * TS + 32 * db, o1 = t_rd + (16 * kk + 8) * TS + 32 * db;
-          const u32x2_t a0 = lds_read_tr4(dtr + o0), a1 = lds_read_tr4(dtr + o1);
-          dv[db] = mfma_32x32x16<BF16>(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, pb, dv[db]);
-          const u32x2_t b0 = lds_read_tr4(qtr + o0), b1 = lds_read_tr4(qtr + o1);
-          dk[db] = mfma_32x32x16<BF16>(u32x4_t{b0[0], b0[1], b1[0], b1[1]}, sb, dk[db]);
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -902,19 +898,13 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // dK = scale * dK^T, dV = dV^T, rounded; keys >= Nk fall outside the range.
   const rsrc_t dkr = make_rsrc(dK + kv_off, kspan);
   const rsrc_t dvr = make_rsrc(dV + kv_off, kspan);
-  const int ovoff = (int)(l32 * kv_rs * 2) + 8 * hh;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
+  for (int kb = 0; kb < 2; ++kb) {
+    const int ovoff = (int)((16 * kb + c) * kv_rs * 2) + 8 * g;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4_t k4, v4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        k4[e] = dk[db][4 * g + e] * scale;
-        v4[e] = dv[db][4 * g + e];
-      }
-      buf_store8(pack4<BF16>(k4), dkr, ovoff + 2 * (32 * db + 8 * g));
-      buf_store8(pack4<BF16>(v4), dvr, ovoff + 2 * (32 * db + 8 * g));
+    for (int db = 0; db < NDB; ++db) {
+      buf_store8(pack4<BF16>(dk[db][kb] * scale), dkr, ovoff + 32 * db);
+      buf_store8(pack4<BF16>(dv[db][kb]), dvr, ovoff + 32 * db);
     }
   }
 }
