@@ -68,14 +68,26 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, i
     }
   }
   // d = 128 without score variants (plain, packed sequences, block mask):
-  // the same tiling on 16x16x32 matrix instructions.
+  // the same tiling on 16x16x32 matrix instructions; non-causal calls
+  // without a block mask in workgroups of 256 query rows.
   if constexpr (!MODS && D == 128) {
     if (scale > 0.f) {
-      hipLaunchKernelGGL((eta::attn_fwd_k16_kernel<D, BF16, CAUSAL, VARLEN, SPARSE>), dim3(total),
-                         dim3(eta::K16Cfg<D>::kThreads), 0, stream,
-                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                         static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq,
-                         Hkv, Nq, Nk, nqb, total, c_log2, va, bm);
+      if constexpr (!CAUSAL && !SPARSE) {
+        using W = eta::K16Cfg<D, true>;
+        const int nqbw = (Nq + W::BM - 1) / W::BM;
+        const int totalw = (int)((int64_t)B * Hq * nqbw);
+        hipLaunchKernelGGL((eta::attn_fwd_k16_kernel<D, BF16, false, VARLEN, false, true>), dim3(totalw),
+                           dim3(W::kThreads), 0, stream, static_cast<const uint16_t*>(q),
+                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                           static_cast<uint16_t*>(out), lse, Hq, Hkv, Nq, Nk, nqbw, totalw, c_log2, va,
+                           bm);
+      } else {
+        hipLaunchKernelGGL((eta::attn_fwd_k16_kernel<D, BF16, CAUSAL, VARLEN, SPARSE>), dim3(total),
+                           dim3(eta::K16Cfg<D>::kThreads), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq,
+                           Hkv, Nq, Nk, nqb, total, c_log2, va, bm);
+      }
       return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
     }
   }

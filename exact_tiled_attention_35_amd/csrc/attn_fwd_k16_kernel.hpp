@@ -1,14 +1,23 @@
 // Exact tiled attention forward on 16x16x32 matrix instructions (gfx950),
 // head dimension 64 or 128.
 //
-// Same computation, tiling and pipeline as attn_fwd_kernel (softmax(Q K^T *
-// scale) V per (batch, query head), the formula of the interface section of
+// Same computation and pipeline as attn_fwd_kernel (softmax(Q K^T * scale) V
+// per (batch, query head), the formula of the interface section of
 // hysenlabs.com's "FlashAttention: exakte Attention-Kernel fuer CUDA und
-// ROCm"; 128 query rows per workgroup, 32 per wave, 64-key K/V tiles in two
-// LDS stages, lazy rescaling, lean tiles), with the products on
-// v_mfma_f32_16x16x32 instead of v_mfma_f32_32x32x16: the same flops in
-// twice as many instructions of half the size, which the matrix cores of
-// this part run at a higher rate for the same power.
+// ROCm"; 32 query rows per wave, K/V tiles in two LDS stages, lazy
+// rescaling, lean tiles), with the products on v_mfma_f32_16x16x32 instead
+// of v_mfma_f32_32x32x16: the same flops in twice as many instructions of
+// half the size, which the matrix cores of this part run at a higher rate
+// for the same power.  Two shapes of workgroup:
+//  * 4 waves (128 query rows), 64-key tiles, two workgroups per CU: the
+//    causal and block-mask instances (a causal workgroup of 256 rows would
+//    idle more waves on the diagonal tiles; a mask block is 128 rows);
+//  * WIDE: 8 waves (256 query rows), 128-key tiles, one workgroup per CU
+//    (147 KB of LDS): the non-causal batched and packed-sequence instances.
+//    Each K/V tile is fetched from L2 once for twice as many rows, and a
+//    workgroup meets a barrier once per 128 keys instead of 64.  Without a
+//    causal mask a wave's work does not depend on the workgroup's other
+//    rows, so both instances compute a sequence's rows bit for bit alike.
 //
 // Layout (lane l, g = l / 16, c = l % 16):
 //  * S^T = K Q^T in 16 x 16 blocks s[qb][kb]: register r holds key
@@ -42,12 +51,15 @@
 
 namespace eta {
 
-template <int D>
+// WIDE: 8 waves (256 query rows) per workgroup and 128-key tiles, one
+// workgroup per CU; otherwise 4 waves (128 rows) and 64-key tiles, two
+// workgroups per CU.
+template <int D, bool WIDE = false>
 struct K16Cfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = WIDE ? 8 : 4;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int BM = 32 * kWaves;                 // query rows per workgroup
-  static constexpr int BN = 64;                          // keys per K/V tile
+  static constexpr int BN = WIDE ? 128 : 64;             // keys per K/V tile
   static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
   static constexpr int KCP = kChunks + 2;                // K row, in 16-byte slots
   static constexpr int VCP = kChunks + 2;                // V row, in 16-byte slots
@@ -68,18 +80,19 @@ struct K16Cfg {
   // of 4 (mod 8) dwords cost about 4 conflict cycles per K read, and V
   // strides of 4 (mod 8) or 16 (mod 64) dwords 2 per transpose read.
   static_assert((KS / 2) % 16 == 8 && (VS / 2) % 16 == 8, "conflict-free row strides");
-  static_assert(2 * kLdsElems * 2 <= 160 * 1024, "two workgroups per CU");
+  static_assert((WIDE ? 1 : 2) * kLdsElems * 2 <= 160 * 1024, "workgroups per CU");
 };
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN = false, bool SPARSE = false>
-__global__ void __launch_bounds__(K16Cfg<D>::kThreads, 2)
+template <int D, bool BF16, bool CAUSAL, bool VARLEN = false, bool SPARSE = false, bool WIDE = false>
+__global__ void __launch_bounds__((K16Cfg<D, WIDE>::kThreads), 2)
 attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                     float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int nqb, int total,
                     float c_log2, VarlenArgs va, BlockMaskArgs bm) {
-  using C = K16Cfg<D>;
+  using C = K16Cfg<D, WIDE>;
   static_assert(!(SPARSE && VARLEN), "block sparsity is an instance of its own");
-  static_assert(kMaskBlock % C::BN == 0 && kMaskBlock == C::BM, "a mask block is whole tiles");
+  static_assert(!WIDE || !SPARSE, "a mask block is one 128-row workgroup");
+  static_assert(kMaskBlock % C::BN == 0 && (!SPARSE || kMaskBlock == C::BM), "a mask block is whole tiles");
   constexpr int BN = C::BN, BM = C::BM, KS = C::KS, VS = C::VS;
   constexpr int NK4 = D / 32;   // 32-wide k-steps of S^T
   constexpr int NKB = BN / 16;  // 16-key blocks of S^T
@@ -187,7 +200,7 @@ attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   };
 
   // ---- Direct global->LDS tile loads: this wave issues the K (V) tile's
-  // instructions j = wave, wave + 4, ...; lane -> 16-byte slot 64 j + lane ->
+  // instructions j = wave, wave + kWaves, ...; lane -> 16-byte slot 64 j + lane ->
   // (row, chunk) of the padded layout.
   int koff[C::kKInstPerWave], voff[C::kVInstPerWave];
 #pragma unroll
@@ -308,15 +321,20 @@ attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   // kMasked -- tile maximum first, masking where the tile crosses the causal
   // diagonal or the ragged end.
   constexpr int kLean = 0, kFull = 1, kMasked = 2;
-  auto tile = [&](int t, auto mode) {
+  // The stage being filled and the one being read come in as
+  // restrict-qualified parameters: the transpose reads of the current stage
+  // then carry alias information that sets them apart from the next tile's
+  // direct loads, so they need not wait for those loads (without it the
+  // compiler waits for every outstanding direct-to-LDS load before the first
+  // V^T read).  The wait at the end of the tile keeps the order.
+  auto tile_body = [&](int t, auto mode, uint16_t* __restrict__ nxt, const uint16_t* __restrict__ st) {
     constexpr int kMode = decltype(mode)::value;
     const int j0 = SPARSE ? sp_cur : t * BN;
     if (t + 1 < nt) {
       int jn = j0 + BN;
       if constexpr (SPARSE) jn = sp_cur = sparse_next();
-      issue_tile(jn, smem + ((t + 1) & 1) * C::kStage);
+      issue_tile(jn, nxt);
     }
-    const uint16_t* st = smem + (t & 1) * C::kStage;
 
     if (j0 < w_end) {  // wave-uniform: skip tiles above this wave's diagonal
       f32x4_t s[2][NKB];
@@ -406,6 +424,9 @@ attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
 
     __builtin_amdgcn_s_waitcnt(0);  // tile t+1 has landed in LDS
     __syncthreads();
+  };
+  auto tile = [&](int t, auto mode) {
+    tile_body(t, mode, smem + ((t + 1) & 1) * C::kStage, smem + (t & 1) * C::kStage);
   };
   using LeanMode = std::integral_constant<int, kLean>;
   using FullMode = std::integral_constant<int, kFull>;

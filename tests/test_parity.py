@@ -306,10 +306,12 @@ def test_rising_scores_wide_grid(slope, causal):
 
 
 # d = 128 grids of 128 or more row blocks (the 16x16x32 kernel): key and row
-# counts around the 64-key tile and the 16-row halves of a wave's rows, both
-# causal alignments (Nq < Nk, Nq > Nk: rows without keys), GQA and MQA.
+# counts around the 64- and 128-key tiles, the 16-row halves of a wave's rows
+# and the 128- and 256-row workgroups (waves past the last row, several row
+# blocks per head), both causal alignments (Nq < Nk, Nq > Nk: rows without
+# keys), GQA and MQA.
 K16_EDGES = [(16, 1), (17, 63), (33, 64), (48, 65), (100, 100), (129, 127), (200, 96),
-             (64, 1000), (250, 30), (31, 300)]
+             (64, 1000), (250, 30), (31, 300), (257, 129), (300, 385), (520, 255), (256, 128)]
 
 
 @pytest.mark.parametrize("nq_nk", K16_EDGES, ids=lambda c: "N%dx%d" % c)
