@@ -37,9 +37,9 @@
 //        dK^T += Q^T dS  (A = Q^T likewise from the Q tile, B = dS packed)
 //    Each lane owns two keys (shared by its four lane groups); lse and D of
 //    the tile's query rows come from LDS.  The GQA group's sum happens in
-//    registers.  At d = 128 the score-variant and block-sparse instances
-//    keep V^T (with ALiBi also the last K^T k-step) in LDS rather than in
-//    registers.
+//    registers.  At d = 128 the causal, score-variant and block-sparse
+//    instances keep V^T (with ALiBi also the last K^T k-step) in LDS rather
+//    than in registers.
 // P is rounded to the element type for the dV product and dS for the dQ and
 // dK products (fp32 accumulation throughout).
 #pragma once
@@ -506,13 +506,13 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   constexpr int NDB = D / 16;  // 16-dimension blocks of dK^T and dV^T
   static_assert(BQ == 32, "one 32-row step of the dK / dV products per tile");
   constexpr int kInst = C::kTile / 512, kPW = (kInst + 3) / 4;
-  // The score-variant and block-sparse instances at d = 128 carry more
-  // per-lane state than the 256 registers of two waves per SIMD leave room
-  // for; there the V^T fragments sit in LDS (one 16-byte slot per lane and
-  // fragment, conflict-free reads) instead of being spilled to scratch, whose
-  // reloads would wait for the next tile's loads.
-  // With the ALiBi bias the last 32 dimensions of K^T go there too.
-  constexpr bool kStashV = (MODS || SPARSE) && D == 128;
+  // The causal, score-variant and block-sparse instances at d = 128 carry
+  // more per-lane state than the 256 registers of two waves per SIMD leave
+  // room for; there the V^T fragments sit in LDS (one 16-byte slot per lane
+  // and fragment, conflict-free reads) instead of being spilled to scratch,
+  // whose reloads would wait for the next tile's loads.  With the ALiBi bias
+  // the last 32 dimensions of K^T go there too.
+  constexpr bool kStashV = (MODS || SPARSE || CAUSAL) && D == 128;
   constexpr int kStashK = (kAlibi && D == 128) ? 1 : 0;  // K^T k-steps, from the last
   constexpr int kStashWave = 2 * (NK4 + kStashK) * 64 * 8;  // elements per wave
   constexpr int kStashElems = kStashV ? 4 * kStashWave : 0;
