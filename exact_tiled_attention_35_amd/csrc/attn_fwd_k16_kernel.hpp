@@ -37,8 +37,11 @@
 //
 // Plain, packed-sequence (VARLEN) and block-mask (SPARSE) instances, with
 // attn_fwd_kernel's work mapping, row offsets and tile walk for the latter
-// two, so that they compute bit for bit what the batched instance computes
-// on the same rows and tiles; no score variants; scale > 0.
+// two: a packed sequence computes bit for bit what the batched instance
+// computes on the same rows, and an all-ones block mask what the causal
+// batched instance computes (the non-causal batched call walks 128-key
+// tiles, the block-mask instance 64-key ones); no score variants;
+// scale > 0.  The launcher uses the kernel at d = 128.
 #pragma once
 
 #include <hip/hip_runtime.h>
