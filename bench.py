@@ -192,6 +192,13 @@ def host_info(op: str = "fwd") -> dict:
                 rev += "+modified"
     except (OSError, subprocess.SubprocessError):
         pass
+    if rev is None:  # a copy of the tree without .git: the revision the library was built from
+        try:
+            with open(os.path.join(ROOT, "exact_tiled_attention_35_amd", "libattn.build.json")) as f:
+                built = json.load(f).get("git_rev")
+            rev = f"{built} (at build)" if built else None
+        except (OSError, ValueError):
+            pass
     src = op if op in OP_SOURCES else "fwd"
     return {"cores": host_cores(), "rocm": rocm, "hip_runtime": torch.version.hip,
             "torch": torch.__version__, "git_rev": rev,

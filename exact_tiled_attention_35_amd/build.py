@@ -86,7 +86,33 @@ def build_library(verbose: bool = False) -> str:
     if link.returncode != 0:
         raise RuntimeError("link failed:\n" + link.stderr[-4000:])
     os.replace(tmp, LIB_PATH)
+    write_build_info()
     return LIB_PATH
+
+
+BUILD_INFO = os.path.join(PKG, "libattn.build.json")
+
+
+def write_build_info() -> None:
+    """Record, beside the library, the git revision of the tree it was built
+    from (with "+modified" when tracked files differ from it), so that a run
+    on a copy of the tree without its .git can still name the build."""
+    import json
+
+    rev = None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"],
+                           capture_output=True, text=True, timeout=10)
+        if r.returncode == 0:
+            rev = r.stdout.strip()
+            d = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"],
+                               capture_output=True, text=True, timeout=10)
+            if d.returncode == 0 and d.stdout.strip():
+                rev += "+modified"
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(BUILD_INFO, "w") as f:
+        json.dump({"git_rev": rev}, f)
 
 
 if __name__ == "__main__":

@@ -220,3 +220,20 @@ def test_host_info_names_cores_and_versions():
     assert info["cores"] == len(os.sched_getaffinity(0))
     assert info["kernel_source_hash"] == bench.kernel_source_hash("fwd")
     assert "torch" in info and "rocm" in info
+
+
+def test_host_info_names_the_build_on_a_tree_without_git(monkeypatch):
+    # The library's build records the revision it was built from; a copy of
+    # the tree without .git (git fails) reports that one, marked as such.
+    from exact_tiled_attention_35_amd import build as b
+
+    b.write_build_info()
+    with open(b.BUILD_INFO) as f:
+        built = json.load(f)["git_rev"]
+
+    def no_git(*args, **kwargs):
+        raise OSError("no git here")
+
+    monkeypatch.setattr(subprocess, "run", no_git)
+    info = bench.host_info("fwd")
+    assert info["git_rev"] == (f"{built} (at build)" if built else None)
