@@ -43,10 +43,22 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* out, con
                        scale, c_log2, bm, eta::VarlenArgs{nullptr, nullptr, 0, 0, 0}, mods);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
   }
-  hipLaunchKernelGGL((eta::attn_bwd_dkdv_kernel<D, BF16, CAUSAL, SPARSE, false, MK>), dim3((int)tk),
-                     dim3(CK::kThreads), 0, stream, Q, Kp, Vp, dO, lse, delta,
-                     static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), Hq, Hkv, Nq, Nk, nkb,
-                     (int)tk, scale, c_log2, bm, eta::VarlenArgs{nullptr, nullptr, 0, 0, 0}, mods);
+  // The plain non-causal d = 128 dK/dV kernel runs 256 keys (8 waves) per
+  // workgroup.
+  if constexpr (!CAUSAL && !SPARSE && MK == 0 && D == 128) {
+    using CW = eta::DkvCfg<D, true>;
+    const int nkbw = (Nk + CW::BK - 1) / CW::BK;
+    const int tkw = (int)((int64_t)B * Hkv * nkbw);
+    hipLaunchKernelGGL((eta::attn_bwd_dkdv_kernel<D, BF16, false, false, false, 0, true>), dim3(tkw),
+                       dim3(CW::kThreads), 0, stream, Q, Kp, Vp, dO, lse, delta,
+                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), Hq, Hkv, Nq, Nk, nkbw,
+                       tkw, scale, c_log2, bm, eta::VarlenArgs{nullptr, nullptr, 0, 0, 0}, mods);
+  } else {
+    hipLaunchKernelGGL((eta::attn_bwd_dkdv_kernel<D, BF16, CAUSAL, SPARSE, false, MK>), dim3((int)tk),
+                       dim3(CK::kThreads), 0, stream, Q, Kp, Vp, dO, lse, delta,
+                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), Hq, Hkv, Nq, Nk, nkb,
+                       (int)tk, scale, c_log2, bm, eta::VarlenArgs{nullptr, nullptr, 0, 0, 0}, mods);
+  }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

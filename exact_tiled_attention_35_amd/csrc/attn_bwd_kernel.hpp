@@ -27,7 +27,9 @@
 //    lse and D are two per-lane scalars.  The kernel first computes D for
 //    its rows and stores it (the dK/dV kernel reads it).
 //  * attn_bwd_dkdv_kernel: one workgroup per 128 keys of one (b, KV head),
-//    4 waves x 32 keys, looping over the query heads of the GQA group and
+//    4 waves x 32 keys (the plain d = 128 instance: 256 keys, 8 waves, one
+//    workgroup per CU, so that each query tile is fetched from L2 once for
+//    twice as many keys), looping over the query heads of the GQA group and
 //    their query tiles of 32 rows.  The roles of queries and keys are
 //    swapped relative to the dQ kernel; on v_mfma_f32_16x16x32:
 //        S    = Q K^T    (A = Q rows from LDS, B = K^T in VGPRs)
@@ -87,9 +89,11 @@ struct DqCfg {
   static constexpr int kMinWavesPerEU = (D >= 256) ? 1 : 2;
 };
 
-template <int D>
+template <int D, bool WIDE = false>
 struct DkvCfg {
-  static constexpr int kWaves = 4, kThreads = 256, BK = 128;
+  // WIDE: 8 waves (256 keys) per workgroup, one workgroup per CU, so that
+  // each query tile is fetched once for twice as many keys.
+  static constexpr int kWaves = WIDE ? 8 : 4, kThreads = 64 * kWaves, BK = 32 * kWaves;
   static constexpr int BQ = 32;  // query rows per tile (two workgroups per CU at d <= 128)
   using L = Bwd16Layout<D>;
   static constexpr int kTile = L::template elems<BQ>();  // Q or dO: rows for S / dP, transposed for dK / dV
@@ -101,23 +105,23 @@ struct DkvCfg {
 };
 
 // Direct-load slot offsets for an R-row tile with CP chunks per row and a
-// global row stride of rs elements: this wave issues instructions
-// j = wave, wave + 4, ...; lane -> slot 64 j + lane -> (row, chunk).
-template <int R, int CP, int D, int NI>
+// global row stride of rs elements: of the W waves, this one issues
+// instructions j = wave, wave + W, ...; lane -> slot 64 j + lane -> (row, chunk).
+template <int R, int CP, int D, int NI, int W = 4>
 __device__ __forceinline__ void tile_offsets(int wave, int lane, int64_t rs, int (&off)[NI]) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int sl = 64 * (wave + 4 * i) + lane;
+    const int sl = 64 * (wave + W * i) + lane;
     const int row = min(sl / CP, R - 1), c = min(sl % CP, D / 8 - 1);
     off[i] = (int)(row * rs * 2) + 16 * c;
   }
 }
 
-template <int NINST, int NI>
+template <int NINST, int NI, int W = 4>
 __device__ __forceinline__ void tile_issue(rsrc_t r, uint16_t* dst, int wave, const int (&off)[NI]) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int j = wave + 4 * i;
+    const int j = wave + W * i;
     if (j < NINST) buf_load_lds16(r, dst + 512 * j, off[i]);
   }
 }
@@ -487,8 +491,8 @@ __device__ __forceinline__ WorkItem map_key_block(int wg, int total, int nkb, in
   return w;
 }
 
-template <int D, bool BF16, bool CAUSAL, bool SPARSE = false, bool VARLEN = false, int MK = 0>
-__global__ void __launch_bounds__(DkvCfg<D>::kThreads, DkvCfg<D>::kMinWavesPerEU)
+template <int D, bool BF16, bool CAUSAL, bool SPARSE = false, bool VARLEN = false, int MK = 0, bool WIDE = false>
+__global__ void __launch_bounds__((DkvCfg<D, WIDE>::kThreads), (DkvCfg<D, WIDE>::kMinWavesPerEU))
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                      const float* __restrict__ LSE, const float* __restrict__ Dlt,
@@ -498,14 +502,16 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   constexpr bool MODS = MK != 0;
   constexpr bool kCap = (MK & kModsCap) != 0, kAlibi = (MK & kModsAlibi) != 0;
   static_assert((int)SPARSE + (int)VARLEN + (int)MODS <= 1, "one instance per extension");
-  using C = DkvCfg<D>;
-  static_assert(kMaskBlock == C::BK && kMaskBlock % C::BQ == 0, "a mask block is whole tiles");
+  using C = DkvCfg<D, WIDE>;
+  static_assert(!WIDE || (!SPARSE && !VARLEN && !MODS && !CAUSAL), "the wide workgroup serves the plain instance");
+  static_assert((!SPARSE || kMaskBlock == C::BK) && kMaskBlock % C::BQ == 0, "a mask block is whole tiles");
   using L = typename C::L;
   constexpr int BQ = C::BQ, BK = C::BK, RS = L::RS;
   constexpr int NK4 = D / 32;  // 32-wide k-steps of S and dP
   constexpr int NDB = D / 16;  // 16-dimension blocks of dK^T and dV^T
   static_assert(BQ == 32, "one 32-row step of the dK / dV products per tile");
-  constexpr int kInst = C::kTile / 512, kPW = (kInst + 3) / 4;
+  constexpr int W = C::kWaves;
+  constexpr int kInst = C::kTile / 512, kPW = (kInst + W - 1) / W;
   // The causal, score-variant and block-sparse instances at d = 128 carry
   // more per-lane state than the 256 registers of two waves per SIMD leave
   // room for; there the V^T fragments sit in LDS (one 16-byte slot per lane
@@ -515,7 +521,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   constexpr bool kStashV = (MODS || SPARSE || CAUSAL) && D == 128;
   constexpr int kStashK = (kAlibi && D == 128) ? 1 : 0;  // K^T k-steps, from the last
   constexpr int kStashWave = 2 * (NK4 + kStashK) * 64 * 8;  // elements per wave
-  constexpr int kStashElems = kStashV ? 4 * kStashWave : 0;
+  constexpr int kStashElems = kStashV ? W * kStashWave : 0;
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::kLdsElems + kStashElems];
 
@@ -668,7 +674,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
   // Q and dO tiles, one padded row-major copy each, then lse and D.
   int toff[kPW];
-  tile_offsets<BQ, L::CP, D>(wave, lane, q_rs, toff);
+  tile_offsets<BQ, L::CP, D, kPW, W>(wave, lane, q_rs, toff);
   // Step s: query head hq = hkv*G + s / nqt, query tile qt_begin + s % nqt.
   auto step_rows = [&](int s) { return (qt_begin + s % nqt) * BQ; };
   auto issue_step = [&](int s, uint16_t* st) {
@@ -676,8 +682,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const int i0 = SPARSE ? sp_i0 : step_rows(s);
     const int64_t off = (q_row0 + i0) * q_rs + (int64_t)h * D;
     const int bytes = span_bytes(i0, BQ, Nq, q_rs, D);
-    tile_issue<kInst>(make_rsrc(Q + off, bytes), st, wave, toff);
-    tile_issue<kInst>(make_rsrc(dO + off, bytes), st + C::kTile, wave, toff);
+    tile_issue<kInst, kPW, W>(make_rsrc(Q + off, bytes), st, wave, toff);
+    tile_issue<kInst, kPW, W>(make_rsrc(dO + off, bytes), st + C::kTile, wave, toff);
     if (wave == 0) {
       const int64_t voff = vec_row0(h) + i0;
       const int vb = max(0, min(BQ, Nq - i0)) * 4;

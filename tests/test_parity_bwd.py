@@ -106,6 +106,12 @@ SMALL = [  # (B, Hq, Hkv, Nq, Nk, d, dtype, causal)
     (1, 2, 2, 257, 513, 256, "bf16", True),
     (3, 6, 3, 129, 200, 64, "fp16", False),
     (1, 4, 1, 511, 511, 128, "fp16", True),
+    # non-causal d = 128 (the dK/dV kernel's 256-key workgroups): key counts
+    # across and around 256, ragged tails, GQA
+    (1, 4, 2, 300, 257, 128, "bf16", False),
+    (2, 2, 1, 200, 600, 128, "fp16", False),
+    (1, 4, 4, 96, 513, 128, "bf16", False),
+    (1, 2, 2, 33, 256, 128, "bf16", False),
 ]
 
 
