@@ -80,14 +80,25 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, i
                            dim3(W::kThreads), 0, stream, static_cast<const uint16_t*>(q),
                            static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                            static_cast<uint16_t*>(out), lse, Hq, Hkv, Nq, Nk, nqbw, totalw, c_log2, va,
-                           bm);
+                           bm, -1, -1);
       } else {
         hipLaunchKernelGGL((eta::attn_fwd_k16_kernel<D, BF16, CAUSAL, VARLEN, SPARSE>), dim3(total),
                            dim3(eta::K16Cfg<D>::kThreads), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                            static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq,
-                           Hkv, Nq, Nk, nqb, total, c_log2, va, bm);
+                           Hkv, Nq, Nk, nqb, total, c_log2, va, bm, -1, -1);
       }
+      return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    }
+  }
+  // d = 128 with a window alone: the 16x16x32 kernel (128-row workgroups).
+  if constexpr (MODS && !VARLEN && !SPARSE && D == 128) {
+    if (scale > 0.f && !mods.slopes && !(mods.cap > 0.f)) {
+      hipLaunchKernelGGL((eta::attn_fwd_k16_kernel<D, BF16, CAUSAL, false, false, false, true>),
+                         dim3(total), dim3(eta::K16Cfg<D>::kThreads), 0, stream,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq, Hkv, Nq,
+                         Nk, nqb, total, c_log2, va, bm, mods.left, mods.right);
       return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
     }
   }

@@ -40,8 +40,12 @@
 // two: a packed sequence computes bit for bit what the batched instance
 // computes on the same rows, and an all-ones block mask what the causal
 // batched instance computes (the non-causal batched call walks 128-key
-// tiles, the block-mask instance 64-key ones); no score variants;
-// scale > 0.  The launcher uses the kernel at d = 128.
+// tiles, the block-mask instance 64-key ones).  Of the score variants only
+// the sliding window (WIN, 128-row workgroups; attn_fwd_kernel's key range,
+// tile modes and edge masking); scale > 0.  The launcher uses the kernel at
+// d = 128.  The tile lambdas are forced inline: the window instances, with
+// a third tile loop, were otherwise left as calls with the accumulators in
+// scratch.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -86,15 +90,17 @@ struct K16Cfg {
   static_assert((WIDE ? 1 : 2) * kLdsElems * 2 <= 160 * 1024, "workgroups per CU");
 };
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN = false, bool SPARSE = false, bool WIDE = false>
+template <int D, bool BF16, bool CAUSAL, bool VARLEN = false, bool SPARSE = false, bool WIDE = false,
+          bool WIN = false>
 __global__ void __launch_bounds__((K16Cfg<D, WIDE>::kThreads), 2)
 attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                     float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int nqb, int total,
-                    float c_log2, VarlenArgs va, BlockMaskArgs bm) {
+                    float c_log2, VarlenArgs va, BlockMaskArgs bm, int wl, int wr) {
   using C = K16Cfg<D, WIDE>;
   static_assert(!(SPARSE && VARLEN), "block sparsity is an instance of its own");
   static_assert(!WIDE || !SPARSE, "a mask block is one 128-row workgroup");
+  static_assert(!WIN || (!SPARSE && !VARLEN && !WIDE), "the window is an instance of the batched layout");
   static_assert(kMaskBlock % C::BN == 0 && (!SPARSE || kMaskBlock == C::BM), "a mask block is whole tiles");
   constexpr int BN = C::BN, BM = C::BM, KS = C::KS, VS = C::VS;
   constexpr int NK4 = D / 32;   // 32-wide k-steps of S^T
@@ -150,12 +156,39 @@ attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   // visible to every row of the workgroup.
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, min(q0 + BM, Nq) + diag);
-  int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   const int rows_end = min(qw0 + 32, Nq);
   int w_end = rows_end > qw0 ? Nk : 0;
   if (CAUSAL && rows_end > qw0) w_end = min(Nk, rows_end + diag);
+  // Sliding window (key j kept for row i iff i + diag - wl <= j <= i + diag
+  // + wr; negative = unbounded): keys right of the last row's window are
+  // never loaded, the walk starts at the tile of the first row's window
+  // (jb), and a wave skips the tiles outside its own rows' windows.
+  int jb = 0, w_begin = 0;
+  if constexpr (WIN) {
+    if (wr >= 0) {
+      kv_end = min(kv_end, max(0, min(q0 + BM, Nq) + diag + wr));
+      if (rows_end > qw0) w_end = min(w_end, max(0, rows_end + diag + wr));
+    }
+    if (wl >= 0) {
+      jb = max(0, q0 + diag - wl) / BN;
+      w_begin = qw0 + diag - wl;
+    }
+  }
+  int nt = kv_end > jb * BN ? (kv_end - jb * BN + BN - 1) / BN : 0;
   int nf = Nk / BN;
   if (CAUSAL) nf = min(nf, max(0, (q0 + diag + 1) / BN));
+  // With a window, tiles [t_lo, nf) (counted from jb) are the ones every row
+  // of the workgroup sees whole; the ones before t_lo are cut by the
+  // window's left edge.
+  int t_lo = 0;
+  if constexpr (WIN) {
+    if (wr >= 0) nf = min(nf, max(0, (q0 + diag + wr + 1) / BN));
+    if (wl >= 0) {
+      const int q_last = min(q0 + BM, Nq) - 1;
+      t_lo = max(0, (q_last + diag - wl + BN - 1) / BN - jb);
+    }
+    nf -= jb;
+  }
 
   // ---- Block sparsity (attn_fwd_kernel's walk): the tiles of flagged key
   // blocks below kv_end, in key order; nt counts them and nf those every row
@@ -187,6 +220,7 @@ attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
     nf = sp_nf + TPB * nf_blocks;
   }
   nf = min(max(nf, 0), nt);
+  t_lo = min(t_lo, nf);
   // Start of the next visited tile (block sparsity only); called once per
   // tile, only while one is left, so a flagged block lies ahead.
   auto sparse_next = [&]() -> int {
@@ -253,7 +287,7 @@ attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   if constexpr (SPARSE) {
     if (nt > 0) sp_cur = sparse_next();
   }
-  if (nt > 0) issue_tile(SPARSE ? sp_cur : 0, smem);
+  if (nt > 0) issue_tile(SPARSE ? sp_cur : jb * BN, smem);
   __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tile 0 have landed
   __syncthreads();
 
@@ -330,16 +364,18 @@ attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   // direct loads, so they need not wait for those loads (without it the
   // compiler waits for every outstanding direct-to-LDS load before the first
   // V^T read).  The wait at the end of the tile keeps the order.
-  auto tile_body = [&](int t, auto mode, uint16_t* __restrict__ nxt, const uint16_t* __restrict__ st) {
+  auto tile_body = [&](int t, auto mode, uint16_t* __restrict__ nxt, const uint16_t* __restrict__ st)
+                       __attribute__((always_inline)) {
     constexpr int kMode = decltype(mode)::value;
-    const int j0 = SPARSE ? sp_cur : t * BN;
+    const int j0 = SPARSE ? sp_cur : (jb + t) * BN;
     if (t + 1 < nt) {
       int jn = j0 + BN;
       if constexpr (SPARSE) jn = sp_cur = sparse_next();
       issue_tile(jn, nxt);
     }
 
-    if (j0 < w_end) {  // wave-uniform: skip tiles above this wave's diagonal
+    // wave-uniform: skip tiles above this wave's diagonal (or outside its window)
+    if (j0 < w_end && (!WIN || j0 + BN > w_begin)) {
       f32x4_t s[2][NKB];
       __builtin_amdgcn_s_setprio(1);
       compute_s(st, s);
@@ -365,6 +401,10 @@ attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
         for (int qb = 0; qb < 2; ++qb) lsum[qb] += psum[qb];
       } else {
         need_mask = kMode == kMasked && ((j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + diag));
+        if constexpr (WIN) {
+          if (wl >= 0 && j0 < qw0 + 31 + diag - wl) need_mask = true;
+          if (wr >= 0 && j0 + BN - 1 > qw0 + diag + wr) need_mask = true;
+        }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           if (need_mask) {
@@ -374,7 +414,9 @@ attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const int j = j0 + 16 * kb + 4 * g + r;
-                const bool vis = j < Nk && (!CAUSAL || j <= my_q + diag);
+                const int dist = my_q + diag - j;
+                const bool vis = j < Nk && (!CAUSAL || dist >= 0) &&
+                                 (!WIN || ((wl < 0 || dist <= wl) && (wr < 0 || -dist <= wr)));
                 s[qb][kb][r] = vis ? s[qb][kb][r] : -INFINITY;
               }
             }
@@ -417,8 +459,16 @@ attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
       };
       __builtin_amdgcn_s_setprio(1);
       // (with a block mask a row may keep only the keys of a ragged last
-      // block, so its masked tiles take the lo half as well)
-      if ((CAUSAL || SPARSE) && need_mask)
+      // block, so its masked tiles take the lo half as well; a tile cut only
+      // by the left edge of a window of at least 128 keys needs no lo half:
+      // every row it holds sees at least that many keys)
+      bool with_lo = (CAUSAL || SPARSE || WIN) && need_mask;
+      if constexpr (WIN) {
+        const bool right_edge = (CAUSAL && j0 + BN - 1 > qw0 + diag) ||
+                                (wr >= 0 && j0 + BN - 1 > qw0 + diag + wr);
+        if (wl >= 127 && !right_edge && j0 + BN <= Nk) with_lo = false;
+      }
+      if (with_lo)
         pv_product(std::true_type{});
       else
         pv_product(std::false_type{});
@@ -428,13 +478,16 @@ attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
     __builtin_amdgcn_s_waitcnt(0);  // tile t+1 has landed in LDS
     __syncthreads();
   };
-  auto tile = [&](int t, auto mode) {
+  auto tile = [&](int t, auto mode) __attribute__((always_inline)) {
     tile_body(t, mode, smem + ((t + 1) & 1) * C::kStage, smem + (t & 1) * C::kStage);
   };
   using LeanMode = std::integral_constant<int, kLean>;
   using FullMode = std::integral_constant<int, kFull>;
   using MaskedMode = std::integral_constant<int, kMasked>;
   int t = 0;
+  if constexpr (WIN) {
+    for (; t < t_lo; ++t) tile(t, MaskedMode{});
+  }
   if (t < nf) tile(t++, FullMode{});
   for (; t < nf; ++t) tile(t, LeanMode{});
   for (; t < nt; ++t) tile(t, MaskedMode{});
