@@ -107,14 +107,13 @@ def test_wide_grid_against_oracle(case):
     assert_close(out, lse, O, L, str(case))
 
 
-@pytest.mark.parametrize("Nk", [33, 64, 65, 97, 200, 1000, 2100])
+@pytest.mark.parametrize("Nk", [33, 64, 65, 97, 128, 129, 200, 1000, 2100, 4100])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 def test_key_split_small_grid_edges(d, Nk, causal):
-    # the key-split kernel: quarter ranges of 1..17 tiles per wave, waves
-    # without keys, ragged last tiles, causal blocks whose rows see few keys;
-    # at d = 64 a wave computes S^T of its next tile during the softmax of
-    # the current one, which these tile counts start, run and end
+    # the key-split kernel (32-key tiles): quarter ranges of 1..33 tiles per
+    # wave, a single tile per wave (where no load runs ahead), waves without
+    # keys, ragged last tiles, causal blocks whose rows see few keys
     Nq = 70
     dt = "fp16" if (d == 64 and causal) else "bf16"
     q, k, v = make_qkv(1, Nq, Nk, 4, 2, d, dt, 1.0, 260 + Nk + d)
