@@ -43,7 +43,7 @@ METRIC_BWD = ("attention bwd TFLOP/s (10*B*Hq*Nq*Nk*d per call, halved for causa
 _CSRC = os.path.join(ROOT, "exact_tiled_attention_35_amd", "csrc")
 OP_SOURCES = {
     "fwd": ("gfx950_ops.hpp", "attn_fwd_kernel.hpp", "attn_fwd_splitk_kernel.hpp",
-            "attn_fwd_pipe_kernel.hpp", "attn_fwd_k16_kernel.hpp", "attn_api.hip", "attn_host.hpp"),
+            "attn_fwd_k16_kernel.hpp", "attn_api.hip", "attn_host.hpp"),
     "bwd": ("gfx950_ops.hpp", "attn_bwd_kernel.hpp", "attn_bwd_api.hip", "attn_host.hpp"),
     "decode": ("gfx950_ops.hpp", "attn_decode_kernel.hpp", "attn_decode_api.hip", "attn_host.hpp"),
 }
@@ -51,10 +51,10 @@ KERNEL_SOURCES = [os.path.join(_CSRC, n) for n in OP_SOURCES["fwd"]]
 TRAFFIC_FILES = {op: os.path.join(ROOT, "profiles", f"attn_{op}_traffic.json") for op in OP_SOURCES}
 TRAFFIC_FILE = TRAFFIC_FILES["fwd"]
 OP_KERNELS = {
-    # one of these per forward call: the tile kernel, at d = 128 (plain) its
-    # 16x16x32 form, at d = 256 the pipelined one (small grids use
+    # one of these per forward call: the tile kernel, or (plain d = 128 and
+    # d = 256, windows at d = 128) its 16x16x32 form (small grids use
     # attn_fwd_splitk_kernel)
-    "fwd": ("attn_fwd_kernel", "attn_fwd_k16_kernel", "attn_fwd_pipe_kernel"),
+    "fwd": ("attn_fwd_kernel", "attn_fwd_k16_kernel"),
     "bwd": ("attn_bwd_dq_kernel", "attn_bwd_dkdv_kernel"),
     # the split attention kernel appends the new rows itself
     "decode": ("attn_decode_kernel", "attn_decode_merge_kernel"),

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = [os.path.join(PKG, "csrc", n) for n in ("attn_api.hip", "attn_bwd_api.hip", "attn_decode_api.hip")]
 HEADERS = [os.path.join(PKG, "csrc", n) for n in ("gfx950_ops.hpp", "attn_fwd_kernel.hpp",
-                                                  "attn_fwd_splitk_kernel.hpp", "attn_fwd_pipe_kernel.hpp",
+                                                  "attn_fwd_splitk_kernel.hpp",
                                                   "attn_fwd_k16_kernel.hpp",
                                                   "attn_bwd_kernel.hpp", "attn_decode_kernel.hpp",
                                                   "attn_host.hpp")] + [

@@ -13,7 +13,6 @@
 #include <cstdint>
 
 #include "attn_fwd_kernel.hpp"
-#include "attn_fwd_pipe_kernel.hpp"
 #include "attn_fwd_k16_kernel.hpp"
 #include "attn_fwd_splitk_kernel.hpp"
 #include "attn_host.hpp"
@@ -55,15 +54,17 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, i
       return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
     }
   }
-  // d = 256, plain: the kernel that overlaps each wave's softmax with the
-  // next tile's S^T product.
+  // d = 256, plain: the 16x16x32 kernel with 32-key tiles, two workgroups
+  // of 128 rows per CU.
   if constexpr (!MODS && !VARLEN && !SPARSE && D == 256) {
     if (scale > 0.f) {
-      hipLaunchKernelGGL((eta::attn_fwd_pipe_kernel<D, BF16, CAUSAL>), dim3(total),
-                         dim3(eta::PipeCfg<D>::kThreads), 0, stream,
+      static_assert(eta::K16Cfg<D>::BM == C::BM, "one workgroup per 128-row block");
+      hipLaunchKernelGGL((eta::attn_fwd_k16_kernel<D, BF16, CAUSAL>), dim3(total),
+                         dim3(eta::K16Cfg<D>::kThreads), 0, stream,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                          static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Hq,
-                         Hkv, Nq, Nk, nqb, total, c_log2);
+                         Hkv, Nq, Nk, nqb, total, c_log2, eta::VarlenArgs{}, eta::BlockMaskArgs{}, -1,
+                         -1);
       return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
     }
   }

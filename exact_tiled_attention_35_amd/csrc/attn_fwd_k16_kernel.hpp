@@ -1,5 +1,5 @@
 // Exact tiled attention forward on 16x16x32 matrix instructions (gfx950),
-// head dimension 64 or 128.
+// head dimension 64, 128 or 256.
 //
 // Same computation and pipeline as attn_fwd_kernel (softmax(Q K^T * scale) V
 // per (batch, query head), the formula of the interface section of
@@ -18,6 +18,12 @@
 //    workgroup meets a barrier once per 128 keys instead of 64.  Without a
 //    causal mask a wave's work does not depend on the workgroup's other
 //    rows, so both instances compute a sequence's rows bit for bit alike.
+//  * d = 256: 4 waves, 32-key tiles (two stages of 68 KB), two workgroups
+//    per CU.  With 128 O^T and 64 Q^T registers per wave the tile body fits
+//    the 256 registers two workgroups leave it only if a diagonal tile's P
+//    goes through the matrix cores as a hi sweep over all of V^T followed
+//    by a lo sweep (V^T read from LDS twice on those tiles); interleaving
+//    the two halves per V^T block spilled 114 registers.
 //
 // Layout (lane l, g = l / 16, c = l % 16):
 //  * S^T = K Q^T in 16 x 16 blocks s[qb][kb]: register r holds key
@@ -43,7 +49,7 @@
 // tiles, the block-mask instance 64-key ones).  Of the score variants only
 // the sliding window (WIN, 128-row workgroups; attn_fwd_kernel's key range,
 // tile modes and edge masking); scale > 0.  The launcher uses the kernel at
-// d = 128.  The tile lambdas are forced inline: the window instances, with
+// d = 128 and, plain batched calls only, at d = 256.  The tile lambdas are forced inline: the window instances, with
 // a third tile loop, were otherwise left as calls with the accumulators in
 // scratch.
 #pragma once
@@ -66,7 +72,7 @@ struct K16Cfg {
   static constexpr int kWaves = WIDE ? 8 : 4;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int BM = 32 * kWaves;                 // query rows per workgroup
-  static constexpr int BN = WIDE ? 128 : 64;             // keys per K/V tile
+  static constexpr int BN = WIDE ? 128 : (D == 256 ? 32 : 64);  // keys per K/V tile
   static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
   static constexpr int KCP = kChunks + 2;                // K row, in 16-byte slots
   static constexpr int VCP = kChunks + 2;                // V row, in 16-byte slots
@@ -80,7 +86,7 @@ struct K16Cfg {
   static constexpr int kVInstPerWave = (kVInst + kWaves - 1) / kWaves;
   static constexpr int kEpiElems = kWaves * 32 * (D + 8);  // the epilogue's staged rows
   static constexpr int kLdsElems = 2 * kStage > kEpiElems ? 2 * kStage : kEpiElems;
-  static_assert(D == 64 || D == 128, "the 16x16x32 kernel serves d = 64 and d = 128");
+  static_assert(D == 64 || D == 128 || D == 256, "the 16x16x32 kernel serves d = 64, 128 and 256");
   // Row strides of 8 (mod 16) dwords: for these read patterns (K: 16 rows x
   // 64 bytes per 16-byte read; V: 16 rows x 32 bytes per transpose read)
   // the counters show no bank conflicts in the tile loop, where a K stride
@@ -468,10 +474,40 @@ attn_fwd_k16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
                                 (wr >= 0 && j0 + BN - 1 > qw0 + diag + wr);
         if (wl >= 127 && !right_edge && j0 + BN <= Nk) with_lo = false;
       }
-      if (with_lo)
-        pv_product(std::true_type{});
-      else
+      if constexpr (D == 256) {
+        // at d = 256 the lo half is a second sweep over the V^T blocks (read
+        // again from LDS) after the hi one: a tile body with both halves
+        // interleaved needs more registers than two workgroups per CU leave
         pv_product(std::false_type{});
+        if (with_lo) {
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            u32x4_t plo[2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              f32x8_t pv;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                pv[e] = s[qb][2 * kk][e];
+                pv[4 + e] = s[qb][2 * kk + 1][e];
+              }
+              plo[qb] = pack8<BF16>(pv - unpack8<BF16>(pack8<BF16>(pv)));
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              const u32x2_t x0 = lds_read_tr4(st + v_rd + 32 * kk * VS + 16 * db);
+              const u32x2_t x1 = lds_read_tr4(st + v_rd + (32 * kk + 16) * VS + 16 * db);
+              const u32x4_t a = {x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+              for (int qb = 0; qb < 2; ++qb) oacc[qb][db] = mfma_16x16x32<BF16>(a, plo[qb], oacc[qb][db]);
+            }
+          }
+        }
+      } else if (with_lo) {
+        pv_product(std::true_type{});
+      } else {
+        pv_product(std::false_type{});
+      }
       __builtin_amdgcn_s_setprio(0);
     }
 

@@ -147,10 +147,10 @@ def test_traffic_summary_needs_the_kernel_and_the_copy(tmp_path, monkeypatch):
     _write_counter_csv(fetch, "FETCH_SIZE", [("neg_kernel", 512.0)])  # no kernel dispatch
     with pytest.raises(SystemExit, match="no forward kernel dispatches"):
         bench.write_traffic_summary(str(fetch), str(write), 1, workload=HEADLINE, op="fwd")
-    # the d = 256 workloads run the pipelined kernel
-    pipe = "void eta::attn_fwd_pipe_kernel<256, false, true>(...)"
-    _write_counter_csv(fetch, "FETCH_SIZE", [(pipe, 200.0), ("neg_kernel", 512.0)])
-    _write_counter_csv(write, "WRITE_SIZE", [(pipe, 30.0), ("neg_kernel", 1024.0)])
+    # the d = 256 workloads run the 16x16x32 kernel
+    k256 = "void eta::attn_fwd_k16_kernel<256, false, true, false, false, false, false>(...)"
+    _write_counter_csv(fetch, "FETCH_SIZE", [(k256, 200.0), ("neg_kernel", 512.0)])
+    _write_counter_csv(write, "WRITE_SIZE", [(k256, 30.0), ("neg_kernel", 1024.0)])
     bench.write_traffic_summary(str(fetch), str(write), 1, workload=HEADLINE, op="fwd")
     rec = json.load(open(tmp_path / "t.json"))["workloads"][HEADLINE]
     assert rec["FETCH_SIZE_KiB_per_launch"] == 200.0

@@ -122,8 +122,8 @@ def test_key_split_small_grid_edges(d, Nk, causal):
     assert_close(out, lse, O, L, f"d {d} Nk {Nk}")
 
 
-# d = 256 goes to the kernel that computes S^T of tile t+1 during the
-# softmax of tile t: key counts around the 32-key tile (one tile, a tile and
+# d = 256 goes to the 16x16x32 kernel with 32-key tiles (hi and lo sweeps
+# of P on diagonal tiles): key counts around the 32-key tile (one tile, a tile and
 # one key, tiles that end before a wave's diagonal), Nq != Nk both ways,
 # query blocks whose waves compute different numbers of tiles.
 D256_EDGES = [(128, 1), (128, 31), (128, 32), (128, 33), (128, 64), (200, 96),
