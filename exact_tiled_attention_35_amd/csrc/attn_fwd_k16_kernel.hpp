@@ -49,7 +49,8 @@
 // tiles, the block-mask instance 64-key ones).  Of the score variants only
 // the sliding window (WIN, 128-row workgroups; attn_fwd_kernel's key range,
 // tile modes and edge masking); scale > 0.  The launcher uses the kernel at
-// d = 128 and, plain batched calls only, at d = 256.  The tile lambdas are forced inline: the window instances, with
+// d = 128, for plain batched calls at d = 256, and for causal calls (batched,
+// packed, block mask) at d = 64.  The tile lambdas are forced inline: the window instances, with
 // a third tile loop, were otherwise left as calls with the accumulators in
 // scratch.
 #pragma once

@@ -326,6 +326,18 @@ def test_d128_wide_grid_edges(nq_nk, causal):
     assert_close(out, lse, O, L, f"Nq {Nq} Nk {Nk}")
 
 
+@pytest.mark.parametrize("nq_nk", K16_EDGES, ids=lambda c: "N%dx%d" % c)
+def test_d64_causal_wide_grid_edges(nq_nk):
+    # batched causal d = 64 on 128 or more row blocks: the 16x16x32 kernel
+    Nq, Nk = nq_nk
+    dt = "bf16" if Nq % 2 else "fp16"
+    q, k, v = make_qkv(1, Nq, Nk, 128, 16, 64, dt, 1.0, 600 + K16_EDGES.index(nq_nk))
+    scale = 1.0 / math.sqrt(64)
+    out, lse = gpu_attn(q, k, v, scale, True)
+    O, L = oracle.attention(q, k, v, scale, True)
+    assert_close(out, lse, O, L, f"Nq {Nq} Nk {Nk}")
+
+
 def test_run_to_run_bitwise_determinism():
     q, k, v = make_qkv(2, 700, 700, 8, 2, 128, "bf16", 1.0, 404)
     a = gpu_attn(q, k, v, 0.088, True)
